@@ -1,0 +1,156 @@
+"""F4 block quantiser and the paged cache's byte layout, fp64.  Test infrastructure only.
+
+The format (mistral.rs PR #2375, "Changes by area" item 2): symmetric 4-bit
+values stored as ``(nibble - 8) * scale``, 32 values per 16-byte row, one
+scale per 32-value block (the V scale granularity follows the workload
+description: one fp16 scale per 32 contiguous values).  "Known limitations"
+on the same page states the per-value error bound max_abs / 16.
+
+Readings taken where the page is silent:
+* scale s = fp16_round_nearest_even(absmax / 8), saturated to 65504; half a
+  step is then absmax / 16, the page's bound;
+* codes q = clamp(round_half_even(x / s), -8, 7) against the stored fp16 s,
+  with the exact quotient; s == 0 gives all codes 0 (nibble 8);
+* nibble = q + 8; byte m of a 32-value block holds elements 2m (low nibble)
+  and 2m + 1 (high nibble).
+
+Exactness of the quotient: x is fp32 and s is fp16, so if x / s is not
+exactly k + 1/2 it differs from it by at least 2**-24 * |x / s| (the gap
+between x and the exactly representable (k + 1/2) * s is at least one fp32
+ulp of x).  A correctly rounded fp64 quotient errs by at most 2**-53 relative,
+so fp64 division followed by round-half-even decides every case exactly.
+
+Physical layout (one layer; P pages of 64 tokens, H kv heads, D = head_dim):
+  k_nib   uint8  [P][H][D/32][64][16]   block c of token t: 16 bytes at (c, t)
+  k_scale fp16   [P][H][64][D/32]
+  v_nib   uint8  [P][H][8][D/4][16]     unit (c, j): tokens 8c..8c+7 x dims
+                                        4j..4j+3; byte 4k + 2r + h holds dims
+                                        4j+2h (low) and 4j+2h+1 (high) of token
+                                        8c + 2k + r
+  v_scale fp16   [P][H][64][D/32]
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+BLOCK = 32
+FP16_MAX = 65504.0
+
+
+def fp16_round(a: np.ndarray) -> np.ndarray:
+    """Round fp64 values to fp16, nearest-even, saturating at 65504."""
+    a = np.minimum(np.asarray(a, dtype=np.float64), FP16_MAX)
+    return a.astype(np.float16)
+
+
+def quantize_blocks(x: np.ndarray):
+    """Quantise x[..., 32] (fp32 values).  Returns (codes int8 in [-8, 7], scale fp16)."""
+    x = np.asarray(x)
+    assert x.shape[-1] == BLOCK
+    xd = x.astype(np.float32).astype(np.float64)
+    assert np.isfinite(xd).all(), "non-finite input to the F4 quantiser"
+    a = np.abs(xd).max(axis=-1)
+    s16 = fp16_round(a * 0.125)
+    s = s16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0.0, np.rint(xd / np.where(s > 0.0, s, 1.0)), 0.0)
+    q = np.clip(q, -8, 7).astype(np.int8)
+    return q, s16
+
+
+def dequantize_blocks(q: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    return q.astype(np.float64) * s16.astype(np.float64)[..., None]
+
+
+def pack_block_bytes(q: np.ndarray) -> np.ndarray:
+    """Codes [..., 32] -> bytes [..., 16]: element 2m low nibble, 2m + 1 high nibble."""
+    n = (q.astype(np.int16) + 8).astype(np.uint8)
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_block_bytes(b: np.ndarray) -> np.ndarray:
+    """Bytes [..., 16] -> codes [..., 32]."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (BLOCK,), dtype=np.int8)
+    out[..., 0::2] = (b & 0x0F).astype(np.int8) - 8
+    out[..., 1::2] = (b >> 4).astype(np.int8) - 8
+    return out
+
+
+class Cache:
+    """The four arrays of one layer's paged F4 cache, in the physical layout above."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int):
+        assert head_dim % BLOCK == 0
+        P, H, D = num_pages, num_kv_heads, head_dim
+        self.P, self.H, self.D = P, H, D
+        self.k_nib = np.zeros((P, H, D // BLOCK, PAGE, 16), dtype=np.uint8)
+        self.v_nib = np.zeros((P, H, PAGE // 8, D // 4, 16), dtype=np.uint8)
+        self.k_scale = np.zeros((P, H, PAGE, D // BLOCK), dtype=np.float16)
+        self.v_scale = np.zeros((P, H, PAGE, D // BLOCK), dtype=np.float16)
+
+    def put_codes(self, pages, offs, kq, ks, vq, vs):
+        """Store codes kq, vq [N, H, D] and scales ks, vs [N, H, D/32] at (page, offset) pairs."""
+        pages = np.asarray(pages, dtype=np.int64)
+        offs = np.asarray(offs, dtype=np.int64)
+        N, H, D = kq.shape
+        nb = D // BLOCK
+        # K: 16 bytes per (block, token)
+        kb = pack_block_bytes(kq.reshape(N, H, nb, BLOCK))          # [N, H, nb, 16]
+        self.k_nib[pages[:, None, None], np.arange(H)[None, :, None],
+                   np.arange(nb)[None, None, :], offs[:, None, None], :] = kb
+        self.k_scale[pages, :, offs, :] = ks
+        # V: for token t, dims 4j+2h, 4j+2h+1 go to byte 4k+2r+h of unit (t//8, j)
+        n = (vq.astype(np.int16) + 8).astype(np.uint8).reshape(N, H, D // 4, 2, 2)
+        vb = n[..., 0] | (n[..., 1] << 4)                               # [N, H, D/4, 2(h)]
+        c = offs // 8
+        base = 4 * ((offs % 8) // 2) + 2 * (offs % 2)
+        for h in range(2):
+            self.v_nib[pages[:, None, None], np.arange(H)[None, :, None], c[:, None, None],
+                       np.arange(D // 4)[None, None, :], (base + h)[:, None, None]] = vb[..., h]
+        self.v_scale[pages, :, offs, :] = vs
+
+    def write(self, k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray):
+        """Quantise k, v [T, H, D] (fp32) into the slots; slot -1 skips the token."""
+        k = np.asarray(k, dtype=np.float32)
+        v = np.asarray(v, dtype=np.float32)
+        T, H, D = k.shape
+        assert (H, D) == (self.H, self.D) and v.shape == k.shape
+        slots = np.asarray(slot_mapping, dtype=np.int64)
+        live = np.nonzero(slots >= 0)[0]
+        assert len(np.unique(slots[live])) == len(live), "slot_mapping entries must be unique"
+        if len(live) == 0:
+            return
+        nb = D // BLOCK
+        kq, ks = quantize_blocks(k[live].reshape(len(live), H, nb, BLOCK))
+        vq, vs = quantize_blocks(v[live].reshape(len(live), H, nb, BLOCK))
+        self.put_codes(slots[live] // PAGE, slots[live] % PAGE,
+                       kq.reshape(len(live), H, D), ks, vq.reshape(len(live), H, D), vs)
+
+    def page_codes(self, page: int, head: int):
+        """Codes [64, D] and fp16 scales [64, D/32] of K and V for one page-head tile."""
+        D, nb = self.D, self.D // BLOCK
+        kb = self.k_nib[page, head]                                  # [nb, 64, 16]
+        kc = unpack_block_bytes(kb).transpose(1, 0, 2).reshape(PAGE, D)
+        u = self.v_nib[page, head]                                   # [8, D/4, 16]
+        vc = np.empty((PAGE, D), dtype=np.int8)
+        for t in range(PAGE):
+            c, base = t // 8, 4 * ((t % 8) // 2) + 2 * (t % 2)
+            for h in range(2):
+                byte = u[c, :, base + h]
+                vc[t, 2 * h::4] = (byte & 0x0F).astype(np.int8) - 8
+                vc[t, 2 * h + 1::4] = (byte >> 4).astype(np.int8) - 8
+        return kc, self.k_scale[page, head], vc, self.v_scale[page, head]
+
+    def page_values(self, page: int, head: int):
+        """Dequantised K and V of one page-head tile, fp64 [64, D] each."""
+        kc, ks, vc, vs = self.page_codes(page, head)
+        nb = self.D // BLOCK
+        kd = dequantize_blocks(kc.reshape(PAGE, nb, BLOCK), ks).reshape(PAGE, self.D)
+        vd = dequantize_blocks(vc.reshape(PAGE, nb, BLOCK), vs).reshape(PAGE, self.D)
+        return kd, vd
+
+    def arrays(self):
+        """The four arrays as raw bytes in C order (k_nib, k_scale bits, v_nib, v_scale bits)."""
+        return (self.k_nib, self.k_scale.view(np.uint16), self.v_nib, self.v_scale.view(np.uint16))
