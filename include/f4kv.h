@@ -1,0 +1,241 @@
+/*
+ * f4kv.h -- C ABI of the F4 paged-attention library for MI355X (gfx950).
+ *
+ * Paged grouped-query attention over a 4-bit symmetric block-scaled KV cache
+ * ("F4": values (nibble - 8) * scale, 32 values per 16-byte row, one fp16
+ * scale per 32 values), with statically YaRN-rotated keys, split across page
+ * chunks and folded by log-sum-exp.
+ *
+ * Sources for what each call computes:
+ *   [MRS]  mistral.rs PR #2375 "YaRN rope scaling, 4-bit F4 packed KV cache,
+ *          and hybrid paged attention", sections "Changes by area" items 1-2
+ *          and "Known limitations".
+ *   [IGN]  ignis docs, configuration / context-and-speculation: the
+ *          --model-rope-scaling, --model-adapt-context-step and
+ *          --model-prefill-chunk rows.
+ *   [FT]   FreeToken issue #568, "Proposed solution" item 2 (device windows
+ *          folded by log2-sum-exp) and "What problem does this solve" item 1.
+ *   [AE]   aeliusai "hybrid-attention-economics", "What a token of context
+ *          costs" (4 KV heads of key length 256).
+ *
+ * Conventions (all entry points):
+ *   - Every call returns an int status (F4KV_OK or an error below).  On error
+ *     nothing has been enqueued and f4kv_last_error() names the reason
+ *     (thread-local, valid until the next call from the same thread).
+ *   - All array arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory.  Parameter structs are host
+ *     memory, read only during the call.
+ *   - Work is enqueued on `stream` (0 = the null stream); no call waits for the
+ *     device.  Faults surface at the caller's next synchronisation.
+ *   - Shapes and pointers are validated on the host before any launch.  Values
+ *     that live on the device (context lengths, page ids, slot ids) cannot be
+ *     checked there: out-of-range entries are skipped by the kernels (never
+ *     read or written out of bounds), and the results for them are undefined.
+ *   - Calls on one stream are ordered; calls on different streams that touch
+ *     the same buffers race like any other kernels.
+ *
+ * Cache layout (one layer; P pages of 64 tokens, H kv heads, D = head_dim):
+ *   k_nib   uint8   [P][H][D/32][64][16]  bytes (c, t): block c of token t;
+ *                                         byte m holds element 2m (low nibble)
+ *                                         and 2m+1 (high nibble) of the block
+ *   k_scale fp16    [P][H][64][D/32]      scale of block c of token t
+ *   v_nib   uint8   [P][H][8][D/4][16]    unit (c, j): tokens 8c..8c+7 x dims
+ *                                         4j..4j+3; byte 4k+2r+h holds dims
+ *                                         4j+2h (low) and 4j+2h+1 (high) of
+ *                                         token 8c+2k+r
+ *   v_scale fp16    [P][H][64][D/32]
+ *   Logical value of element e of block c of token t: (nibble - 8) * scale.
+ *   Token i of a sequence lives in page page_table[i / 64], slot i % 64.
+ */
+#ifndef F4KV_H
+#define F4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define F4KV_ABI_VERSION 1
+
+enum {
+  F4KV_OK = 0,
+  F4KV_ERR_INVALID = 1,      /* a null/misaligned pointer or an argument out of range */
+  F4KV_ERR_UNSUPPORTED = 2,  /* valid, but a shape these kernels do not implement     */
+  F4KV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_size */
+  F4KV_ERR_LAUNCH = 4        /* the HIP runtime refused a launch                       */
+};
+
+enum { F4KV_F32 = 0, F4KV_BF16 = 1 };
+
+/* ABI version of the loaded library (F4KV_ABI_VERSION it was built with). */
+int f4kv_abi_version(void);
+
+/* Reason for the last non-zero status returned on this thread ("" if none). */
+const char* f4kv_last_error(void);
+
+/*
+ * YaRN parameters [MRS item 1; IGN --model-rope-scaling].
+ *   theta       rope base (> 1)
+ *   rotary_dim  channels rotated, even, > 0 (the rest pass through)
+ *   factor      1 = plain RoPE; otherwise YaRN with factor in (1, 64]
+ *   orig_ctx    trained context the correction dims refer to (> 0)
+ *   beta_fast / beta_slow   correction-dim betas (beta_fast > beta_slow > 0)
+ *   mscale      table scale; <= 0 derives it: 1 for factor 1, otherwise
+ *               1 + 0.1 ln(factor) (net 1.0199427025 at factor 1.220703125)
+ */
+typedef struct {
+  double theta;
+  int32_t rotary_dim;
+  double factor;
+  int32_t orig_ctx;
+  double beta_fast;
+  double beta_slow;
+  double mscale;
+} f4kv_yarn_params;
+
+/*
+ * One layer's paged F4 cache (layout above).  All four pointers are device
+ * memory aligned to 16 bytes.  page_size must be 64 [IGN
+ * --model-adapt-context-step: pages are multiples of 64 tokens]; head_dim a
+ * multiple of 32.
+ */
+typedef struct {
+  uint8_t* k_nib;
+  uint16_t* k_scale;
+  uint8_t* v_nib;
+  uint16_t* v_scale;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+} f4kv_cache;
+
+/* Bytes of each of the four cache arrays for the given geometry (host helper,
+ * no device work).  Any output pointer may be NULL.  Returns the total, or 0
+ * for an invalid geometry. */
+size_t f4kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                        size_t* k_nib, size_t* k_scale, size_t* v_nib, size_t* v_scale);
+
+/*
+ * yarn_rope_table [MRS item 1; IGN --model-rope-scaling; FT problem item 1]
+ * Rows of the static YaRN table for n positions:
+ *   cos_out[i][p] = m * cos(pos[i] * theta'_p), sin_out likewise, p < rotary_dim/2,
+ * where theta'_p blends theta^(-2p/rotary_dim) and that divided by the factor
+ * with a linear ramp between the beta_fast / beta_slow correction dims
+ * (floored / ceiled, clamped to [0, rotary_dim - 1]).  Angles and the
+ * trigonometry are evaluated in fp64; outputs are rounded to fp32.
+ *   positions  int32 [n], each in [0, 2^24)   (values outside give undefined rows)
+ *   cos_out, sin_out  fp32 [n][rotary_dim/2]
+ */
+int yarn_rope_table(const f4kv_yarn_params* params, const int32_t* positions, int32_t n,
+                    float* cos_out, float* sin_out, hipStream_t stream);
+
+/*
+ * yarn_rope_apply [MRS item 1: partial rotary; IMROPE-to-NEOX equivalence]
+ * NEOX rotation of the first rotary_dim channels of every head of every row:
+ *   y[t][h][i]      = x[t][h][i] * c[t][i] - x[t][h][i + r/2] * s[t][i]
+ *   y[t][h][i + r/2] = x[t][h][i + r/2] * c[t][i] + x[t][h][i] * s[t][i]
+ * for i < r/2 (r = rotary_dim); channels >= r are copied.  Arithmetic in fp64,
+ * one rounding to the output type (bf16: nearest-even via fp32).
+ *   cos_rows, sin_rows fp32 [T][r/2];  x, y [T][H][D] of dtype F4KV_F32 or
+ *   F4KV_BF16 (y may equal x: in place).  x, y aligned to 4 bytes.
+ */
+int yarn_rope_apply(const float* cos_rows, const float* sin_rows,
+                    const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
+                    int32_t T, int32_t H, int32_t D, int32_t rotary_dim, hipStream_t stream);
+
+/*
+ * kv_cache_write_f4 [MRS item 2: reshape_and_cache writes symmetric 4-bit
+ * (nibble - 8) * scale; "Known limitations": per-value bound max_abs/16]
+ * Quantises k and v (fp32 [T][H][D], 16-byte aligned) into the cache slots
+ * slot_mapping[t] = page * 64 + offset (-1 skips the token; live entries must
+ * be distinct, else the result is undefined).  Per token, kv head and
+ * 32-value block:
+ *   s = fp16_nearest_even(min(absmax * 0.125, 65504)),
+ *   code = clamp(nearest_even(x / s), -8, 7) with the exact quotient
+ *   (s == 0: every code 0), nibble = code + 8.
+ * One thread owns whole blocks: no byte is written by two threads.
+ */
+int kv_cache_write_f4(const f4kv_cache* cache, const float* k, const float* v,
+                      const int32_t* slot_mapping, int32_t T, hipStream_t stream);
+
+/*
+ * paged_attn_decode_f4 [MRS item 2: paged attention dequantises F4 cells
+ * inline; FT item 2: windows folded by log-sum-exp; AE: grouped KV heads]
+ * One query row per sequence.  For sequence b, query head h, KV head
+ * g = h / (Hq / H) and window w:
+ *   s_t = sm_scale * q[b][h] . k_t over the window's tokens t of [0, ctx_b),
+ *   out_m = max s_t,  out_l = sum exp(s_t - out_m),
+ *   out   = sum exp(s_t - out_m) v_t / out_l
+ * (natural-log units).  Window w covers tokens [w*window_tokens,
+ * (w+1)*window_tokens); num_windows == 1 with window_tokens == 0 means the
+ * whole context.  An empty window gives (-inf, 0, 0), the identity of
+ * lse_merge.  Internally each window is split further across the GPU and
+ * folded with the same merge.
+ *   q             bf16 [B][Hq][D] (already rotated), 16-byte aligned
+ *   page_table    int32 [B][max_pages]
+ *   context_lens  int32 [B], each in [0, max_context_len]
+ *   max_context_len  host bound, <= max_pages * 64
+ *   window_tokens    multiple of 64 (0 only with num_windows == 1)
+ *   out    fp32 [W][B][Hq][D] (16-byte aligned); out_m, out_l fp32 [W][B][Hq] or NULL
+ *   workspace   device scratch of at least paged_attn_decode_f4_workspace_size()
+ *               bytes (16-byte aligned); may be NULL when that size is 0
+ * Supported: D == 256, Hq / H in {1, 2, 4, 8}.
+ */
+size_t paged_attn_decode_f4_workspace_size(int32_t B, int32_t Hq, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_context_len,
+                                           int32_t num_windows, int32_t window_tokens);
+int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q,
+                         const int32_t* page_table, const int32_t* context_lens,
+                         int32_t B, int32_t Hq, int32_t max_pages, int32_t max_context_len,
+                         int32_t num_windows, int32_t window_tokens, float sm_scale,
+                         float* out, float* out_m, float* out_l,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * lse_merge [FT item 2: partial windows folded by log-sum-exp]
+ * Folds C partial states per row:  M = max_c m_c,  w_c = l_c exp(m_c - M),
+ *   L = sum w_c,  out = sum w_c o_c / L;  rows with every l_c == 0 give
+ *   (-inf, 0, 0).
+ *   m, l  fp32 [C][R];  o fp32 [C][R][D];  out fp32 [R][D];
+ *   out_m, out_l fp32 [R] or NULL.   D a multiple of 4, pointers 16-byte aligned.
+ */
+int lse_merge(const float* m, const float* l, const float* o, int32_t C, int32_t R, int32_t D,
+              float* out, float* out_m, float* out_l, hipStream_t stream);
+
+/*
+ * paged_attn_prefill_f4 [IGN --model-prefill-chunk: chunk widths; FT item 2:
+ * a prefill attends within a device window; MRS item 2: F4 cells dequantised
+ * inline]
+ * Writes the chunk's own keys and values (when k_new/v_new are non-NULL, as
+ * kv_cache_write_f4 at positions pos0 .. pos0+T-1 through page_table), then
+ * computes causal attention of T query rows at positions pos0 + i over cache
+ * tokens [0, pos0 + i] of one sequence:
+ *   out[i][h] = softmax_t(sm_scale * q[i][h] . k_t) . v_t ;  out_m, out_l as in
+ *   decode (natural-log units).
+ *   q            bf16 [T][Hq][D] (already rotated), 16-byte aligned
+ *   k_new, v_new fp32 [T][H][D] or both NULL (cache already holds them)
+ *   page_table   int32 [max_pages] of this sequence; pos0 + T <= max_pages * 64
+ *   out          fp32 [T][Hq][D];  out_m, out_l fp32 [T][Hq] or NULL
+ *   workspace    at least paged_attn_prefill_f4_workspace_size() bytes
+ * Supported: D == 256, Hq / H == 4.  The products run in fp16 on MFMA with
+ * fp32 accumulation, so cache values must lie within fp16 range (|x| < 65504,
+ * which holds whenever the written keys/values did).
+ */
+size_t paged_attn_prefill_f4_workspace_size(int32_t T, int32_t Hq, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t pos0);
+int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q,
+                          const float* k_new, const float* v_new,
+                          const int32_t* page_table, int32_t max_pages,
+                          int32_t T, int32_t Hq, int32_t pos0, float sm_scale,
+                          float* out, float* out_m, float* out_l,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* F4KV_H */

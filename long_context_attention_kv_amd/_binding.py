@@ -1,0 +1,299 @@
+"""ctypes marshalling for libf4kv.so: tensors -> pointers, sizes and the current stream."""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libf4kv.so")
+_lib = None
+
+F32, BF16 = 0, 1
+PAGE = 64
+
+
+class F4KVError(RuntimeError):
+    """A call the library refused (status != 0), with its reason."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed (status {status}): {msg}")
+        self.status = status
+
+
+class _YarnParamsC(C.Structure):
+    _fields_ = [("theta", C.c_double), ("rotary_dim", C.c_int32), ("factor", C.c_double),
+                ("orig_ctx", C.c_int32), ("beta_fast", C.c_double), ("beta_slow", C.c_double),
+                ("mscale", C.c_double)]
+
+
+class _CacheC(C.Structure):
+    _fields_ = [("k_nib", C.c_void_p), ("k_scale", C.c_void_p), ("v_nib", C.c_void_p),
+                ("v_scale", C.c_void_p), ("num_pages", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("page_size", C.c_int32)]
+
+
+_P = C.c_void_p
+_I = C.c_int32
+_SIGS = {
+    "f4kv_abi_version": (C.c_int, []),
+    "f4kv_last_error": (C.c_char_p, []),
+    "f4kv_cache_bytes": (C.c_size_t, [_I, _I, _I, _P, _P, _P, _P]),
+    "yarn_rope_table": (C.c_int, [C.POINTER(_YarnParamsC), _P, _I, _P, _P, _P]),
+    "yarn_rope_apply": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
+    "kv_cache_write_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _P]),
+    "paged_attn_decode_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
+    "paged_attn_decode_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, C.c_float,
+                                       _P, _P, _P, _P, C.c_size_t, _P]),
+    "lse_merge": (C.c_int, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "paged_attn_prefill_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I]),
+    "paged_attn_prefill_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
+                                        _P, _P, _P, _P, C.c_size_t, _P]),
+}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libf4kv.so (built in-tree by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run long_context_attention_kv_amd/build.py "
+                           "(or __graft_entry__.build()) first")
+    lib = C.CDLL(_LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise F4KVError(fn, status, _lib.f4kv_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _need(t, dtype, shape=None, name="tensor"):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda and t.numel() > 0:
+        raise ValueError(f"{name} must live on the GPU")
+
+
+def abi_version() -> int:
+    return load_library().f4kv_abi_version()
+
+
+def cache_bytes(num_pages: int, num_kv_heads: int, head_dim: int):
+    lib = load_library()
+    a, b, c, d = (C.c_size_t() for _ in range(4))
+    total = lib.f4kv_cache_bytes(num_pages, num_kv_heads, head_dim, C.byref(a), C.byref(b), C.byref(c),
+                                 C.byref(d))
+    return total, (a.value, b.value, c.value, d.value)
+
+
+@dataclass
+class YarnParams:
+    theta: float = 1.0e7
+    rotary_dim: int = 256
+    factor: float = 1.0
+    orig_ctx: int = 262144
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    mscale: float = 0.0
+
+    def _c(self):
+        return _YarnParamsC(float(self.theta), int(self.rotary_dim), float(self.factor), int(self.orig_ctx),
+                            float(self.beta_fast), float(self.beta_slow), float(self.mscale))
+
+
+class F4Cache:
+    """One layer's paged F4 cache: four device tensors in the library's layout."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int = 256, device="cuda"):
+        nb = head_dim // 32
+        self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.k_nib = torch.zeros((num_pages, num_kv_heads, nb, PAGE, 16), dtype=torch.uint8, device=device)
+        self.k_scale = torch.zeros((num_pages, num_kv_heads, PAGE, nb), dtype=torch.int16, device=device)
+        self.v_nib = torch.zeros((num_pages, num_kv_heads, PAGE // 8, head_dim // 4, 16), dtype=torch.uint8,
+                                 device=device)
+        self.v_scale = torch.zeros((num_pages, num_kv_heads, PAGE, nb), dtype=torch.int16, device=device)
+
+    def _c(self):
+        return _CacheC(self.k_nib.data_ptr(), self.k_scale.data_ptr(), self.v_nib.data_ptr(),
+                       self.v_scale.data_ptr(), self.num_pages, self.num_kv_heads, self.head_dim, PAGE)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.k_nib, self.k_scale, self.v_nib, self.v_scale))
+
+
+def yarn_rope_table(params: YarnParams, positions: torch.Tensor, cos_out=None, sin_out=None):
+    lib = load_library()
+    n = positions.numel()
+    _need(positions, torch.int32, (n,), "positions")
+    half = params.rotary_dim // 2
+    if cos_out is None:
+        cos_out = torch.empty((n, half), dtype=torch.float32, device=positions.device)
+    if sin_out is None:
+        sin_out = torch.empty((n, half), dtype=torch.float32, device=positions.device)
+    _need(cos_out, torch.float32, (n, half), "cos_out")
+    _need(sin_out, torch.float32, (n, half), "sin_out")
+    p = params._c()
+    _check("yarn_rope_table", lib.yarn_rope_table(C.byref(p), _ptr(positions), n, _ptr(cos_out), _ptr(sin_out),
+                                                  _stream()))
+    return cos_out, sin_out
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("rope tensors must be float32 or bfloat16")
+
+
+def yarn_rope_apply(cos_rows, sin_rows, x, y=None, rotary_dim=None):
+    """Rotate x [T, H, D] in fp64 arithmetic; y defaults to a new tensor of x's dtype (y=x: in place)."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, H, D]")
+    T, H, D = x.shape
+    rd = rotary_dim if rotary_dim is not None else 2 * cos_rows.shape[-1]
+    _need(cos_rows, torch.float32, (T, rd // 2), "cos_rows")
+    _need(sin_rows, torch.float32, (T, rd // 2), "sin_rows")
+    if y is None:
+        y = torch.empty_like(x)
+    if not x.is_contiguous() or not y.is_contiguous() or tuple(y.shape) != tuple(x.shape):
+        raise ValueError("x and y must be contiguous [T, H, D]")
+    _check("yarn_rope_apply", lib.yarn_rope_apply(_ptr(cos_rows), _ptr(sin_rows), _ptr(x), _dt(x), _ptr(y), _dt(y),
+                                                  T, H, D, rd, _stream()))
+    return y
+
+
+def kv_cache_write_f4(cache: F4Cache, k, v, slot_mapping):
+    lib = load_library()
+    T = k.shape[0]
+    shape = (T, cache.num_kv_heads, cache.head_dim)
+    _need(k, torch.float32, shape, "k")
+    _need(v, torch.float32, shape, "v")
+    _need(slot_mapping, torch.int32, (T,), "slot_mapping")
+    c = cache._c()
+    _check("kv_cache_write_f4", lib.kv_cache_write_f4(C.byref(c), _ptr(k), _ptr(v), _ptr(slot_mapping), T,
+                                                      _stream()))
+
+
+def decode_workspace_size(B, Hq, num_kv_heads, head_dim, max_context_len, num_windows=1, window_tokens=0) -> int:
+    return load_library().paged_attn_decode_f4_workspace_size(B, Hq, num_kv_heads, head_dim, max_context_len,
+                                                              num_windows, window_tokens)
+
+
+def paged_attn_decode_f4(cache: F4Cache, q, page_table, context_lens, max_context_len: int, sm_scale: float,
+                         num_windows: int = 1, window_tokens: int = 0, out=None, out_m=None, out_l=None,
+                         workspace=None):
+    """Decode attention; returns (out [W, B, Hq, D], m [W, B, Hq], l [W, B, Hq])."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(q, torch.bfloat16, (B, Hq, D), "q")
+    _need(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    _need(context_lens, torch.int32, (B,), "context_lens")
+    W = num_windows
+    dev = q.device
+    if out is None:
+        out = torch.empty((W, B, Hq, D), dtype=torch.float32, device=dev)
+    if out_m is None:
+        out_m = torch.empty((W, B, Hq), dtype=torch.float32, device=dev)
+    if out_l is None:
+        out_l = torch.empty((W, B, Hq), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, (W, B, Hq, D), "out")
+    ws_need = decode_workspace_size(B, Hq, cache.num_kv_heads, cache.head_dim, max_context_len, W, window_tokens)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cache._c()
+    _check("paged_attn_decode_f4",
+           lib.paged_attn_decode_f4(C.byref(c), _ptr(q), _ptr(page_table), _ptr(context_lens), B, Hq,
+                                    page_table.shape[1], int(max_context_len), W, int(window_tokens),
+                                    float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _ptr(workspace), ws_bytes,
+                                    _stream()))
+    return out, out_m, out_l
+
+
+def lse_merge(m, l, o, out=None, out_m=None, out_l=None):
+    """Fold C partial states: m, l [C, R...], o [C, R..., D] -> (out [R..., D], M [R...], L [R...])."""
+    lib = load_library()
+    Cn = o.shape[0]
+    D = o.shape[-1]
+    rshape = tuple(o.shape[1:-1])
+    R = math.prod(rshape)
+    _need(m, torch.float32, (Cn,) + rshape, "m")
+    _need(l, torch.float32, (Cn,) + rshape, "l")
+    _need(o, torch.float32, None, "o")
+    dev = o.device
+    if out is None:
+        out = torch.empty(rshape + (D,), dtype=torch.float32, device=dev)
+    if out_m is None:
+        out_m = torch.empty(rshape, dtype=torch.float32, device=dev)
+    if out_l is None:
+        out_l = torch.empty(rshape, dtype=torch.float32, device=dev)
+    _check("lse_merge", lib.lse_merge(_ptr(m), _ptr(l), _ptr(o), Cn, R, D, _ptr(out), _ptr(out_m), _ptr(out_l),
+                                      _stream()))
+    return out, out_m, out_l
+
+
+def prefill_workspace_size(T, Hq, num_kv_heads, head_dim, pos0) -> int:
+    return load_library().paged_attn_prefill_f4_workspace_size(T, Hq, num_kv_heads, head_dim, pos0)
+
+
+def paged_attn_prefill_f4(cache: F4Cache, q, k_new, v_new, page_table, pos0: int, sm_scale: float, out=None,
+                          out_m=None, out_l=None, workspace=None):
+    """Write the chunk's K/V (if given) and attend causally; returns (out [T, Hq, D], m [T, Hq], l [T, Hq])."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    _need(q, torch.bfloat16, (T, Hq, D), "q")
+    if k_new is not None:
+        _need(k_new, torch.float32, (T, cache.num_kv_heads, cache.head_dim), "k_new")
+        _need(v_new, torch.float32, (T, cache.num_kv_heads, cache.head_dim), "v_new")
+    _need(page_table, torch.int32, None, "page_table")
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    if out_m is None:
+        out_m = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if out_l is None:
+        out_l = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    ws_need = prefill_workspace_size(T, Hq, cache.num_kv_heads, cache.head_dim, pos0)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cache._c()
+    _check("paged_attn_prefill_f4",
+           lib.paged_attn_prefill_f4(C.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(page_table),
+                                     page_table.numel(), T, Hq, int(pos0), float(sm_scale), _ptr(out), _ptr(out_m),
+                                     _ptr(out_l), _ptr(workspace), ws_bytes, _stream()))
+    return out, out_m, out_l

@@ -1,0 +1,88 @@
+// Internal declarations shared by the library's translation units (HIP path only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "f4kv.h"
+
+namespace f4kv {
+
+constexpr int kPage = 64;      // tokens per page
+constexpr int kBlock = 32;     // values per scale block
+constexpr int kHeadDim = 256;  // head_dim the attention kernels implement
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- scalar conversions (device) --------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, nearest-even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float f16bits_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// ---- kernel launchers (host); arguments already validated ------------------
+hipError_t launch_kv_write(const f4kv_cache& c, const float* k, const float* v,
+                           const int32_t* slots, int32_t T, hipStream_t s);
+
+// Same, with slot = page_table[(pos0 + t) / 64] * 64 + (pos0 + t) % 64.
+hipError_t launch_kv_write_paged(const f4kv_cache& c, const float* k, const float* v,
+                                 const int32_t* page_table, int32_t pos0, int32_t T, hipStream_t s);
+
+hipError_t launch_rope_table(const f4kv_yarn_params& p, double mscale, const int32_t* pos,
+                             int32_t n, float* cos_out, float* sin_out, hipStream_t s);
+
+hipError_t launch_rope_apply(const float* c, const float* sn, const void* x, int32_t xdt,
+                             void* y, int32_t ydt, int32_t T, int32_t H, int32_t D,
+                             int32_t rd, hipStream_t s);
+
+hipError_t launch_merge(const float* m, const float* l, const float* o, int32_t C, int32_t R,
+                        int32_t D, float* out, float* out_m, float* out_l, hipStream_t s);
+
+struct DecodePlan {
+  int32_t pages_per_window;  // pages a window spans at most
+  int32_t pages_per_split;   // pages one workgroup covers
+  int32_t splits;            // workgroups per (window, sequence, kv head)
+  size_t ws_bytes;           // partial states in the workspace (0 when splits == 1)
+};
+
+DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx,
+                       int32_t num_windows, int32_t window_tokens);
+
+hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
+                         const int32_t* ctx, int32_t B, int32_t Hq, int32_t max_pages,
+                         int32_t max_ctx, int32_t num_windows, int32_t window_tokens,
+                         float sm_scale, float* out, float* out_m, float* out_l,
+                         void* ws, const DecodePlan& plan, hipStream_t s);
+
+struct PrefillPlan {
+  int32_t q_tiles;      // query tiles of 32 positions
+  int32_t kv_splits;    // workgroups along the key range per query tile
+  size_t ws_bytes;
+};
+
+PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0);
+
+hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
+                          int32_t max_pages, int32_t T, int32_t Hq, int32_t pos0,
+                          float sm_scale, float* out, float* out_m, float* out_l,
+                          void* ws, const PrefillPlan& plan, hipStream_t s);
+
+}  // namespace f4kv

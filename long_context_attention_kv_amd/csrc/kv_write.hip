@@ -1,0 +1,159 @@
+// kv_cache_write_f4: fp32 keys/values -> paged F4 cells.
+//
+// Format from mistral.rs PR #2375 ("Changes by area" item 2): symmetric 4-bit
+// values (nibble - 8) * scale, 32 values per 16-byte row; error bound max_abs/16
+// ("Known limitations").  The scale is fp16(absmax / 8), nearest-even, saturated
+// at 65504; codes round x / s to nearest-even and clamp to [-8, 7].
+//
+// Exact rounding decisions: x is fp32 and s is fp16, so an inexact x / s lies at
+// least 2^-24 |x / s| away from any half-integer.  The quotient is therefore
+// formed in fp64 (correctly rounded, error <= 2^-53 relative), which decides
+// every tie and near-tie exactly; an fp32 quotient could land on a false tie.
+//
+// One thread owns one 32-value block of one token's K or V row: it writes the
+// block's 16 bytes (K) or eight 2-byte pieces (V) and its scale, so no byte is
+// shared between threads.
+#include "f4kv_internal.h"
+
+namespace f4kv {
+namespace {
+
+struct KvWriteArgs {
+  uint8_t* k_nib;
+  uint16_t* k_scale;
+  uint8_t* v_nib;
+  uint16_t* v_scale;
+  const float* k;
+  const float* v;
+  const int32_t* slots;      // slot per token, or null: use page_table and pos0
+  const int32_t* page_table;
+  int32_t pos0;
+  int64_t per_kind;  // T * H * (D / 32)
+  int32_t H, D, num_pages;
+};
+
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= 2 * a.per_kind) return;
+  const int kind = gid >= a.per_kind ? 1 : 0;  // 0 = K, 1 = V
+  const int64_t r = kind ? gid - a.per_kind : gid;
+  const int nb = a.D / kBlock;
+  const int c = static_cast<int>(r % nb);
+  const int64_t th = r / nb;
+  const int h = static_cast<int>(th % a.H);
+  const int64_t t = th / a.H;
+
+  int32_t slot;
+  if (a.slots) {
+    slot = a.slots[t];
+  } else {
+    const int64_t pos = a.pos0 + t;
+    const int32_t pg = a.page_table[pos / kPage];
+    slot = pg < 0 ? -1 : pg * kPage + static_cast<int32_t>(pos % kPage);
+  }
+  if (slot < 0 || slot >= static_cast<int64_t>(a.num_pages) * kPage) return;
+  const int page = slot / kPage;
+  const int off = slot % kPage;
+
+  const float4_t* src = reinterpret_cast<const float4_t*>(
+      (kind ? a.v : a.k) + (t * a.H + h) * a.D + c * kBlock);
+  float x[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock / 4; ++i) {
+    float4_t f = src[i];
+    x[4 * i + 0] = f.x;
+    x[4 * i + 1] = f.y;
+    x[4 * i + 2] = f.z;
+    x[4 * i + 3] = f.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(x[i]));
+
+  // absmax * 0.125 is exact in fp32; a single rounding to fp16 follows.
+  const _Float16 s16 = static_cast<_Float16>(fminf(amax * 0.125f, 65504.0f));
+  const double sd = static_cast<double>(static_cast<float>(s16));
+
+  uint32_t nib[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    int code = 0;
+    if (sd > 0.0) {
+      double qd = __builtin_rint(static_cast<double>(x[i]) / sd);
+      qd = fmin(fmax(qd, -8.0), 7.0);
+      code = static_cast<int>(qd);
+    }
+    nib[i] = static_cast<uint32_t>(code + 8);
+  }
+
+  const int64_t ph = static_cast<int64_t>(page) * a.H + h;
+  const uint16_t sbits = __builtin_bit_cast(uint16_t, s16);
+  if (kind == 0) {
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v |= nib[8 * d + e] << (4 * e);
+      w[d] = v;
+    }
+    uint8_t* dst = a.k_nib + ((ph * nb + c) * kPage + off) * 16;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    a.k_scale[(ph * kPage + off) * nb + c] = sbits;
+  } else {
+    const int quads = a.D / 4;
+    uint8_t* tile = a.v_nib + ph * (static_cast<int64_t>(kPage) * a.D / 2);
+    const int unit_c = off / 8;
+    const int byte_in_unit = 4 * ((off % 8) / 2) + 2 * (off % 2);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = c * 8 + q;  // dim quad 4j .. 4j+3
+      const uint32_t b0 = nib[4 * q + 0] | (nib[4 * q + 1] << 4);
+      const uint32_t b1 = nib[4 * q + 2] | (nib[4 * q + 3] << 4);
+      uint16_t* dst = reinterpret_cast<uint16_t*>(
+          tile + (static_cast<int64_t>(unit_c) * quads + j) * 16 + byte_in_unit);
+      *dst = static_cast<uint16_t>(b0 | (b1 << 8));
+    }
+    a.v_scale[(ph * kPage + off) * nb + c] = sbits;
+  }
+}
+
+}  // namespace
+
+namespace {
+hipError_t launch_common(const f4kv_cache& c, const float* k, const float* v, const int32_t* slots,
+                         const int32_t* page_table, int32_t pos0, int32_t T, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  KvWriteArgs a;
+  a.page_table = page_table;
+  a.pos0 = pos0;
+  a.k_nib = c.k_nib;
+  a.k_scale = c.k_scale;
+  a.v_nib = c.v_nib;
+  a.v_scale = c.v_scale;
+  a.k = k;
+  a.v = v;
+  a.slots = slots;
+  a.H = c.num_kv_heads;
+  a.D = c.head_dim;
+  a.num_pages = c.num_pages;
+  a.per_kind = static_cast<int64_t>(T) * a.H * (a.D / kBlock);
+  const int64_t total = 2 * a.per_kind;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(kv_write_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kv_write(const f4kv_cache& c, const float* k, const float* v, const int32_t* slots, int32_t T,
+                           hipStream_t s) {
+  return launch_common(c, k, v, slots, nullptr, 0, T, s);
+}
+
+hipError_t launch_kv_write_paged(const f4kv_cache& c, const float* k, const float* v, const int32_t* page_table,
+                                 int32_t pos0, int32_t T, hipStream_t s) {
+  return launch_common(c, k, v, nullptr, page_table, pos0, T, s);
+}
+
+}  // namespace f4kv

@@ -1,0 +1,156 @@
+"""The C ABI library loads, exports every declared symbol, and refuses bad arguments on the host.
+
+These run without a GPU: every call below fails validation before any HIP work.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import long_context_attention_kv_amd as f4
+from long_context_attention_kv_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "f4kv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(f4.library_path()):
+        import long_context_attention_kv_amd.build as bld
+        bld.build()
+    return f4.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 11, names
+    assert set(names) == set(f4.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    src = open(HEADER).read()
+    v = int(re.search(r"#define F4KV_ABI_VERSION (\d+)", src).group(1))
+    assert lib.f4kv_abi_version() == v
+
+
+def test_cache_bytes(lib):
+    total, parts = f4.cache_bytes(16384, 4, 256)
+    # per token and KV head: 128 bytes of nibbles + 8 fp16 scales, for K and for V
+    assert parts == (16384 * 4 * 64 * 128, 16384 * 4 * 64 * 16, 16384 * 4 * 64 * 128, 16384 * 4 * 64 * 16)
+    assert total == 16384 * 64 * 4 * 2 * 144
+    assert lib.f4kv_cache_bytes(1, 1, 48, None, None, None, None) == 0
+
+
+def _cache(ptr=16, pages=8, heads=4, dim=256, page=64):
+    return B._CacheC(ptr, ptr, ptr, ptr, pages, heads, dim, page)
+
+
+def _yarn(**kw):
+    d = dict(theta=1e7, rotary_dim=256, factor=4.0, orig_ctx=262144, beta_fast=32.0, beta_slow=1.0, mscale=0.0)
+    d.update(kw)
+    return B._YarnParamsC(**d)
+
+
+def _err(lib):
+    return lib.f4kv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(factor=0.5), "factor"),
+    (dict(factor=64.5), "factor"),
+    (dict(rotary_dim=255), "rotary_dim"),
+    (dict(theta=1.0), "theta"),
+    (dict(beta_fast=1.0, beta_slow=32.0), "beta"),
+    (dict(orig_ctx=0), "orig_ctx"),
+])
+def test_yarn_params_refused(lib, kw, needle):
+    p = _yarn(**kw)
+    r = lib.yarn_rope_table(C.byref(p), 16, 4, 16, 16, None)
+    assert r == 1 and needle in _err(lib)
+
+
+def test_yarn_factor_range_edges(lib):
+    # factor 64 is the largest accepted (ignis --model-rope-scaling: F in (1, 64]); n == 0 is a no-op
+    p = _yarn(factor=64.0)
+    assert lib.yarn_rope_table(C.byref(p), None, 0, None, None, None) == 0
+    p = _yarn(factor=1.0)
+    assert lib.yarn_rope_table(C.byref(p), None, 0, None, None, None) == 0
+    p = _yarn(factor=4.0)
+    assert lib.yarn_rope_table(C.byref(p), None, 5, None, None, None) == 1
+
+
+@pytest.mark.parametrize("field,val,needle", [
+    ("page_size", 32, "page_size"),
+    ("head_dim", 48, "head_dim"),
+    ("num_pages", 0, "num_pages"),
+    ("k_nib", 0, "NULL"),
+    ("v_scale", 8, "aligned"),
+])
+def test_cache_descriptor_refused(lib, field, val, needle):
+    c = _cache()
+    setattr(c, field, val)
+    r = lib.kv_cache_write_f4(C.byref(c), 16, 16, 16, 1, None)
+    assert r == 1 and needle in _err(lib)
+
+
+def test_writer_argument_checks(lib):
+    c = _cache()
+    assert lib.kv_cache_write_f4(C.byref(c), 16, 16, 16, 0, None) == 0          # empty: nothing to do
+    assert lib.kv_cache_write_f4(C.byref(c), None, 16, 16, 3, None) == 1
+    assert lib.kv_cache_write_f4(C.byref(c), 20, 16, 16, 3, None) == 1           # k misaligned
+    assert lib.kv_cache_write_f4(C.byref(c), 16, 16, 16, -1, None) == 1
+    assert lib.kv_cache_write_f4(None, 16, 16, 16, 1, None) == 1
+
+
+def _decode(lib, c, B_=1, Hq=16, max_pages=64, max_ctx=4096, W=1, wt=0, ws=None, ws_bytes=0, q=16, out=16):
+    return lib.paged_attn_decode_f4(C.byref(c), q, 16, 16, B_, Hq, max_pages, max_ctx, W, wt, 0.0625, out, None,
+                                    None, ws, ws_bytes, None)
+
+
+def test_decode_argument_checks(lib):
+    c = _cache()
+    assert _decode(lib, c, Hq=6) == 1 and "multiple" in _err(lib)
+    assert _decode(lib, c, max_ctx=64 * 64 + 1) == 1 and "max_pages" in _err(lib)
+    assert _decode(lib, c, W=4, wt=0) == 1 and "window" in _err(lib)
+    assert _decode(lib, c, W=2, wt=100) == 1 and "64" in _err(lib)
+    assert _decode(lib, c, Hq=12) == 2 and "1, 2, 4 or 8" in _err(lib)
+    c128 = _cache(dim=128)
+    assert _decode(lib, c128) == 2 and "head_dim" in _err(lib)
+    assert _decode(lib, c, q=8) == 1 and "aligned" in _err(lib)
+    assert _decode(lib, c, B_=0) == 0
+    need = lib.paged_attn_decode_f4_workspace_size(1, 16, 4, 256, 1 << 20, 16, 65536)
+    assert need > 0
+    assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=16, ws_bytes=need - 1) == 3
+    assert "workspace" in _err(lib)
+    assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=None, ws_bytes=need) == 3
+
+
+def test_merge_and_rope_apply_checks(lib):
+    assert lib.lse_merge(16, 16, 16, 0, 4, 256, 16, None, None, None) == 1
+    assert lib.lse_merge(16, 16, 16, 2, 4, 250, 16, None, None, None) == 1
+    assert lib.lse_merge(16, 16, 16, 2, 0, 256, 16, None, None, None) == 0
+    assert lib.yarn_rope_apply(16, 16, 16, 2, 16, 0, 1, 1, 256, 256, None) == 1   # bad dtype
+    assert lib.yarn_rope_apply(16, 16, 16, 0, 16, 0, 1, 1, 256, 300, None) == 1   # rotary_dim > D
+    assert lib.yarn_rope_apply(16, 16, 16, 0, 16, 1, 1, 1, 256, 256, None) == 1   # in place, dtypes differ
+
+
+def test_prefill_argument_checks(lib):
+    c = _cache()
+    f = lambda **kw: lib.paged_attn_prefill_f4(
+        C.byref(c), 16, kw.get("k", 16), kw.get("v", 16), 16, kw.get("mp", 64), kw.get("T", 64), kw.get("Hq", 16),
+        kw.get("pos0", 0), 0.0625, 16, None, None, None, 0, None)
+    assert f(pos0=64 * 64) == 1 and "max_pages" in _err(lib)
+    assert f(k=None) == 1 and "together" in _err(lib)
+    assert f(Hq=8) == 2
+    assert f(T=0) == 0

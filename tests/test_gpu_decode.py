@@ -1,0 +1,130 @@
+"""paged_attn_decode_f4 and lse_merge on the GPU vs the oracle (max |delta| <= 2e-3 x output RMS)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_kv_amd as f4
+import synth
+from oracle import attention as oatt
+from gpu_cases import (PagedSet, assert_attention_close, assert_states_close, bf16_tensor, cache_arrays_equal,
+                       oracle_decode, random_q)
+
+pytestmark = pytest.mark.gpu
+SM = 1.0 / 16.0
+
+
+def _run(ps: PagedSet, Hq, seed=0, W=1, wt=0, q_scale=1.0, max_ctx=None):
+    B = len(ps.lengths)
+    bits, qv = random_q(B, Hq, ps.D, seed, q_scale)
+    max_ctx = max(ps.lengths) if max_ctx is None else max_ctx
+    out, m, l = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), ps.gpu_lengths(), max_ctx,
+                                        SM, num_windows=W, window_tokens=wt)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle_decode(ps, qv, SM, num_windows=W, window_tokens=wt)
+    return (out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()), (ro, rm, rl)
+
+
+@pytest.mark.parametrize("lengths", [[1], [63], [64], [65], [130, 1, 700], [64 * 37 + 5]])
+def test_small_contexts(lengths):
+    ps = PagedSet(lengths, Hkv=4, seed=len(lengths) * 100 + lengths[0])
+    assert cache_arrays_equal(ps.gc, ps.oc) == []
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=lengths[0])
+    assert_attention_close(o, ro, f"lengths {lengths}")
+    assert_states_close(m, l, rm, rl, f"lengths {lengths}")
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 1), (8, 2)])
+def test_group_sizes(G, Hkv):
+    ps = PagedSet([300, 1024], Hkv=Hkv, seed=G)
+    (o, m, l), (ro, rm, rl) = _run(ps, G * Hkv, seed=G)
+    assert_attention_close(o, ro, f"G={G}")
+    assert_states_close(m, l, rm, rl, f"G={G}")
+
+
+def test_config0_shape():
+    # one sequence of 4,096 tokens in a permuted pool of 64 pages, 16 query / 4 KV heads
+    ps = PagedSet([4096], Hkv=4, seed=7, extra_pages=0)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=7)
+    assert_attention_close(o, ro, "config0")
+    assert_states_close(m, l, rm, rl, "config0")
+
+
+def test_windows_and_empty_windows():
+    ps = PagedSet([1000, 130, 4096], Hkv=4, seed=8)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=8, W=5, wt=1024)
+    # windows past a sequence's end are the merge identity
+    assert np.all(np.isneginf(m[1:, 0])) and np.all(l[1:, 0] == 0) and not o[1:, 0].any()
+    assert_attention_close(o, ro, "windows")
+    assert_states_close(m, l, rm, rl, "windows")
+    # folding the windows on the GPU gives the whole-context answer
+    out, M, L = f4.lse_merge(torch.from_numpy(m).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(o).cuda())
+    (wo, wm, wl), _ = _run(ps, 16, seed=8)
+    assert_attention_close(out.cpu().numpy(), wo[0], "window fold")
+
+
+def test_large_and_small_query_scale():
+    ps = PagedSet([777], Hkv=4, seed=9)
+    for sc in (1e-3, 30.0):
+        (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=9, q_scale=sc)
+        assert_attention_close(o, ro, f"q scale {sc}")
+        assert_states_close(m, l, rm, rl, f"q scale {sc}")
+
+
+def test_outliers_and_scaled_values():
+    ps = PagedSet([2000], Hkv=4, seed=10, outliers=True, v_scale=100.0)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=10)
+    assert_attention_close(o, ro, "outliers")
+
+
+def test_page_permutation_invariance_and_determinism():
+    ps = PagedSet([3000, 64], Hkv=4, seed=11)
+    bits, _ = random_q(2, 16, 256, 11)
+    q = bf16_tensor(bits)
+    a = f4.paged_attn_decode_f4(ps.gc, q, ps.gpu_page_table(), ps.gpu_lengths(), 3000, SM)[0]
+    b = f4.paged_attn_decode_f4(ps.gc, q, ps.gpu_page_table(), ps.gpu_lengths(), 3000, SM)[0]
+    assert torch.equal(a, b)
+    # the same tokens in a different physical placement give the same result bit for bit
+    ps2 = PagedSet([3000, 64], Hkv=4, seed=11, extra_pages=9, placement=5)
+    c = f4.paged_attn_decode_f4(ps2.gc, q, ps2.gpu_page_table(), ps2.gpu_lengths(), 3000, SM)[0]
+    assert torch.equal(a, c)
+
+
+def test_context_lens_beyond_bound_are_clamped():
+    ps = PagedSet([500], Hkv=4, seed=12)
+    bits, qv = random_q(1, 16, 256, 12)
+    lens = torch.tensor([10 ** 6], dtype=torch.int32, device="cuda")
+    o, m, l = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), lens, 500, SM)
+    ro, rm, rl = oracle_decode(ps, qv, SM)
+    assert_attention_close(o.cpu().numpy(), ro, "clamped")
+
+
+def test_zero_length_sequence():
+    ps = PagedSet([0, 100], Hkv=4, seed=13)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=13)
+    assert np.all(np.isneginf(m[0, 0])) and np.all(l[0, 0] == 0) and not o[0, 0].any()
+    assert_attention_close(o, ro, "zero length")
+
+
+@pytest.mark.parametrize("C,R", [(1, 3), (16, 16), (300, 5)])
+def test_lse_merge_vs_oracle(C, R):
+    g = synth.rng(500, C)
+    m = (g.standard_normal((C, R)) * 5).astype(np.float32)
+    l = g.uniform(0.5, 1000, (C, R)).astype(np.float32)
+    o = g.standard_normal((C, R, 256)).astype(np.float32)
+    m[0, 0] = -np.inf
+    l[0, 0] = 0.0
+    o[0, 0] = 0.0
+    if R > 1:
+        m[:, 1] = -np.inf
+        l[:, 1] = 0.0
+        o[:, 1] = 0.0
+    out, M, L = f4.lse_merge(torch.from_numpy(m).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(o).cuda())
+    out, M, L = out.cpu().numpy(), M.cpu().numpy(), L.cpu().numpy()
+    for r in range(R):
+        rm_, rl_, ro_ = oatt.merge_states(m[:, r], l[:, r], o[:, r])
+        if rl_ == 0:
+            assert np.isneginf(M[r]) and L[r] == 0 and not out[r].any()
+            continue
+        assert abs(M[r] - rm_) <= 1e-6 * max(1, abs(rm_))
+        assert abs(L[r] - rl_) <= 1e-5 * rl_
+        np.testing.assert_allclose(out[r], ro_, rtol=1e-5, atol=1e-5 * np.abs(ro_).max())

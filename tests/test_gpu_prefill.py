@@ -1,0 +1,84 @@
+"""paged_attn_prefill_f4 on the GPU vs the oracle (max |delta| <= 2e-3 x output RMS)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_kv_amd as f4
+import synth
+from oracle import attention as oatt
+from oracle import f4 as of4
+from gpu_cases import assert_attention_close, assert_states_close, bf16_tensor, bf16_values, cache_arrays_equal
+
+pytestmark = pytest.mark.gpu
+SM = 1.0 / 16.0
+PAGE = 64
+
+
+class Chunk:
+    """A sequence whose first pos0 tokens are cached; a chunk of T new tokens follows."""
+
+    def __init__(self, pos0, T, Hkv=4, G=4, D=256, seed=0, extra_pages=2):
+        g = synth.rng(600 + seed, 0)
+        n = pos0 + T
+        npg = (n + PAGE - 1) // PAGE
+        self.P = npg + extra_pages
+        perm = synth.page_permutation(g, self.P)
+        self.pt = perm[:npg].astype(np.int32)
+        self.pos0, self.T, self.Hkv, self.D, self.Hq = pos0, T, Hkv, D, G * Hkv
+        k_old = synth.normal_f32(g, (pos0, Hkv, D))
+        v_old = synth.normal_f32(g, (pos0, Hkv, D))
+        self.k_new = synth.normal_f32(g, (T, Hkv, D))
+        self.v_new = synth.normal_f32(g, (T, Hkv, D))
+        self.qbits = synth.f32_to_bf16_bits(synth.normal_f32(g, (T, self.Hq, D)))
+        t = np.arange(pos0)
+        old_slots = (self.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+        self.oc = of4.Cache(self.P, Hkv, D)
+        self.oc.write(k_old, v_old, old_slots)
+        self.gc = f4.F4Cache(self.P, Hkv, D)
+        if pos0:
+            f4.kv_cache_write_f4(self.gc, torch.from_numpy(k_old).cuda(), torch.from_numpy(v_old).cuda(),
+                                 torch.from_numpy(old_slots).cuda())
+
+    def run_gpu(self, write=True):
+        kn = torch.from_numpy(self.k_new).cuda() if write else None
+        vn = torch.from_numpy(self.v_new).cuda() if write else None
+        out = f4.paged_attn_prefill_f4(self.gc, bf16_tensor(self.qbits), kn, vn, torch.from_numpy(self.pt).cuda(),
+                                       self.pos0, SM)
+        torch.cuda.synchronize()
+        return [x.cpu().numpy() for x in out]
+
+    def run_oracle(self, rows=None):
+        t = np.arange(self.pos0, self.pos0 + self.T)
+        slots = (self.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+        self.oc.write(self.k_new, self.v_new, slots)
+        return oatt.prefill(self.oc, bf16_values(self.qbits), self.pt, self.pos0, SM, rows=rows)
+
+
+@pytest.mark.parametrize("pos0,T", [(0, 1), (0, 64), (100, 37), (64, 130), (1000, 200), (4000, 33)])
+def test_prefill_small(pos0, T):
+    ch = Chunk(pos0, T, seed=pos0 + T)
+    o, m, l = ch.run_gpu()
+    ro, rm, rl = ch.run_oracle()
+    assert cache_arrays_equal(ch.gc, ch.oc) == []
+    assert_attention_close(o, ro, f"prefill pos0={pos0} T={T}")
+    assert_states_close(m, l, rm, rl, f"prefill pos0={pos0} T={T}")
+
+
+def test_prefill_kv_already_written():
+    ch = Chunk(300, 70, seed=5)
+    t = np.arange(300, 370)
+    slots = (ch.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+    f4.kv_cache_write_f4(ch.gc, torch.from_numpy(ch.k_new).cuda(), torch.from_numpy(ch.v_new).cuda(),
+                         torch.from_numpy(slots).cuda())
+    o, m, l = ch.run_gpu(write=False)
+    ro, rm, rl = ch.run_oracle()
+    assert_attention_close(o, ro, "prefill, cache pre-written")
+
+
+def test_prefill_last_row_matches_decode():
+    ch = Chunk(2000, 96, seed=6)
+    o, m, l = ch.run_gpu()
+    lens = torch.tensor([2096], dtype=torch.int32, device="cuda")
+    q_last = bf16_tensor(ch.qbits[-1:])
+    d, dm, dl = f4.paged_attn_decode_f4(ch.gc, q_last, torch.from_numpy(ch.pt[None]).cuda(), lens, 2096, SM)
+    assert_attention_close(o[-1], d.cpu().numpy()[0, 0], "prefill last row vs decode")
