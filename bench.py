@@ -1,0 +1,385 @@
+"""Benchmark: F4 paged decode attention on one MI355X.
+
+One step is one decode step of the hybrid model's attention stack: 16 layers,
+3 lanes of 262,144 cached tokens, 16 query / 4 KV heads of 256, F4 KV, YaRN x4.
+Per layer: YaRN rows for the lanes' positions, rotation of the query and of the
+new key, F4 write of the new token, split-K paged decode folded by the
+log-sum-exp merge.  The printed value is KV-tokens attended per second over
+the timed steps; the inputs sit in HBM before timing starts.
+
+Also measured (same JSON line): the decode kernel against the HBM roofline,
+the 1,048,576-token decode in 16 windows of 65,536 folded by lse_merge, the
+ragged 8-sequence batch, the 2,048-query chunked prefill against the MFMA
+roofline, and the fp64 oracle on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import long_context_attention_kv_amd as f4  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "decode KV-tokens/s + achieved HBM GB/s (% of peak) for F4 paged attention"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+PAGE = 64
+HQ, HKV, D = 16, 4, 256
+SM = 1.0 / 16.0
+BYTES_PER_TOKEN_HEAD = 2 * (D // 2 + 2 * (D // 32))  # K and V: 128 B nibbles + 8 fp16 scales each
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def yarn_params(factor):
+    return f4.YarnParams(theta=1e7, rotary_dim=256, factor=factor, orig_ctx=262144, beta_fast=32.0, beta_slow=1.0)
+
+
+class DecodeLayer:
+    """One layer's cache for B lanes of given lengths, filled from seeded N(0,1) draws."""
+
+    def __init__(self, lengths, factor, gen, outliers, chunk=65536, dev="cuda"):
+        self.lengths = [int(x) for x in lengths]
+        pages = [(n + PAGE - 1) // PAGE for n in self.lengths]
+        self.num_pages = sum(pages)
+        self.max_pages = max(pages)
+        perm = torch.randperm(self.num_pages, generator=gen, device="cpu").to(torch.int32).numpy()
+        self.pt_np = synth.page_table_for(self.lengths, perm, self.max_pages)
+        self.pt = torch.from_numpy(self.pt_np).to(dev)
+        self.ctx = torch.tensor(self.lengths, dtype=torch.int32, device=dev)
+        self.cache = f4.F4Cache(self.num_pages, HKV, D, device=dev)
+        yp = yarn_params(factor)
+        cols = None
+        if outliers:
+            cols = torch.randperm(HKV * D, generator=gen)[: round(0.01 * HKV * D)].to(dev)
+        cgen = torch.Generator(device=dev)
+        cgen.manual_seed(int(torch.randint(0, 2 ** 31, (1,), generator=gen)))
+        for b, n in enumerate(self.lengths):
+            for t0 in range(0, n, chunk):
+                t1 = min(n, t0 + chunk)
+                T = t1 - t0
+                k = torch.randn((T, HKV, D), generator=cgen, device=dev, dtype=torch.float32)
+                v = torch.randn((T, HKV, D), generator=cgen, device=dev, dtype=torch.float32)
+                if cols is not None:
+                    k.view(T, -1)[:, cols] *= 8.0
+                    v.view(T, -1)[:, cols] *= 8.0
+                pos = torch.arange(t0, t1, dtype=torch.int32, device=dev)
+                c, s = f4.yarn_rope_table(yp, pos)
+                f4.yarn_rope_apply(c, s, k, y=k)
+                tt = torch.arange(t0, t1, device=dev)
+                slots = (self.pt[b, tt // PAGE].to(torch.int64) * PAGE + tt % PAGE).to(torch.int32)
+                f4.kv_cache_write_f4(self.cache, k, v, slots)
+        torch.cuda.synchronize()
+
+
+def gb(x):
+    return x / 1e9
+
+
+def decode_algorithmic_bytes(lengths, windows=1):
+    kv = sum(lengths) * HKV * BYTES_PER_TOKEN_HEAD
+    q = len(lengths) * HQ * D * 2
+    pt = sum((n + PAGE - 1) // PAGE for n in lengths) * 4
+    out = windows * len(lengths) * HQ * (D + 2) * 4
+    return kv + q + pt + out
+
+
+def run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs):
+    """One step: YaRN rows, rotations, new-token writes, decode per layer."""
+    yp = yarn_params(factor)
+    c, s = f4.yarn_rope_table(yp, positions)
+    for i, L in enumerate(layers):
+        q = f4.yarn_rope_apply(c, s, q_raw[i])
+        k = f4.yarn_rope_apply(c, s, k_new[i])
+        f4.kv_cache_write_f4(L.cache, k, v_new[i], L.new_slots)
+        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, max(L.lengths), SM, out=outs[i][0], out_m=outs[i][1],
+                                out_l=outs[i][2], workspace=ws)
+
+
+def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 1)
+    t0 = time.time()
+    layers = []
+    for i in range(n_layers):
+        L = DecodeLayer([ctx] * lanes, factor, gen, outliers=True)
+        pos = torch.full((lanes,), ctx - 1, dtype=torch.int64, device=dev)
+        L.new_slots = (L.pt[torch.arange(lanes, device=dev), pos // PAGE].to(torch.int64) * PAGE + pos % PAGE).to(
+            torch.int32)
+        layers.append(L)
+    log(f"config1 cache filled: {n_layers} layers x {lanes} x {ctx} tokens, "
+        f"{gb(sum(L.cache.nbytes() for L in layers)):.2f} GB in {time.time() - t0:.1f}s")
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 11)
+    q_raw = [torch.randn((lanes, HQ, D), generator=g, device=dev).to(torch.bfloat16) for _ in layers]
+    k_new = [torch.randn((lanes, HKV, D), generator=g, device=dev) for _ in layers]
+    v_new = [torch.randn((lanes, HKV, D), generator=g, device=dev) for _ in layers]
+    positions = torch.full((lanes,), ctx - 1, dtype=torch.int32, device=dev)
+    ws_bytes = f4.decode_workspace_size(lanes, HQ, HKV, D, ctx)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [(torch.empty((1, lanes, HQ, D), device=dev), torch.empty((1, lanes, HQ), device=dev),
+             torch.empty((1, lanes, HQ), device=dev)) for _ in layers]
+
+    for _ in range(warmup):
+        run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs)
+    torch.cuda.synchronize()
+    # timed steps; the decode launches are bracketed by events on the launch stream
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    end_ev = torch.cuda.Event(enable_timing=True)
+    start_ev.record(stream)
+    yp = yarn_params(factor)
+    for st in range(steps):
+        c, s = f4.yarn_rope_table(yp, positions)
+        for i, L in enumerate(layers):
+            q = f4.yarn_rope_apply(c, s, q_raw[i])
+            k = f4.yarn_rope_apply(c, s, k_new[i])
+            f4.kv_cache_write_f4(L.cache, k, v_new[i], L.new_slots)
+            ev[st][i][0].record(stream)
+            f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, ctx, SM, out=outs[i][0], out_m=outs[i][1],
+                                    out_l=outs[i][2], workspace=ws)
+            ev[st][i][1].record(stream)
+    end_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = start_ev.elapsed_time(end_ev)
+    dec_ms = [ev[st][i][0].elapsed_time(ev[st][i][1]) for st in range(steps) for i in range(n_layers)]
+    ms_step = max(gpu_ms, wall * 1e3) / steps
+    tokens = n_layers * lanes * ctx
+    dec_avg_ms = float(np.mean(dec_ms))
+    dec_bytes = decode_algorithmic_bytes([ctx] * lanes)
+    return {
+        "ms_per_step": ms_step,
+        "kv_tokens_per_step": tokens,
+        "value": tokens / (ms_step / 1e3),
+        "decode_call_ms_avg": dec_avg_ms,
+        "decode_call_ms_min": float(np.min(dec_ms)),
+        "decode_bytes_per_call": dec_bytes,
+        "decode_gbs": dec_bytes / (dec_avg_ms / 1e3) / 1e9,
+        "layers": layers,
+        "out_sample": outs[0][0][0, 0, 0, :4].float().cpu().tolist(),
+    }
+
+
+def bench_1m(iters=10):
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 2)
+    ctx, W, wt = 1048576, 16, 65536
+    L = DecodeLayer([ctx], 4.0, gen, outliers=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 12)
+    q = torch.randn((1, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(max(16, f4.decode_workspace_size(1, HQ, HKV, D, ctx, W, wt)), dtype=torch.uint8, device=dev)
+    o = torch.empty((W, 1, HQ, D), device=dev)
+    m = torch.empty((W, 1, HQ), device=dev)
+    l = torch.empty((W, 1, HQ), device=dev)
+
+    def once():
+        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, ctx, SM, num_windows=W, window_tokens=wt, out=o,
+                                out_m=m, out_l=l, workspace=ws)
+        return f4.lse_merge(m, l, o)
+
+    for _ in range(3):
+        once()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        once()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    by = decode_algorithmic_bytes([ctx], windows=W)
+    del L
+    return {"workload": "1 x 1,048,576 tokens, 16 windows of 65,536 + lse_merge", "ms": ms,
+            "kv_tokens_per_s": ctx / (ms / 1e3), "gbs": by / (ms / 1e3) / 1e9,
+            "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_ragged(iters=20):
+    dev = "cuda"
+    lengths = synth.ragged_lengths(4)
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 4)
+    L = DecodeLayer(lengths, 1.220703125, gen, outliers=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 14)
+    q = torch.randn((len(lengths), HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    mx = max(lengths)
+    ws = torch.empty(max(16, f4.decode_workspace_size(len(lengths), HQ, HKV, D, mx)), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, mx, SM, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, mx, SM, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    by = decode_algorithmic_bytes(lengths)
+    return {"workload": "8 ragged sequences, log-uniform 1,024..320,000", "lengths": lengths, "ms": ms,
+            "kv_tokens_per_s": sum(lengths) / (ms / 1e3), "gbs": by / (ms / 1e3) / 1e9,
+            "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def prefill_flops(T, pos0):
+    return 4 * D * HQ * sum(pos0 + i + 1 for i in range(T))
+
+
+def bench_prefill(iters=5, T=2048, window=131072):
+    dev = "cuda"
+    pos0 = window - T
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 3)
+    # one sequence's window of 2,048 pages placed by a random permutation of the pool;
+    # the first 129,024 tokens are written before timing, the chunk's own inside each call
+    n_pages = window // PAGE
+    perm = torch.randperm(n_pages, generator=gen).to(torch.int32)
+    cache = f4.F4Cache(n_pages, HKV, D, device=dev)
+    pt = perm.to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 13)
+    for t0 in range(0, pos0, 65536):
+        t1 = min(pos0, t0 + 65536)
+        k = torch.randn((t1 - t0, HKV, D), generator=g, device=dev)
+        v = torch.randn((t1 - t0, HKV, D), generator=g, device=dev)
+        pos = torch.arange(t0, t1, dtype=torch.int32, device=dev)
+        c, s = f4.yarn_rope_table(yarn_params(4.0), pos)
+        f4.yarn_rope_apply(c, s, k, y=k)
+        tt = torch.arange(t0, t1, device=dev)
+        f4.kv_cache_write_f4(cache, k, v, (pt[tt // PAGE].to(torch.int64) * PAGE + tt % PAGE).to(torch.int32))
+    q = torch.randn((T, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    kn = torch.randn((T, HKV, D), generator=g, device=dev)
+    vn = torch.randn((T, HKV, D), generator=g, device=dev)
+    ws = torch.empty(max(16, f4.prefill_workspace_size(T, HQ, HKV, D, pos0)), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, HQ, D), device=dev)
+    for _ in range(2):
+        f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    fl = prefill_flops(T, pos0)
+    tf = fl / (ms / 1e3) / 1e12
+    return {"workload": "2,048 queries at 129,024..131,071 over a 131,072-token causal window (write included)",
+            "ms": ms, "tflops": tf, "mfma_frac": tf / MFMA_F16_PEAK_TFLOPS, "flops": fl}
+
+
+def cpu_baseline(sample_tokens=32768):
+    """The fp64 oracle on a bounded sample: one lane, all 4 KV heads, sample_tokens cached tokens."""
+    from oracle import attention as oatt
+    from oracle import f4 as of4
+    from oracle import yarn as oyarn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    g = synth.rng(1, 7)
+    n = sample_tokens
+    k = synth.normal_f32(g, (n, HKV, D))
+    v = synth.normal_f32(g, (n, HKV, D))
+    cols = synth.outlier_columns(g, HKV, D)
+    synth.apply_outliers(k, cols)
+    synth.apply_outliers(v, cols)
+    spec = synth.YarnSpec(factor=4.0)
+    pos = np.arange(n)
+    cs, sn = oyarn.yarn_table(spec, pos)
+    k = oyarn.rope_apply(k, cs, sn, 256).astype(np.float32)
+    pages = n // PAGE
+    cache = of4.Cache(pages, HKV, D)
+    perm = synth.page_permutation(g, pages)
+    cache.write(k, v, (perm[pos // PAGE].astype(np.int64) * PAGE + pos % PAGE))
+    q = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.normal_f32(g, (1, HQ, D)))).astype(np.float64)
+    t0 = time.perf_counter()
+    oatt.decode(cache, q, perm[None, :], [n], SM)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "KV-tokens/s", "cores": threads if threads else len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"1 lane x {n} tokens x 4 KV heads (16 query heads), one layer of the same recipe "
+                      f"(N(0,1), 1% outlier channels x8, YaRN x4), host-generated; {dt:.1f} s",
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 1M, ragged and prefill measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    f4.load_library()
+    log(f"device {torch.cuda.get_device_name(0)}")
+    r = bench_config1(args.steps, args.warmup)
+    log(f"config1: {r['ms_per_step']:.3f} ms/step, {r['value'] / 1e9:.3f} G KV-tokens/s, decode call "
+        f"{r['decode_call_ms_avg'] * 1e3:.1f} us -> {r['decode_gbs']:.0f} GB/s")
+    del r["layers"]
+    torch.cuda.empty_cache()
+    extra = {}
+    if not args.no_extra:
+        extra["decode_1m_windows"] = bench_1m()
+        log("1M:", extra["decode_1m_windows"])
+        torch.cuda.empty_cache()
+        extra["decode_ragged"] = bench_ragged()
+        log("ragged:", extra["decode_ragged"])
+        torch.cuda.empty_cache()
+        extra["prefill"] = bench_prefill()
+        log("prefill:", extra["prefill"])
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_tokens)
+        log("cpu:", cpu)
+    line = {
+        "metric": METRIC,
+        "value": r["value"],
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode: 16 layers x 3 lanes x 262,144 cached tokens, 16 query / 4 KV heads, "
+                               "head_dim 256, 64-token pages, F4 KV, YaRN x4, 1% outlier channels x8",
+                   "lanes": 3, "context": 262144, "layers": 16},
+        "roofline": {"bound": "hbm", "achieved": r["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["decode_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "paged_attn_decode_f4 call (split kernel + fold)",
+                     "bytes_per_launch": r["decode_bytes_per_call"], "launch_ms_avg": r["decode_call_ms_avg"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

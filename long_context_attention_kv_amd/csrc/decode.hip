@@ -25,10 +25,14 @@
 //  * values: lane = 4 consecutive channels.  The V tile stores 8 tokens x 4
 //    channels per 16-byte unit, two tokens per dword, so the same AND trick
 //    yields fp16 pairs over two tokens and a dot product accumulates
-//    p_t s_t (n_t - 8) over token pairs.  The weights p_t * s_t (softmax weight
-//    times the token's block scale) travel from the key phase to the value
-//    phase through LDS as fp16; the "- 8" is corrected once per page with the
-//    page's summed weights.
+//    p_t s_t (n_t - 8) over token pairs.  The weights w = p_t * s_t (softmax
+//    weight times the token's block scale) travel from the key phase to the
+//    value phase through LDS as an fp16 pair hi + lo (hi = fp16(w), lo =
+//    fp16(w - hi)), and each product is taken twice, once per part: a single
+//    fp16 weight (11 bits) leaves ~2e-3 of the output RMS on channels whose
+//    values are many times the others' (outlier channels), the split keeps
+//    ~22 bits.  The "- 8" is corrected once per page with the page's summed
+//    weights.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
 #include "f4kv_internal.h"
@@ -106,7 +110,7 @@ struct __align__(16) DecodeSmem {
   int32_t qexp[G];
   union alignas(16) {
     float qf[G][kHeadDim];                   // prologue staging
-    uint16_t w[kWaves][G][8][kWRow];         // per-wave weight transpose
+    uint16_t w[kWaves][2][G][8][kWRow];      // per-wave weight transpose (hi, lo)
     float fold[kWaves][G][kHeadDim];         // epilogue: per-wave outputs
   } u;
   float fold_m[kWaves][G];
@@ -293,7 +297,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const uint32_t sw = word(vs, c >> 1);
       const float sv = (c & 1) ? f16_hi(sw) : f16_lo(sw);
 #pragma unroll
-      for (int h = 0; h < G; ++h) sm.u.w[wave][h][c][lane] = f32_to_f16bits(p[h] * sv);
+      for (int h = 0; h < G; ++h) {
+        const float w = p[h] * sv;
+        const _Float16 hi = static_cast<_Float16>(w);
+        const _Float16 lo = static_cast<_Float16>(w - static_cast<float>(hi));
+        sm.u.w[wave][0][h][c][lane] = __builtin_bit_cast(uint16_t, hi);
+        sm.u.w[wave][1][h][c][lane] = __builtin_bit_cast(uint16_t, lo);
+      }
     }
     lds_wave_sync();
 
@@ -305,9 +315,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       pin(vq[ct]);
-      uint4 wv[G];
+      uint4 wh[G], wl[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) wv[h] = *reinterpret_cast<const uint4*>(&sm.u.w[wave][h][cj][ct * 8]);
+      for (int h = 0; h < G; ++h) {
+        wh[h] = *reinterpret_cast<const uint4*>(&sm.u.w[wave][0][h][cj][ct * 8]);
+        wl[h] = *reinterpret_cast<const uint4*>(&sm.u.w[wave][1][h][cj][ct * 8]);
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t wd = word(vq[ct], k);
@@ -318,22 +331,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const uint32_t v3 = w8 & 0x00F000F0u;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const uint32_t wp = word(wv[h], k);
-          o[h][0] = dot2(v0, wp, o[h][0]);
-          o[h][1] = dot2(v1, wp, o[h][1]);
-          o[h][2] = dot2(v2, wp, o[h][2]);
-          o[h][3] = dot2(v3, wp, o[h][3]);
+          const uint32_t hp = word(wh[h], k);
+          const uint32_t lp2 = word(wl[h], k);
+          o[h][0] = dot2(v0, lp2, dot2(v0, hp, o[h][0]));
+          o[h][1] = dot2(v1, lp2, dot2(v1, hp, o[h][1]));
+          o[h][2] = dot2(v2, lp2, dot2(v2, hp, o[h][2]));
+          o[h][3] = dot2(v3, lp2, dot2(v3, hp, o[h][3]));
         }
       }
     }
     // "- 8" correction: the page's summed weights of block cj
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(&sm.u.w[wave][h][cj][sub * 8]);
+      const uint4 wv = *reinterpret_cast<const uint4*>(&sm.u.w[wave][0][h][cj][sub * 8]);
+      const uint4 wu = *reinterpret_cast<const uint4*>(&sm.u.w[wave][1][h][cj][sub * 8]);
       float ws = dot2(wv.x, kOne2, 0.0f);
       ws = dot2(wv.y, kOne2, ws);
       ws = dot2(wv.z, kOne2, ws);
       ws = dot2(wv.w, kOne2, ws);
+      ws = dot2(wu.x, kOne2, ws);
+      ws = dot2(wu.y, kOne2, ws);
+      ws = dot2(wu.z, kOne2, ws);
+      ws = dot2(wu.w, kOne2, ws);
       ws += __shfl_xor(ws, 1, 64);
       ws += __shfl_xor(ws, 2, 64);
       ws += __shfl_xor(ws, 4, 64);
