@@ -35,6 +35,8 @@
 //    weights.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
+#include <atomic>
+
 #include "f4kv_internal.h"
 
 namespace f4kv {
@@ -42,9 +44,18 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWRow = 72;  // fp16 weights per (head, block) row: 64 tokens + 16 B pad
+constexpr int kWRow = 68;  // fp32 weights per (head, block) row: 64 tokens + 16 B pad
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Query operands of one (sequence, KV head), prepared once per call and read by
+// the decode kernel with scalar loads (the same for every lane).
+template <int G>
+struct __align__(64) QPrep {
+  uint32_t pair[G][8][4][4];  // fp16 pairs [head][block][dword][pair], scaled by 2^e_h
+  float qinit[G][8];          // -8 * 2^-24 * sum of the block's scaled query values
+  float kscale[G];            // 2^(24 - e_h) * sm_scale * log2(e)
+};
 
 struct DecodeArgs {
   const uint8_t* k_nib;
@@ -67,9 +78,38 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                 false);
 }
 
+// DPP lane permutations within a row of 16 lanes (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within each row
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF,
+                                                               false));
+}
+
+// Max over the 64 lanes, returned in every lane: DPP within rows of 16, then
+// the four row results read into scalars.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Sum over each group of 8 consecutive lanes, returned in all 8.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
   return x;
 }
 
@@ -102,27 +142,75 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One workgroup per (sequence, KV head): query rows -> QPrep.
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* __restrict__ q,
+                                                               QPrep<G>* __restrict__ out, int32_t Hq,
+                                                               int32_t Hkv, float qk_scale) {
+  __shared__ float qf[G][kHeadDim];
+  __shared__ int32_t qexp[G];
+  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  QPrep<G>& P = out[blockIdx.x];
+  const uint16_t* qsrc = q + (static_cast<int64_t>(b) * Hq + g * G) * kHeadDim;
+  for (int i = tid; i < G * kHeadDim; i += kThreads) qf[i / kHeadDim][i % kHeadDim] = bf16_to_f32(qsrc[i]);
+  __syncthreads();
+  for (int h = wave; h < G; h += kWaves) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mx = fmaxf(mx, fabsf(qf[h][lane + 64 * k]));
+    mx = wave_max(mx);
+    if (lane == 0) {
+      int e = 0;
+      if (mx > 0.0f) {
+        int ex;
+        frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+        e = 11 - ex;      // scaled max in [2^10, 2^11)
+      }
+      qexp[h] = e;
+      P.kscale[h] = ldexpf(qk_scale, 24 - e);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * 128; i += kThreads) {
+    const int h = i / 128, r = i % 128;
+    const int c = r / 16, k = (r / 4) % 4, p = r % 4;
+    // pair p of dword k holds channels (base + p, base + p + 4); odd p are the x16 slots
+    const int base = 32 * c + 8 * k + p;
+    const float sc = ldexpf((p & 1) ? 0.0625f : 1.0f, qexp[h]);
+    const _Float16 lo = static_cast<_Float16>(qf[h][base] * sc);
+    const _Float16 hi = static_cast<_Float16>(qf[h][base + 4] * sc);
+    P.pair[h][c][k][p] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+  }
+  for (int i = tid; i < G * 8; i += kThreads) {
+    const int h = i / 8, c = i % 8;
+    float sum = 0.0f;
+    for (int d = 0; d < kBlock; ++d) {
+      const float v = qf[h][32 * c + d];
+      // the value each channel contributes through its fp16 operand
+      const float rep = (d & 1) ? 16.0f * static_cast<float>(static_cast<_Float16>(v * ldexpf(0.0625f, qexp[h])))
+                                : static_cast<float>(static_cast<_Float16>(v * ldexpf(1.0f, qexp[h])));
+      sum += rep;
+    }
+    P.qinit[h][c] = -8.0f * ldexpf(sum, -24);
+  }
+}
+
 template <int G>
 struct __align__(16) DecodeSmem {
-  alignas(16) uint32_t q[G][8][4][4];  // fp16 query pairs [head][block][dword][pair]
-  float qinit[G][8];       // accumulator start per (head, block)
-  float kscale[G];         // 2^(24 - e_h) * sm_scale * log2(e)
-  int32_t qexp[G];
   union alignas(16) {
-    float qf[G][kHeadDim];                   // prologue staging
-    uint16_t w[kWaves][2][G][8][kWRow];      // per-wave weight transpose (hi, lo)
-    float fold[kWaves][G][kHeadDim];         // epilogue: per-wave outputs
+    float w[kWaves][G][8][kWRow];     // per-wave weight transpose [head][block][token]
+    float fold[kWaves][G][kHeadDim];  // epilogue: per-wave outputs
   } u;
   float fold_m[kWaves][G];
   float fold_l[kWaves][G];
 };
 
-static_assert(offsetof(DecodeSmem<1>, u) % 16 == 0, "weight rows must be 16-byte aligned");
-static_assert(offsetof(DecodeSmem<4>, u) % 16 == 0, "weight rows must be 16-byte aligned");
-static_assert((kWRow * 2) % 16 == 0, "weight rows must be 16-byte aligned");
+static_assert((kWRow * 4) % 16 == 0, "weight rows must be 16-byte aligned");
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QPrep<G>* __restrict__ qprep) {
   __shared__ DecodeSmem<G> sm;
   const int split = blockIdx.x;
   const int b = blockIdx.y / a.Hkv;
@@ -154,55 +242,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---- prologue: query rows -> scaled fp16 pairs in LDS --------------------
-  const uint16_t* qsrc = a.q + (static_cast<int64_t>(b) * a.Hq + g * G) * kHeadDim;
-  for (int i = tid; i < G * kHeadDim; i += kThreads)
-    sm.u.qf[i / kHeadDim][i % kHeadDim] = bf16_to_f32(qsrc[i]);
-  __syncthreads();
-  for (int h = wave; h < G; h += kWaves) {
-    float mx = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) mx = fmaxf(mx, fabsf(sm.u.qf[h][lane + 64 * k]));
-    mx = wave_max(mx);
-    if (lane == 0) {
-      int e = 0;
-      if (mx > 0.0f) {
-        int ex;
-        frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
-        e = 11 - ex;      // scaled max in [2^10, 2^11)
-      }
-      sm.qexp[h] = e;
-      sm.kscale[h] = ldexpf(a.qk_scale, 24 - e);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < G * 128; i += kThreads) {
-    const int h = i / 128, r = i % 128;
-    const int c = r / 16, k = (r / 4) % 4, P = r % 4;
-    // pair P of dword k holds channels (base + P, base + P + 4); odd P are the x16 slots
-    const int base = 32 * c + 8 * k + P;
-    const float sc = ldexpf((P & 1) ? 0.0625f : 1.0f, sm.qexp[h]);
-    const _Float16 lo = static_cast<_Float16>(sm.u.qf[h][base] * sc);
-    const _Float16 hi = static_cast<_Float16>(sm.u.qf[h][base + 4] * sc);
-    sm.q[h][c][k][P] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-  }
-  for (int i = tid; i < G * 8; i += kThreads) {
-    const int h = i / 8, c = i % 8;
-    float sum = 0.0f;
-    for (int d = 0; d < kBlock; ++d) {
-      const float v = sm.u.qf[h][32 * c + d];
-      // the value each channel contributes through its fp16 operand
-      const float rep = (d & 1) ? 16.0f * static_cast<float>(static_cast<_Float16>(
-                                              v * ldexpf(0.0625f, sm.qexp[h])))
-                                : static_cast<float>(static_cast<_Float16>(v * ldexpf(1.0f, sm.qexp[h])));
-      sum += rep;
-    }
-    sm.qinit[h][c] = -8.0f * ldexpf(sum, -24);
-  }
-  __syncthreads();
-
-  // ---- main loop ----------------------------------------------------------
+  const QPrep<G>* QP = qprep + blockIdx.y;
   float m_run[G], l_lane[G], o[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -214,15 +254,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int cj = lane >> 3;  // block holding this lane's 4 value channels
   const int sub = lane & 7;
   const int32_t* ptrow = a.pt + static_cast<int64_t>(b) * a.max_pages;
-  const uint32_t kOne2 = 0x3C003C00u;  // fp16 pair (1, 1)
 
   for (int lp = pbeg + wave; lp < pend; lp += kWaves) {
-    // The query pairs are re-read from LDS every page (broadcast reads).  An
-    // offset the compiler cannot see through keeps it from hoisting all of them
-    // out of the loop into hundreds of registers.
+    // The query operands are re-read (scalar loads) every page.  An offset the
+    // compiler cannot see through keeps it from hoisting all 512 of them out
+    // of the loop, which would spill.
     int qoff = 0;
-    asm volatile("" : "+v"(qoff));
-    const char* qbase = reinterpret_cast<const char*>(&sm.q[0][0][0][0]) + qoff;
+    asm volatile("" : "+s"(qoff));
+    const QPrep<G>* qp = reinterpret_cast<const QPrep<G>*>(reinterpret_cast<const char*>(QP) + qoff);
     int32_t pid = ptrow[lp];
     // an out-of-range page id reads page 0 and contributes nothing
     const bool pvalid = static_cast<uint32_t>(pid) < static_cast<uint32_t>(a.num_pages);
@@ -247,13 +286,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h) logit[h] = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+      // one block's query operands (G x 16 dwords) in SGPRs at a time
+      __builtin_amdgcn_sched_barrier(0);
+      int qo = 0;
+      asm volatile("" : "+s"(qo));
+      const QPrep<G>* qb = reinterpret_cast<const QPrep<G>*>(reinterpret_cast<const char*>(qp) + qo);
       pin(kq[c]);
-      __builtin_amdgcn_sched_barrier(0);  // one block's query reads in flight at a time
       const uint32_t sw = word(ks, c >> 1);
       const float sc = (c & 1) ? f16_hi(sw) : f16_lo(sw);
       float acc[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = sm.qinit[h][c];
+      for (int h = 0; h < G; ++h) acc[h] = qb->qinit[h][c];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t wd = word(kq[c], k);
@@ -264,11 +307,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const uint32_t p3 = w8 & 0x00F000F0u;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const uint4 qv = *reinterpret_cast<const uint4*>(qbase + ((h * 8 + c) * 4 + k) * 16);
-          acc[h] = dot2(p0, qv.x, acc[h]);
-          acc[h] = dot2(p1, qv.y, acc[h]);
-          acc[h] = dot2(p2, qv.z, acc[h]);
-          acc[h] = dot2(p3, qv.w, acc[h]);
+          acc[h] = dot2(p0, qb->pair[h][c][k][0], acc[h]);
+          acc[h] = dot2(p1, qb->pair[h][c][k][1], acc[h]);
+          acc[h] = dot2(p2, qb->pair[h][c][k][2], acc[h]);
+          acc[h] = dot2(p3, qb->pair[h][c][k][3], acc[h]);
         }
       }
 #pragma unroll
@@ -281,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h) {
       // additive mask: written as a select, the compiler turns the whole key
       // phase into a branch on the token's validity
-      const float s = fmaf(logit[h], sm.kscale[h], tmask);
+      const float s = fmaf(logit[h], qp->kscale[h], tmask);
       const float mn = fmaxf(m_run[h], wave_max(s));
       // mn == -inf only while no valid token has been seen: keep everything at 0
       const float ms = mn == -INFINITY ? 0.0f : mn;
@@ -291,19 +333,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       m_run[h] = mn;
     }
 
-    // weights p * s_v per (head, block) to LDS, transposed to [head][block][token]
+    // weights p * s_v per (head, block) to LDS in fp32, transposed to [head][block][token]
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t sw = word(vs, c >> 1);
       const float sv = (c & 1) ? f16_hi(sw) : f16_lo(sw);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float w = p[h] * sv;
-        const _Float16 hi = static_cast<_Float16>(w);
-        const _Float16 lo = static_cast<_Float16>(w - static_cast<float>(hi));
-        sm.u.w[wave][0][h][c][lane] = __builtin_bit_cast(uint16_t, hi);
-        sm.u.w[wave][1][h][c][lane] = __builtin_bit_cast(uint16_t, lo);
-      }
+      for (int h = 0; h < G; ++h) sm.u.w[wave][h][c][lane] = p[h] * sv;
     }
     lds_wave_sync();
 
@@ -315,47 +351,39 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       pin(vq[ct]);
-      uint4 wh[G], wl[G];
+      float4_t wa[G], wb[G];  // weights of tokens 8ct..8ct+3 and 8ct+4..8ct+7
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        wh[h] = *reinterpret_cast<const uint4*>(&sm.u.w[wave][0][h][cj][ct * 8]);
-        wl[h] = *reinterpret_cast<const uint4*>(&sm.u.w[wave][1][h][cj][ct * 8]);
+        wa[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][ct * 8]);
+        wb[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][ct * 8 + 4]);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t wd = word(vq[ct], k);
-        const uint32_t v0 = wd & 0x000F000Fu;
-        const uint32_t v1 = wd & 0x00F000F0u;
+        // fp16 pairs (token 8ct+2k, token 8ct+2k+1) of channels 0..3
+        const half2_t v0 = __builtin_bit_cast(half2_t, wd & 0x000F000Fu);
+        const half2_t v1 = __builtin_bit_cast(half2_t, wd & 0x00F000F0u);
         const uint32_t w8 = wd >> 8;
-        const uint32_t v2 = w8 & 0x000F000Fu;
-        const uint32_t v3 = w8 & 0x00F000F0u;
+        const half2_t v2 = __builtin_bit_cast(half2_t, w8 & 0x000F000Fu);
+        const half2_t v3 = __builtin_bit_cast(half2_t, w8 & 0x00F000F0u);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const uint32_t hp = word(wh[h], k);
-          const uint32_t lp2 = word(wl[h], k);
-          o[h][0] = dot2(v0, lp2, dot2(v0, hp, o[h][0]));
-          o[h][1] = dot2(v1, lp2, dot2(v1, hp, o[h][1]));
-          o[h][2] = dot2(v2, lp2, dot2(v2, hp, o[h][2]));
-          o[h][3] = dot2(v3, lp2, dot2(v3, hp, o[h][3]));
+          const float w0 = k < 2 ? wa[h][2 * k] : wb[h][2 * k - 4];
+          const float w1 = k < 2 ? wa[h][2 * k + 1] : wb[h][2 * k - 3];
+          // fp32 weight x fp16 nibble operand, fp32 accumulate (v_fma_mix_f32)
+          o[h][0] = fmaf(w1, static_cast<float>(v0.y), fmaf(w0, static_cast<float>(v0.x), o[h][0]));
+          o[h][1] = fmaf(w1, static_cast<float>(v1.y), fmaf(w0, static_cast<float>(v1.x), o[h][1]));
+          o[h][2] = fmaf(w1, static_cast<float>(v2.y), fmaf(w0, static_cast<float>(v2.x), o[h][2]));
+          o[h][3] = fmaf(w1, static_cast<float>(v3.y), fmaf(w0, static_cast<float>(v3.x), o[h][3]));
         }
       }
     }
     // "- 8" correction: the page's summed weights of block cj
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(&sm.u.w[wave][0][h][cj][sub * 8]);
-      const uint4 wu = *reinterpret_cast<const uint4*>(&sm.u.w[wave][1][h][cj][sub * 8]);
-      float ws = dot2(wv.x, kOne2, 0.0f);
-      ws = dot2(wv.y, kOne2, ws);
-      ws = dot2(wv.z, kOne2, ws);
-      ws = dot2(wv.w, kOne2, ws);
-      ws = dot2(wu.x, kOne2, ws);
-      ws = dot2(wu.y, kOne2, ws);
-      ws = dot2(wu.z, kOne2, ws);
-      ws = dot2(wu.w, kOne2, ws);
-      ws += __shfl_xor(ws, 1, 64);
-      ws += __shfl_xor(ws, 2, 64);
-      ws += __shfl_xor(ws, 4, 64);
+      const float4_t x = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][sub * 8]);
+      const float4_t y = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][sub * 8 + 4]);
+      const float ws = sum8(((x.x + x.y) + (x.z + x.w)) + ((y.x + y.y) + (y.z + y.w)));
       const float c1 = ws * 4.76837158203125e-07f;  // 8 * 2^-24
       o[h][0] -= c1;
       o[h][1] -= 16.0f * c1;
@@ -412,9 +440,52 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }
 
 template <int G>
-hipError_t launch_decode_g(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL(decode_kernel<G>, grid, dim3(kThreads), 0, s, a);
+hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, dim3 grid, hipStream_t s) {
+  QPrep<G>* qp = static_cast<QPrep<G>*>(qprep);
+  hipLaunchKernelGGL(decode_qprep_kernel<G>, dim3(a.B * a.Hkv), dim3(kThreads), 0, s, a.q, qp, a.Hq, a.Hkv,
+                     a.qk_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_kernel<G>, grid, dim3(kThreads), 0, s, a, static_cast<const QPrep<G>*>(qp));
   return hipGetLastError();
+}
+
+// Workgroups of the decode kernel the current device holds at once (CUs x
+// occupancy), computed once per (device, group size).
+int64_t resident_workgroups(int G) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int64_t> cached[kMaxDev][4];
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  int dev = 0, cus = 256, per = 0;
+  const bool have_dev = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev;
+  if (have_dev) {
+    const int64_t c = cached[dev][gi].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  if (have_dev) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  hipError_t e = hipErrorUnknown;
+  switch (G) {
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<1>, kThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<2>, kThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<4>, kThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<8>, kThreads, 0); break;
+  }
+  if (e != hipSuccess || per <= 0) per = 2;
+  const int64_t total = static_cast<int64_t>(cus) * per;
+  if (have_dev) cached[dev][gi].store(total, std::memory_order_relaxed);
+  return total;
+}
+
+size_t qprep_bytes(int G, int64_t items) {
+  switch (G) {
+    case 1: return sizeof(QPrep<1>) * items;
+    case 2: return sizeof(QPrep<2>) * items;
+    case 4: return sizeof(QPrep<4>) * items;
+    default: return sizeof(QPrep<8>) * items;
+  }
 }
 
 }  // namespace
@@ -426,7 +497,8 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int3
   int32_t ppw = window_tokens > 0 ? std::min(window_tokens / kPage, ctx_pages) : ctx_pages;
   ppw = std::max(ppw, 1);
   const int64_t items = static_cast<int64_t>(num_windows) * B * Hkv;
-  const int64_t target_wgs = 2048;
+  // one full wave of workgroups: every CU holds as many as its registers allow
+  const int64_t target_wgs = resident_workgroups(Hq / Hkv);
   int64_t pps = (items * ppw + target_wgs - 1) / target_wgs;
   pps = std::max<int64_t>(pps, kWaves);
   pps = std::min<int64_t>(pps, ppw);
@@ -434,7 +506,9 @@ DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int3
   p.pages_per_split = static_cast<int32_t>(pps);
   p.splits = static_cast<int32_t>((ppw + pps - 1) / pps);
   const int64_t R = static_cast<int64_t>(num_windows) * B * Hq;
-  p.ws_bytes = p.splits > 1 ? static_cast<size_t>(p.splits) * R * (kHeadDim + 2) * sizeof(float) : 0;
+  const size_t part = p.splits > 1 ? static_cast<size_t>(p.splits) * R * (kHeadDim + 2) * sizeof(float) : 0;
+  p.qprep_offset = (part + 255) / 256 * 256;
+  p.ws_bytes = p.qprep_offset + qprep_bytes(Hq / Hkv, static_cast<int64_t>(B) * Hkv);
   return p;
 }
 
@@ -477,12 +551,13 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
   }
   const dim3 grid(plan.splits, B * a.Hkv, num_windows);
   const int G = Hq / a.Hkv;
+  void* qprep = static_cast<char*>(ws) + plan.qprep_offset;
   hipError_t e;
   switch (G) {
-    case 1: e = launch_decode_g<1>(a, grid, s); break;
-    case 2: e = launch_decode_g<2>(a, grid, s); break;
-    case 4: e = launch_decode_g<4>(a, grid, s); break;
-    default: e = launch_decode_g<8>(a, grid, s); break;
+    case 1: e = launch_decode_g<1>(a, qprep, grid, s); break;
+    case 2: e = launch_decode_g<2>(a, qprep, grid, s); break;
+    case 4: e = launch_decode_g<4>(a, qprep, grid, s); break;
+    default: e = launch_decode_g<8>(a, qprep, grid, s); break;
   }
   if (e != hipSuccess || plan.splits == 1) return e;
   return launch_merge(part_m, part_l, a.o, plan.splits, static_cast<int32_t>(R), kHeadDim, out, out_m,

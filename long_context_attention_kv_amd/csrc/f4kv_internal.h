@@ -60,7 +60,8 @@ struct DecodePlan {
   int32_t pages_per_window;  // pages a window spans at most
   int32_t pages_per_split;   // pages one workgroup covers
   int32_t splits;            // workgroups per (window, sequence, kv head)
-  size_t ws_bytes;           // partial states in the workspace (0 when splits == 1)
+  size_t qprep_offset;       // where the prepared query operands start in the workspace
+  size_t ws_bytes;           // partial states (when splits > 1) + prepared query operands
 };
 
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx,

@@ -6,17 +6,15 @@
 // Folding C of them:  M = max m_c, w_c = l_c exp(m_c - M), L = sum w_c,
 // O = sum w_c o_c / L.  States with l == 0 (empty ranges) carry no weight.
 //
-// One workgroup per row (D <= 1024); each thread owns up to 4 groups of 4
-// consecutive channels and streams
-// the C partial rows with 16-byte loads.  The C (m, l) pairs are staged in LDS
-// in chunks, turned into weights once, and shared by the workgroup.
+// One workgroup per row (D <= 1024): four thread groups each fold a quarter of
+// the partial states with 16-byte loads, then fold their results in LDS.
 #include "f4kv_internal.h"
 
 namespace f4kv {
 namespace {
 
-constexpr int kMergeThreads = 64;
-constexpr int kChunk = 256;
+constexpr int kMergeThreads = 256;
+constexpr int kGroups = kMergeThreads / 64;  // partial states are split over 4 thread groups
 
 struct MergeArgs {
   const float* m;
@@ -28,11 +26,15 @@ struct MergeArgs {
   int32_t C, R, D;
 };
 
+// One workgroup per row.  Each of the 4 groups of 64 threads folds a quarter of
+// the C partial states (thread = 4 consecutive channels, D <= 256 per pass),
+// then the groups fold their results in LDS.
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  __shared__ float s_w[kChunk];
+  const int tid = threadIdx.x, grp = tid >> 6, t = tid & 63;
   __shared__ float s_red[kMergeThreads];
+  __shared__ float s_gm[kGroups], s_gl[kGroups];
+  __shared__ float4_t s_acc[kGroups][64];
 
   // global max over live states
   float mx = -INFINITY;
@@ -47,46 +49,43 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     __syncthreads();
   }
   const float M = s_red[0];
-  __syncthreads();
-
   const int d4 = a.D / 4;
-  float4_t acc[4];
-  for (int k = 0; k < 4; ++k) acc[k] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int c0 = 0; c0 < a.C; c0 += kChunk) {
-      const int n = min(kChunk, a.C - c0);
-      for (int c = tid; c < n; c += kMergeThreads) {
-        const int64_t i = static_cast<int64_t>(c0 + c) * a.R + r;
+  const int per = (a.C + kGroups - 1) / kGroups;
+  const int c0 = grp * per, c1 = min(a.C, c0 + per);
+
+  for (int j0 = 0; j0 < d4; j0 += 64) {
+    const int j = j0 + t;
+    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+    float L = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+      for (int c = c0; c < c1; ++c) {
+        const int64_t i = static_cast<int64_t>(c) * a.R + r;
         const float lc = a.l[i];
-        s_w[c] = lc > 0.0f ? lc * __expf(a.m[i] - M) : 0.0f;
-      }
-      __syncthreads();
-      for (int c = 0; c < n; ++c) {
-        const float wgt = s_w[c];
+        const float wgt = lc > 0.0f ? lc * __expf(a.m[i] - M) : 0.0f;
         L += wgt;
-        if (wgt == 0.0f) continue;
-        const float4_t* src = reinterpret_cast<const float4_t*>(
-            a.o + (static_cast<int64_t>(c0 + c) * a.R + r) * a.D);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int j = tid + k * kMergeThreads;
-          if (j < d4) acc[k] += wgt * src[j];
-        }
+        if (j < d4 && wgt != 0.0f) acc += wgt * reinterpret_cast<const float4_t*>(a.o + i * a.D)[j];
       }
-      __syncthreads();
     }
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  float4_t* dst = reinterpret_cast<float4_t*>(a.out + static_cast<int64_t>(r) * a.D);
+    s_acc[grp][t] = acc;
+    if (t == 0) s_gl[grp] = L;
+    __syncthreads();
+    if (grp == 0) {
+      float Lt = 0.0f;
+      float4_t at = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int j = tid + k * kMergeThreads;
-    if (j < d4) dst[j] = acc[k] * inv;
-  }
-  if (tid == 0) {
-    if (a.out_m) a.out_m[r] = L > 0.0f ? M : -INFINITY;
-    if (a.out_l) a.out_l[r] = L;
+      for (int q = 0; q < kGroups; ++q) {
+        Lt += s_gl[q];
+        at += s_acc[q][t];
+      }
+      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+      if (j < d4) reinterpret_cast<float4_t*>(a.out + static_cast<int64_t>(r) * a.D)[j] = at * inv;
+      if (t == 0 && j0 == 0) {
+        if (a.out_m) a.out_m[r] = Lt > 0.0f ? M : -INFINITY;
+        if (a.out_l) a.out_l[r] = Lt;
+      }
+    }
+    __syncthreads();
   }
 }
 
