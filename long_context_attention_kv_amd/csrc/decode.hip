@@ -7,10 +7,12 @@
 // attention of one query row over the window's cached tokens, returned as the
 // partial state (m, l, o).
 //
-// Work split.  A workgroup of 4 waves owns a run of pages of one (window,
-// sequence, KV head); each wave streams every 4th page of the run with its own
-// running max / sum / output, the waves fold in LDS at the end, and the
-// workgroups of one window are folded by the merge kernel.
+// Work split.  A small planning step (run on the device, from the context
+// lengths) cuts every (window, sequence) range of pages into chunks of about
+// the same length, enough of them to fill one resident wave of workgroups.  A
+// workgroup of 4 waves owns one chunk of one KV head; each wave streams every
+// 4th page of the chunk with its own running max / sum / output, the waves fold
+// in LDS at the end, and a fold kernel combines the chunks of each output row.
 //
 // Per page (64 tokens) a wave does two phases:
 //  * keys: lane = token.  The lane loads its token's 8 blocks (8 x 16 B, each
@@ -27,12 +29,11 @@
 //    yields fp16 pairs over two tokens and a dot product accumulates
 //    p_t s_t (n_t - 8) over token pairs.  The weights w = p_t * s_t (softmax
 //    weight times the token's block scale) travel from the key phase to the
-//    value phase through LDS as an fp16 pair hi + lo (hi = fp16(w), lo =
-//    fp16(w - hi)), and each product is taken twice, once per part: a single
-//    fp16 weight (11 bits) leaves ~2e-3 of the output RMS on channels whose
-//    values are many times the others' (outlier channels), the split keeps
-//    ~22 bits.  The "- 8" is corrected once per page with the page's summed
-//    weights.
+//    value phase through LDS in fp32 and enter the products through the
+//    mixed-precision FMA (fp32 weight times fp16 nibble operand): an fp16
+//    weight (11 bits) would leave ~2e-3 of the output RMS on channels whose
+//    values are many times the others' (outlier channels).  The "- 8" is
+//    corrected once per page with the page's summed weights.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
 #include <atomic>
@@ -65,13 +66,153 @@ struct DecodeArgs {
   const uint16_t* q;
   const int32_t* pt;
   const int32_t* ctx;
-  float* o;  // [S][R][D]
-  float* m;  // [S][R] or null
-  float* l;  // [S][R] or null
+  const int4* items;       // work items (window * B + sequence, first page, end page, first item of the range)
+  const int32_t* n_items;  // number of valid items
+  const int32_t* count;    // [W * B] items of each (window, sequence)
+  float* o;                // partial outputs [item][Hq][D]
+  float* m;                // [item][Hq], log2 units
+  float* l;                // [item][Hq]
+  float* out;              // [W * B][Hq][D]
+  float* out_m;            // [W * B][Hq] or null
+  float* out_l;            // [W * B][Hq] or null
   int32_t B, Hq, Hkv, num_pages, max_pages, max_ctx;
-  int32_t window_tokens, pages_per_split;
+  int32_t window_tokens;
   float qk_scale;  // sm_scale * log2(e)
 };
+
+// The work list: every (window, sequence) range of pages is cut into chunks of
+// about the same number of pages, sized from the actual context lengths (read
+// on the device) so that all chunks of all KV heads fill one resident wave of
+// workgroups.  A ragged batch is thus balanced by pages, not by sequences.
+struct PlanArgs {
+  const int32_t* ctx;
+  int4* items;
+  int32_t* first;    // [W * B] first item of each (window, sequence)
+  int32_t* count;    // [W * B] its number of items
+  int32_t* n_items;
+  float* out;        // rows of empty ranges are written here
+  float* out_m;
+  float* out_l;
+  int32_t B, W, Hq, Hkv, window_tokens, max_ctx, per_head_target;
+};
+
+__device__ __forceinline__ void window_pages(const PlanArgs& p, int wb, int& p0, int& p1) {
+  const int b = wb % p.B, w = wb / p.B;
+  const int ctx = max(0, min(p.ctx[b], p.max_ctx));
+  int t0 = 0, t1 = ctx;
+  if (p.window_tokens > 0) {
+    t0 = w * p.window_tokens;
+    t1 = min(ctx, t0 + p.window_tokens);
+  }
+  p0 = t0 / kPage;
+  p1 = t1 > t0 ? (t1 + kPage - 1) / kPage : p0;
+}
+
+__device__ int64_t block_sum(int64_t v, int64_t* s64) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  s64[tid] = v;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) s64[tid] += s64[tid + w];
+    __syncthreads();
+  }
+  return s64[0];
+}
+
+// Number of chunks when every range is cut into pieces of at most pps pages.
+__device__ int64_t count_chunks(const PlanArgs& p, int pps, int64_t* s64) {
+  int64_t c = 0;
+  for (int wb = threadIdx.x; wb < p.W * p.B; wb += kThreads) {
+    int p0, p1;
+    window_pages(p, wb, p0, p1);
+    c += (p1 - p0 + pps - 1) / pps;
+  }
+  return block_sum(c, s64);
+}
+
+// Run by one workgroup of kThreads threads.  The chunk length is the smallest
+// one (at least kWaves pages) whose chunk count fits the per-head target; the
+// pages of a range are then shared evenly among its chunks.  Ranges with no
+// tokens get no item; their output rows are written here (m = -inf, l = 0,
+// o = 0).
+__device__ void build_work_list(const PlanArgs& p) {
+  __shared__ int64_t s64[kThreads];
+  __shared__ int32_t s_end[kThreads];  // inclusive scan of the chunk counts of a batch of ranges
+  __shared__ int32_t s_p0[kThreads], s_len[kThreads];
+  const int tid = threadIdx.x;
+  const int n = p.W * p.B;
+  int64_t total = 0;
+  for (int wb = tid; wb < n; wb += kThreads) {
+    int p0, p1;
+    window_pages(p, wb, p0, p1);
+    total += p1 - p0;
+  }
+  total = block_sum(total, s64);
+  const int64_t target = p.per_head_target;
+  int64_t lo = max<int64_t>(kWaves, (total + target - 1) / target);
+  // with chunks of hi pages the rounding adds at most one chunk per range
+  int64_t hi = target > n ? max<int64_t>(lo, (total + target - n - 1) / (target - n)) : lo;
+  while (lo < hi) {  // smallest length in [lo, hi] whose count fits
+    const int64_t mid = (lo + hi) / 2;
+    if (count_chunks(p, static_cast<int>(mid), s64) <= target)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int pps = static_cast<int>(lo);
+  int base = 0;
+  for (int t0 = 0; t0 < n; t0 += kThreads) {
+    const int wb = t0 + tid;
+    int p0 = 0, p1 = 0, chunks = 0;
+    if (wb < n) {
+      window_pages(p, wb, p0, p1);
+      chunks = (p1 - p0 + pps - 1) / pps;
+    }
+    __syncthreads();
+    s_end[tid] = chunks;
+    s_p0[tid] = p0;
+    s_len[tid] = p1 - p0;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = tid >= off ? s_end[tid - off] : 0;
+      __syncthreads();
+      s_end[tid] += v;
+      __syncthreads();
+    }
+    const int batch = s_end[kThreads - 1];
+    if (wb < n) {
+      p.first[wb] = base + s_end[tid] - chunks;
+      p.count[wb] = chunks;
+    }
+    if (__syncthreads_count(wb < n && chunks == 0)) {  // identity rows of empty ranges
+      for (int r = 0; r < kThreads && t0 + r < n; ++r) {
+        if (s_len[r] > 0) continue;
+        const int64_t r0 = static_cast<int64_t>(t0 + r) * p.Hq;
+        for (int i = tid; i < p.Hq * kHeadDim; i += kThreads) p.out[r0 * kHeadDim + i] = 0.0f;
+        for (int i = tid; i < p.Hq; i += kThreads) {
+          if (p.out_m) p.out_m[r0 + i] = -INFINITY;
+          if (p.out_l) p.out_l[r0 + i] = 0.0f;
+        }
+      }
+    }
+    // item j of the batch belongs to the first range whose running count exceeds j
+    for (int j = tid; j < batch; j += kThreads) {
+      int r = 0;
+      for (int step = kThreads / 2; step > 0; step >>= 1)
+        if (s_end[r + step - 1] <= j) r += step;
+      const int c_cnt = s_end[r] - (r ? s_end[r - 1] : 0);
+      const int c = j - (s_end[r] - c_cnt);
+      const int len = s_len[r], q = len / c_cnt, rem = len % c_cnt;
+      const int beg = s_p0[r] + c * q + min(c, rem);
+      const int end = beg + q + (c < rem ? 1 : 0);
+      p.items[base + j] = make_int4(t0 + r, beg, end, base + j - c);
+    }
+    base += batch;
+    __syncthreads();
+  }
+  if (tid == 0) *p.n_items = base;
+}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
@@ -143,10 +284,16 @@ __device__ __forceinline__ void lds_wave_sync() {
 }
 
 // One workgroup per (sequence, KV head): query rows -> QPrep.
+// Workgroups 0 .. B*Hkv-1 prepare the query operands of one (sequence, KV
+// head) each; the last workgroup builds the work list.
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* __restrict__ q,
                                                                QPrep<G>* __restrict__ out, int32_t Hq,
-                                                               int32_t Hkv, float qk_scale) {
+                                                               int32_t Hkv, float qk_scale, PlanArgs plan) {
+  if (blockIdx.x == gridDim.x - 1) {
+    build_work_list(plan);
+    return;
+  }
   __shared__ float qf[G][kHeadDim];
   __shared__ int32_t qexp[G];
   const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
@@ -207,20 +354,59 @@ struct __align__(16) DecodeSmem {
   float fold_l[kWaves][G];
 };
 
+// Combines the per-wave states in LDS (max in log2 units, sum, normalised
+// output) into rows row0 .. row0 + G - 1 of dst: the output (max in natural
+// log) when final, else a partial state (max in log2 units).
+template <int G>
+__device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, int64_t row0, bool final,
+                                           float* out_m, float* out_l, float* pm, float* pl) {
+  for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (sm.fold_l[w][h] > 0.0f) M = fmaxf(M, sm.fold_m[w][h]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (sm.fold_l[w][h] > 0.0f) {
+          const float e = __builtin_amdgcn_exp2f(sm.fold_m[w][h] - M);
+          L = fmaf(sm.fold_l[w][h], e, L);
+          acc = fmaf(sm.u.fold[w][h][d], e, acc);
+        }
+      }
+    }
+    dst[(row0 + h) * kHeadDim + d] = L > 0.0f ? acc / L : 0.0f;
+    if (d == 0) {
+      if (final) {
+        if (out_m) out_m[row0 + h] = L > 0.0f ? M * kLn2 : -INFINITY;
+        if (out_l) out_l[row0 + h] = L;
+      } else {
+        pm[row0 + h] = L > 0.0f ? M : -INFINITY;
+        pl[row0 + h] = L;
+      }
+    }
+  }
+}
+
 static_assert((kWRow * 4) % 16 == 0, "weight rows must be 16-byte aligned");
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QPrep<G>* __restrict__ qprep) {
   __shared__ DecodeSmem<G> sm;
-  const int split = blockIdx.x;
-  const int b = blockIdx.y / a.Hkv;
-  const int g = blockIdx.y % a.Hkv;
-  const int win = blockIdx.z;
+  const int item = blockIdx.x;
+  const int g = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int4 it = a.items[item];
+  const int b = it.x % a.B;
+  const int win = it.x / a.B;
+  const int pbeg = it.y, pend = it.z;
+  const int nchunks = a.count[it.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int R = gridDim.z * a.B * a.Hq;
-  const int row0 = (win * a.B + b) * a.Hq + g * G;  // first output row of this group
+  const int64_t out_row = static_cast<int64_t>(item) * a.Hq + g * G;  // first partial row of this group
 
   int ctx = a.ctx[b];
   ctx = max(0, min(ctx, a.max_ctx));
@@ -229,20 +415,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     t0 = win * a.window_tokens;
     t1 = min(ctx, t0 + a.window_tokens);
   }
-  const int pbeg = t0 / kPage + split * a.pages_per_split;
-  const int pend = min(pbeg + a.pages_per_split, (t1 + kPage - 1) / kPage);
-  const int64_t out_row = static_cast<int64_t>(split) * R + row0;
 
-  if (t1 <= t0 || pend <= pbeg) {  // nothing to attend: merge identity
-    for (int i = tid; i < G * kHeadDim; i += kThreads) a.o[out_row * kHeadDim + i] = 0.0f;
-    if (tid < G) {
-      if (a.m) a.m[out_row + tid] = -INFINITY;
-      if (a.l) a.l[out_row + tid] = 0.0f;
-    }
-    return;
-  }
-
-  const QPrep<G>* QP = qprep + blockIdx.y;
+  const QPrep<G>* QP = qprep + static_cast<int64_t>(b) * a.Hkv + g;
   float m_run[G], l_lane[G], o[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -274,8 +448,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int c = 0; c < 8; ++c) kq[c] = kt[c * 64 + lane];
     const uint4 ks = reinterpret_cast<const uint4*>(a.k_scale + ph * (kPage * 8))[lane];
     const uint4 vs = reinterpret_cast<const uint4*>(a.v_scale + ph * (kPage * 8))[lane];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vq[c] = vt[c * 64 + lane];
 
     const int tok = lp * kPage + lane;
     const float tmask = (pvalid && tok >= t0 && tok < t1) ? 0.0f : -INFINITY;
@@ -317,6 +489,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       for (int h = 0; h < G; ++h) logit[h] = fmaf(sc, acc[h], logit[h]);
     }
 
+    // the values are requested only now, so they do not hold registers through
+    // the key phase (other waves cover their latency)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vq[c] = vt[c * 64 + lane];
+
     // online softmax (log2 units), wave-uniform running max per head
     float alpha[G], p[G];
 #pragma unroll
@@ -350,6 +528,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       for (int d = 0; d < 4; ++d) o[h][d] *= alpha[h];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
+      if ((ct & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two token groups' weights in flight
       pin(vq[ct]);
       float4_t wa[G], wb[G];  // weights of tokens 8ct..8ct+3 and 8ct+4..8ct+7
 #pragma unroll
@@ -392,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     }
   }
 
-  // ---- epilogue: fold the 4 waves, write the partial state -----------------
+  // ---- epilogue: fold the 4 waves -------------------------------------------
   float l_w[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_lane[h]);
@@ -414,39 +593,88 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * kHeadDim; i += kThreads) {
-    const int h = i / kHeadDim, d = i % kHeadDim;
-    float M = -INFINITY;
+  // A range of a single item writes its output rows directly; otherwise the
+  // item writes its partial state for the fold kernel.
+  const bool single = nchunks == 1;
+  const int64_t final_row = static_cast<int64_t>(it.x) * a.Hq + g * G;
+  fold_waves<G>(sm, single ? a.out : a.o, single ? final_row : out_row, single, a.out_m, a.out_l, a.m, a.l);
+}
+
+constexpr int kFoldWaves = 16;
+
+// Folds the partial states of each output row (window, sequence, query head)
+// whose range has two or more items: items first[wb] .. first[wb] + count[wb] - 1,
+// maxima in log2 units.  Wave w takes every 16th item with a running max
+// (lane = 4 channels); the 16 wave states meet in LDS.
+__global__ __launch_bounds__(64 * kFoldWaves) void decode_fold_kernel(const float* __restrict__ po,
+                                                                     const float* __restrict__ pm,
+                                                                     const float* __restrict__ pl,
+                                                                     const int32_t* __restrict__ first,
+                                                                     const int32_t* __restrict__ count,
+                                                                     int32_t Hq, float* out, float* out_m,
+                                                                     float* out_l) {
+  const int r = blockIdx.x;  // (window * B + sequence) * Hq + query head
+  const int wb = r / Hq, hq = r % Hq;
+  const int n = count[wb];
+  if (n < 2) return;  // written by the decode kernel or the planning step
+  const int c0 = first[wb];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float4_t s_acc[kFoldWaves][64];
+  __shared__ float s_m[kFoldWaves], s_l[kFoldWaves];
+  float Mr = -INFINITY, Lr = 0.0f;
+  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int c = wave; c < n; c += kFoldWaves) {
+    const int64_t i = static_cast<int64_t>(c0 + c) * Hq + hq;
+    const float mi = pm[i], li = pl[i];
+    const float4_t oi = reinterpret_cast<const float4_t*>(po + i * kHeadDim)[lane];
+    const float Mn = li > 0.0f ? fmaxf(Mr, mi) : Mr;
+    const float sc = Mr == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mr - Mn);
+    const float wi = li > 0.0f ? li * __builtin_amdgcn_exp2f(mi - Mn) : 0.0f;
+    acc = acc * sc + oi * wi;
+    Lr = Lr * sc + wi;
+    Mr = Mn;
+  }
+  s_acc[wave][lane] = acc;
+  if (lane == 0) {
+    s_m[wave] = Mr;
+    s_l[wave] = Lr;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (sm.fold_l[w][h] > 0.0f) M = fmaxf(M, sm.fold_m[w][h]);
-    float L = 0.0f, acc = 0.0f;
-    if (M != -INFINITY) {
+  for (int w = 0; w < kFoldWaves; ++w)
+    if (s_l[w] > 0.0f) M = fmaxf(M, s_m[w]);
+  float L = 0.0f;
+  float4_t at = float4_t{0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (sm.fold_l[w][h] > 0.0f) {
-          const float e = __builtin_amdgcn_exp2f(sm.fold_m[w][h] - M);
-          L = fmaf(sm.fold_l[w][h], e, L);
-          acc = fmaf(sm.u.fold[w][h][d], e, acc);
-        }
+    for (int w = 0; w < kFoldWaves; ++w) {
+      if (s_l[w] > 0.0f) {
+        const float e = __builtin_amdgcn_exp2f(s_m[w] - M);
+        L = fmaf(s_l[w], e, L);
+        at += s_acc[w][lane] * e;
       }
     }
-    a.o[(out_row + h) * kHeadDim + d] = L > 0.0f ? acc / L : 0.0f;
-    if (d == 0) {
-      if (a.m) a.m[out_row + h] = L > 0.0f ? M * kLn2 : -INFINITY;
-      if (a.l) a.l[out_row + h] = L;
-    }
+  }
+  reinterpret_cast<float4_t*>(out + static_cast<int64_t>(r) * kHeadDim)[lane] = L > 0.0f ? at / L : at * 0.0f;
+  if (lane == 0) {
+    if (out_m) out_m[r] = L > 0.0f ? M * kLn2 : -INFINITY;
+    if (out_l) out_l[r] = L;
   }
 }
 
 template <int G>
-hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, dim3 grid, hipStream_t s) {
+hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, const PlanArgs& plan, int max_items,
+                           hipStream_t s) {
   QPrep<G>* qp = static_cast<QPrep<G>*>(qprep);
-  hipLaunchKernelGGL(decode_qprep_kernel<G>, dim3(a.B * a.Hkv), dim3(kThreads), 0, s, a.q, qp, a.Hq, a.Hkv,
-                     a.qk_scale);
+  hipLaunchKernelGGL(decode_qprep_kernel<G>, dim3(a.B * a.Hkv + 1), dim3(kThreads), 0, s, a.q, qp, a.Hq, a.Hkv,
+                     a.qk_scale, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_kernel<G>, grid, dim3(kThreads), 0, s, a, static_cast<const QPrep<G>*>(qp));
+  hipLaunchKernelGGL(decode_kernel<G>, dim3(max_items, a.Hkv), dim3(kThreads), 0, s, a,
+                     static_cast<const QPrep<G>*>(qp));
   return hipGetLastError();
 }
 
@@ -492,23 +720,27 @@ size_t qprep_bytes(int G, int64_t items) {
 
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
                        int32_t window_tokens) {
+  (void)max_ctx;
+  (void)window_tokens;
   DecodePlan p;
-  const int32_t ctx_pages = (max_ctx + kPage - 1) / kPage;
-  int32_t ppw = window_tokens > 0 ? std::min(window_tokens / kPage, ctx_pages) : ctx_pages;
-  ppw = std::max(ppw, 1);
-  const int64_t items = static_cast<int64_t>(num_windows) * B * Hkv;
-  // one full wave of workgroups: every CU holds as many as its registers allow
+  // all chunks of all KV heads fill one resident wave of workgroups
   const int64_t target_wgs = resident_workgroups(Hq / Hkv);
-  int64_t pps = (items * ppw + target_wgs - 1) / target_wgs;
-  pps = std::max<int64_t>(pps, kWaves);
-  pps = std::min<int64_t>(pps, ppw);
-  p.pages_per_window = ppw;
-  p.pages_per_split = static_cast<int32_t>(pps);
-  p.splits = static_cast<int32_t>((ppw + pps - 1) / pps);
-  const int64_t R = static_cast<int64_t>(num_windows) * B * Hq;
-  const size_t part = p.splits > 1 ? static_cast<size_t>(p.splits) * R * (kHeadDim + 2) * sizeof(float) : 0;
-  p.qprep_offset = (part + 255) / 256 * 256;
-  p.ws_bytes = p.qprep_offset + qprep_bytes(Hq / Hkv, static_cast<int64_t>(B) * Hkv);
+  p.per_head_target = static_cast<int32_t>(std::max<int64_t>(1, target_wgs / Hkv));
+  const int64_t wb = static_cast<int64_t>(num_windows) * B;
+  p.max_items = static_cast<int32_t>(wb + p.per_head_target + 1);
+  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t off = 0;
+  p.part_o_offset = off;
+  off = align(off + static_cast<size_t>(p.max_items) * Hq * kHeadDim * sizeof(float));
+  p.part_ml_offset = off;
+  off = align(off + static_cast<size_t>(p.max_items) * Hq * 2 * sizeof(float));
+  p.items_offset = off;
+  off = align(off + static_cast<size_t>(p.max_items) * sizeof(int4));
+  p.count_offset = off;  // first [W * B], count [W * B], n_items
+  off = align(off + static_cast<size_t>(wb) * 2 * sizeof(int32_t) + sizeof(int32_t));
+  p.qprep_offset = off;
+  off = align(off + qprep_bytes(Hq / Hkv, static_cast<int64_t>(B) * Hkv));
+  p.ws_bytes = off;
   return p;
 }
 
@@ -517,6 +749,8 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
                          int32_t window_tokens, float sm_scale, float* out, float* out_m, float* out_l,
                          void* ws, const DecodePlan& plan, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  char* base = static_cast<char*>(ws);
+  const int64_t wb = static_cast<int64_t>(num_windows) * B;
   DecodeArgs a;
   a.k_nib = c.k_nib;
   a.k_scale = c.k_scale;
@@ -532,36 +766,49 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
   a.max_pages = max_pages;
   a.max_ctx = max_ctx;
   a.window_tokens = window_tokens;
-  a.pages_per_split = plan.pages_per_split;
   a.qk_scale = sm_scale * kLog2e;
-  const int64_t R = static_cast<int64_t>(num_windows) * B * Hq;
-  float* part_m = nullptr;
-  float* part_l = nullptr;
-  if (plan.splits > 1) {
-    float* base = static_cast<float*>(ws);
-    a.o = base;
-    part_m = base + static_cast<size_t>(plan.splits) * R * kHeadDim;
-    part_l = part_m + static_cast<size_t>(plan.splits) * R;
-    a.m = part_m;
-    a.l = part_l;
-  } else {
-    a.o = out;
-    a.m = out_m;
-    a.l = out_l;
-  }
-  const dim3 grid(plan.splits, B * a.Hkv, num_windows);
+  a.o = reinterpret_cast<float*>(base + plan.part_o_offset);
+  a.m = reinterpret_cast<float*>(base + plan.part_ml_offset);
+  a.l = a.m + static_cast<size_t>(plan.max_items) * Hq;
+  int4* items = reinterpret_cast<int4*>(base + plan.items_offset);
+  int32_t* first = reinterpret_cast<int32_t*>(base + plan.count_offset);
+  int32_t* count = first + wb;
+  int32_t* n_items = count + wb;
+  a.items = items;
+  a.n_items = n_items;
+  a.count = count;
+  a.out = out;
+  a.out_m = out_m;
+  a.out_l = out_l;
+  PlanArgs pa;
+  pa.ctx = ctx;
+  pa.items = items;
+  pa.first = first;
+  pa.count = count;
+  pa.n_items = n_items;
+  pa.out = out;
+  pa.out_m = out_m;
+  pa.out_l = out_l;
+  pa.B = B;
+  pa.W = num_windows;
+  pa.Hq = Hq;
+  pa.Hkv = a.Hkv;
+  pa.window_tokens = window_tokens;
+  pa.max_ctx = max_ctx;
+  pa.per_head_target = plan.per_head_target;
+  void* qprep = base + plan.qprep_offset;
   const int G = Hq / a.Hkv;
-  void* qprep = static_cast<char*>(ws) + plan.qprep_offset;
   hipError_t e;
   switch (G) {
-    case 1: e = launch_decode_g<1>(a, qprep, grid, s); break;
-    case 2: e = launch_decode_g<2>(a, qprep, grid, s); break;
-    case 4: e = launch_decode_g<4>(a, qprep, grid, s); break;
-    default: e = launch_decode_g<8>(a, qprep, grid, s); break;
+    case 1: e = launch_decode_g<1>(a, qprep, pa, plan.max_items, s); break;
+    case 2: e = launch_decode_g<2>(a, qprep, pa, plan.max_items, s); break;
+    case 4: e = launch_decode_g<4>(a, qprep, pa, plan.max_items, s); break;
+    default: e = launch_decode_g<8>(a, qprep, pa, plan.max_items, s); break;
   }
-  if (e != hipSuccess || plan.splits == 1) return e;
-  return launch_merge(part_m, part_l, a.o, plan.splits, static_cast<int32_t>(R), kHeadDim, out, out_m,
-                      out_l, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_fold_kernel, dim3(static_cast<unsigned>(wb * Hq)), dim3(64 * kFoldWaves), 0, s, a.o,
+                     a.m, a.l, first, count, Hq, out, out_m, out_l);
+  return hipGetLastError();
 }
 
 }  // namespace f4kv

@@ -57,11 +57,10 @@ hipError_t launch_merge(const float* m, const float* l, const float* o, int32_t 
                         int32_t D, float* out, float* out_m, float* out_l, hipStream_t s);
 
 struct DecodePlan {
-  int32_t pages_per_window;  // pages a window spans at most
-  int32_t pages_per_split;   // pages one workgroup covers
-  int32_t splits;            // workgroups per (window, sequence, kv head)
-  size_t qprep_offset;       // where the prepared query operands start in the workspace
-  size_t ws_bytes;           // partial states (when splits > 1) + prepared query operands
+  int32_t per_head_target;   // work items per KV head that fill the GPU once
+  int32_t max_items;         // bound on the work items of any context lengths
+  size_t part_o_offset, part_ml_offset, items_offset, count_offset, qprep_offset;
+  size_t ws_bytes;           // workspace the call needs
 };
 
 DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx,
