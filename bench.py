@@ -140,24 +140,27 @@ def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
           for _ in range(steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    start_ev = torch.cuda.Event(enable_timing=True)
-    end_ev = torch.cuda.Event(enable_timing=True)
-    start_ev.record(stream)
-    yp = yarn_params(factor)
-    for st in range(steps):
-        c, s = f4.yarn_rope_table(yp, positions)
-        for i, L in enumerate(layers):
-            q = f4.yarn_rope_apply(c, s, q_raw[i])
-            k = f4.yarn_rope_apply(c, s, k_new[i])
-            f4.kv_cache_write_f4(L.cache, k, v_new[i], L.new_slots)
-            ev[st][i][0].record(stream)
-            f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, ctx, SM, out=outs[i][0], out_m=outs[i][1],
-                                    out_l=outs[i][2], workspace=ws)
-            ev[st][i][1].record(stream)
-    end_ev.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    timer = f4.KernelTimer(f4.KERNEL_DECODE, max_launches=steps * n_layers)
+    with timer:
+        t_start = time.perf_counter()
+        start_ev = torch.cuda.Event(enable_timing=True)
+        end_ev = torch.cuda.Event(enable_timing=True)
+        start_ev.record(stream)
+        yp = yarn_params(factor)
+        for st in range(steps):
+            c, s = f4.yarn_rope_table(yp, positions)
+            for i, L in enumerate(layers):
+                q = f4.yarn_rope_apply(c, s, q_raw[i])
+                k = f4.yarn_rope_apply(c, s, k_new[i])
+                f4.kv_cache_write_f4(L.cache, k, v_new[i], L.new_slots)
+                ev[st][i][0].record(stream)
+                f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, ctx, SM, out=outs[i][0], out_m=outs[i][1],
+                                        out_l=outs[i][2], workspace=ws)
+                ev[st][i][1].record(stream)
+        end_ev.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    assert timer.launches == steps * n_layers, (timer.launches, steps * n_layers)
     gpu_ms = start_ev.elapsed_time(end_ev)
     dec_ms = [ev[st][i][0].elapsed_time(ev[st][i][1]) for st in range(steps) for i in range(n_layers)]
     ms_step = max(gpu_ms, wall * 1e3) / steps
@@ -170,8 +173,10 @@ def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
         "value": tokens / (ms_step / 1e3),
         "decode_call_ms_avg": dec_avg_ms,
         "decode_call_ms_min": float(np.min(dec_ms)),
+        "decode_kernel_ms_avg": timer.avg_ms,
         "decode_bytes_per_call": dec_bytes,
-        "decode_gbs": dec_bytes / (dec_avg_ms / 1e3) / 1e9,
+        "decode_gbs": dec_bytes / (timer.avg_ms / 1e3) / 1e9,
+        "decode_call_gbs": dec_bytes / (dec_avg_ms / 1e3) / 1e9,
         "layers": layers,
         "out_sample": outs[0][0][0, 0, 0, :4].float().cpu().tolist(),
     }
@@ -272,19 +277,22 @@ def bench_prefill(iters=5, T=2048, window=131072):
         f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
+    with f4.KernelTimer(f4.KERNEL_PREFILL, max_launches=iters) as timer:
+        e0.record()
+        for _ in range(iters):
+            f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     fl = prefill_flops(T, pos0)
     tf = fl / (ms / 1e3) / 1e12
+    tk = fl / (timer.avg_ms / 1e3) / 1e12
     return {"workload": "2,048 queries at 129,024..131,071 over a 131,072-token causal window (write included)",
-            "ms": ms, "tflops": tf, "mfma_frac": tf / MFMA_F16_PEAK_TFLOPS, "flops": fl}
+            "ms": ms, "tflops": tf, "mfma_frac": tf / MFMA_F16_PEAK_TFLOPS, "flops": fl,
+            "kernel_ms": timer.avg_ms, "kernel_tflops": tk, "kernel_mfma_frac": tk / MFMA_F16_PEAK_TFLOPS}
 
 
-def cpu_baseline(sample_tokens=32768):
+def cpu_baseline(sample_tokens=458752):
     """The fp64 oracle on a bounded sample: one lane, all 4 KV heads, sample_tokens cached tokens."""
     from oracle import attention as oatt
     from oracle import f4 as of4
@@ -320,6 +328,43 @@ def cpu_baseline(sample_tokens=32768):
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.md")
+DECODE_SOURCE = os.path.join(ROOT, "long_context_attention_kv_amd", "csrc", "decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode-kernel launch from the committed counter summary, or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith("#"):
+                    k, v = ln.split(":", 1)
+                    fields[k.strip().strip("-* `")] = v.strip().strip("`")
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("decode.hip sha256") != sha:
+            return None
+        return float(fields["traffic bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes):
+    """A plain device-to-device copy of nbytes, three times: the reference a byte
+    counter is scaled by (its algorithmic traffic is nbytes read + nbytes written)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,7 +372,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="skip the 1M, ragged and prefill measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--cpu-tokens", type=int, default=458752)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="also run a plain device copy of BYTES bytes 3 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -336,9 +383,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     f4.load_library()
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     r = bench_config1(args.steps, args.warmup)
-    log(f"config1: {r['ms_per_step']:.3f} ms/step, {r['value'] / 1e9:.3f} G KV-tokens/s, decode call "
-        f"{r['decode_call_ms_avg'] * 1e3:.1f} us -> {r['decode_gbs']:.0f} GB/s")
+    log(f"config1: {r['ms_per_step']:.3f} ms/step, {r['value'] / 1e9:.3f} G KV-tokens/s, decode kernel "
+        f"{r['decode_kernel_ms_avg'] * 1e3:.1f} us -> {r['decode_gbs']:.0f} GB/s, whole call "
+        f"{r['decode_call_ms_avg'] * 1e3:.1f} us -> {r['decode_call_gbs']:.0f} GB/s")
     del r["layers"]
     torch.cuda.empty_cache()
     extra = {}
@@ -372,9 +422,10 @@ def main():
                                "head_dim 256, 64-token pages, F4 KV, YaRN x4, 1% outlier channels x8",
                    "lanes": 3, "context": 262144, "layers": 16},
         "roofline": {"bound": "hbm", "achieved": r["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": r["decode_gbs"] / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "paged_attn_decode_f4 call (split kernel + fold)",
-                     "bytes_per_launch": r["decode_bytes_per_call"], "launch_ms_avg": r["decode_call_ms_avg"]},
+                     "frac": r["decode_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "decode_kernel<4> (split-K attention kernel of paged_attn_decode_f4)",
+                     "bytes_per_launch": r["decode_bytes_per_call"], "launch_ms_avg": r["decode_kernel_ms_avg"],
+                     "whole_call_ms_avg": r["decode_call_ms_avg"], "whole_call_gbs": r["decode_call_gbs"]},
         "cpu_baseline": cpu,
         "extra": extra,
     }

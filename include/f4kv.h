@@ -234,6 +234,24 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q,
                           float* out, float* out_m, float* out_l,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Kernel timing (a measurement aid of this library, not an operation of the
+ * method).  f4kv_timing_start(kernel, max_launches) makes every following call
+ * that launches `kernel` record a pair of HIP events on its stream right
+ * around that one launch, for up to max_launches launches (the events are
+ * created here, on the current device; no device memory is allocated).
+ * f4kv_timing_stop(kernel, &total_ms, &launches) waits for the recorded
+ * events, returns the summed kernel time and the number of timed launches, and
+ * ends the timing.  Launches beyond max_launches are not timed.
+ *   kernel  F4KV_KERNEL_DECODE: the split-K attention kernel of
+ *           paged_attn_decode_f4 (not its query preparation or fold);
+ *           F4KV_KERNEL_PREFILL: the attention kernel of paged_attn_prefill_f4.
+ * Timing one kernel from two host threads at once is not supported.
+ */
+enum { F4KV_KERNEL_DECODE = 0, F4KV_KERNEL_PREFILL = 1 };
+int f4kv_timing_start(int32_t kernel, int32_t max_launches);
+int f4kv_timing_stop(int32_t kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

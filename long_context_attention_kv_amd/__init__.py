@@ -8,8 +8,11 @@ current stream, allocates outputs and workspaces with torch, and raises
 library is not built the calls raise; there is no other code path.
 """
 from ._binding import (  # noqa: F401
+    KERNEL_DECODE,
+    KERNEL_PREFILL,
     F4KVError,
     F4Cache,
+    KernelTimer,
     YarnParams,
     abi_version,
     cache_bytes,
@@ -37,4 +40,6 @@ EXPORTED_SYMBOLS = (
     "lse_merge",
     "paged_attn_prefill_f4_workspace_size",
     "paged_attn_prefill_f4",
+    "f4kv_timing_start",
+    "f4kv_timing_stop",
 )

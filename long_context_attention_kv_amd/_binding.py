@@ -52,7 +52,11 @@ _SIGS = {
     "paged_attn_prefill_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I]),
     "paged_attn_prefill_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                                         _P, _P, _P, _P, C.c_size_t, _P]),
+    "f4kv_timing_start": (C.c_int, [_I, _I]),
+    "f4kv_timing_stop": (C.c_int, [_I, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
+
+KERNEL_DECODE, KERNEL_PREFILL = 0, 1
 
 
 def library_path() -> str:
@@ -297,3 +301,27 @@ def paged_attn_prefill_f4(cache: F4Cache, q, k_new, v_new, page_table, pos0: int
                                      page_table.numel(), T, Hq, int(pos0), float(sm_scale), _ptr(out), _ptr(out_m),
                                      _ptr(out_l), _ptr(workspace), ws_bytes, _stream()))
     return out, out_m, out_l
+
+
+class KernelTimer:
+    """Times one library kernel with HIP events the library records around each
+    of its launches (see f4kv_timing_start): ``with KernelTimer(KERNEL_DECODE) as t:
+    ...``; afterwards ``t.total_ms``, ``t.launches`` and ``t.avg_ms``."""
+
+    def __init__(self, kernel: int, max_launches: int = 4096):
+        self.kernel, self.max_launches = kernel, max_launches
+        self.total_ms, self.launches = 0.0, 0
+
+    def __enter__(self):
+        _check("f4kv_timing_start", load_library().f4kv_timing_start(self.kernel, self.max_launches))
+        return self
+
+    def __exit__(self, *exc):
+        ms, n = C.c_double(0.0), C.c_int64(0)
+        _check("f4kv_timing_stop", load_library().f4kv_timing_stop(self.kernel, C.byref(ms), C.byref(n)))
+        self.total_ms, self.launches = ms.value, n.value
+        return False
+
+    @property
+    def avg_ms(self) -> float:
+        return self.total_ms / self.launches if self.launches else float("nan")

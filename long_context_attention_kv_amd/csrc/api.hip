@@ -246,4 +246,24 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q, const floa
                   fn);
 }
 
+int f4kv_timing_start(int32_t kernel, int32_t max_launches) {
+  const char* fn = "f4kv_timing_start";
+  if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL)
+    return fail(F4KV_ERR_INVALID, "%s: unknown kernel %d", fn, kernel);
+  if (max_launches <= 0 || max_launches > (1 << 20))
+    return fail(F4KV_ERR_INVALID, "%s: max_launches must be in [1, 2^20], got %d", fn, max_launches);
+  hipError_t e = f4kv::timing_start(kernel, max_launches);
+  if (e != hipSuccess) return fail(F4KV_ERR_LAUNCH, "%s: hipEventCreate failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int f4kv_timing_stop(int32_t kernel, double* total_ms, int64_t* launches) {
+  const char* fn = "f4kv_timing_stop";
+  if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL)
+    return fail(F4KV_ERR_INVALID, "%s: unknown kernel %d", fn, kernel);
+  hipError_t e = f4kv::timing_stop(kernel, total_ms, launches);
+  if (e != hipSuccess) return fail(F4KV_ERR_LAUNCH, "%s: reading the events failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

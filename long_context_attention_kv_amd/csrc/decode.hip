@@ -673,9 +673,12 @@ hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, const PlanArgs& pla
                      a.qk_scale, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  timing_begin(F4KV_KERNEL_DECODE, s);
   hipLaunchKernelGGL(decode_kernel<G>, dim3(max_items, a.Hkv), dim3(kThreads), 0, s, a,
                      static_cast<const QPrep<G>*>(qp));
-  return hipGetLastError();
+  e = hipGetLastError();
+  timing_end(F4KV_KERNEL_DECODE, s);
+  return e;
 }
 
 // Workgroups of the decode kernel the current device holds at once (CUs x

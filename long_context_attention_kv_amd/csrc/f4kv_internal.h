@@ -38,6 +38,14 @@ __device__ __forceinline__ uint16_t f32_to_f16bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// ---- kernel timing (host) ----------------------------------------------------
+// Record the start / end event of one timed launch of `kernel` on stream s
+// (no-ops unless f4kv_timing_start is active for that kernel).
+void timing_begin(int kernel, hipStream_t s);
+void timing_end(int kernel, hipStream_t s);
+hipError_t timing_start(int kernel, int max_launches);
+hipError_t timing_stop(int kernel, double* total_ms, int64_t* launches);
+
 // ---- kernel launchers (host); arguments already validated ------------------
 hipError_t launch_kv_write(const f4kv_cache& c, const float* k, const float* v,
                            const int32_t* slots, int32_t T, hipStream_t s);

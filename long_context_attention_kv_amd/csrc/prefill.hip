@@ -353,8 +353,10 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
     a.m = out_m;
     a.l = out_l;
   }
+  timing_begin(F4KV_KERNEL_PREFILL, s);
   hipLaunchKernelGGL(prefill_kernel, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
+  timing_end(F4KV_KERNEL_PREFILL, s);
   if (e != hipSuccess || plan.kv_splits == 1) return e;
   return launch_merge(pm, pl, a.o, plan.kv_splits, static_cast<int32_t>(R), kHeadDim, out, out_m, out_l, s);
 }

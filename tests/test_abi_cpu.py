@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -154,3 +154,14 @@ def test_prefill_argument_checks(lib):
     assert f(k=None) == 1 and "together" in _err(lib)
     assert f(Hq=8) == 2
     assert f(T=0) == 0
+
+
+def test_timing_argument_checks(lib):
+    assert lib.f4kv_timing_start(7, 16) == 1 and "unknown kernel" in _err(lib)
+    assert lib.f4kv_timing_start(0, 0) == 1 and "max_launches" in _err(lib)
+    assert lib.f4kv_timing_start(1, (1 << 20) + 1) == 1
+    ms, n = C.c_double(-1.0), C.c_int64(-1)
+    assert lib.f4kv_timing_stop(-1, C.byref(ms), C.byref(n)) == 1 and "unknown kernel" in _err(lib)
+    # stopping a timer that never started reports no launches and touches no device
+    assert lib.f4kv_timing_stop(0, C.byref(ms), C.byref(n)) == 0
+    assert ms.value == 0.0 and n.value == 0

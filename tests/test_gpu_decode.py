@@ -128,3 +128,16 @@ def test_lse_merge_vs_oracle(C, R):
         assert abs(M[r] - rm_) <= 1e-6 * max(1, abs(rm_))
         assert abs(L[r] - rl_) <= 1e-5 * rl_
         np.testing.assert_allclose(out[r], ro_, rtol=1e-5, atol=1e-5 * np.abs(ro_).max())
+
+
+def test_kernel_timer_counts_decode_launches():
+    ps = PagedSet([5000, 300], Hkv=4, seed=14)
+    bits, _ = random_q(2, 16, 256, 14)
+    q = bf16_tensor(bits)
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=2) as t:
+        for _ in range(3):  # the third launch is beyond max_launches
+            f4.paged_attn_decode_f4(ps.gc, q, ps.gpu_page_table(), ps.gpu_lengths(), 5000, SM)
+    assert t.launches == 2 and t.total_ms > 0.0
+    with f4.KernelTimer(f4.KERNEL_PREFILL) as t2:  # a decode call is not a prefill launch
+        f4.paged_attn_decode_f4(ps.gc, q, ps.gpu_page_table(), ps.gpu_lengths(), 5000, SM)
+    assert t2.launches == 0

@@ -1,0 +1,240 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times.
+
+Every output is computed on the GPU through the C ABI, by the same calls with
+the same shapes as the benchmark: YaRN table and rotation of the keys and of
+the query, F4 writes, then the decode (or prefill) call.  The fp64 oracle
+cannot redo a whole 262,144-token layer of 3 lanes in seconds, so it recomputes
+a sample: chosen (sequence, KV head) pairs -- all 4 query heads of the group,
+every channel -- from the same seeded draws, with its own table, rotation,
+quantiser and attention.  Where even a sample is too long for the oracle
+(1,048,576 tokens), it checks sampled windows, and the fold of all windows is
+checked against the unwindowed call (log-sum-exp identity) on the GPU.
+
+Draws: K and V of sequence b, KV head h are N(0,1) fp32 in blocks of 65,536
+tokens, each block from its own seeded stream, so the oracle regenerates only
+the blocks it needs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_kv_amd as f4
+import synth
+from oracle import attention as oatt
+from oracle import yarn as oyarn
+from gpu_cases import assert_attention_close, bf16_tensor, bf16_values
+
+pytestmark = pytest.mark.gpu
+
+HQ, HKV, D, G = 16, 4, 256, 4
+PAGE = 64
+SM = 1.0 / 16.0
+BLK = 65536
+
+
+def spec_for(factor):
+    return synth.YarnSpec(factor=factor)
+
+
+def gpu_params(spec):
+    return f4.YarnParams(spec.theta, spec.rotary_dim, spec.factor, spec.orig_ctx, spec.beta_fast, spec.beta_slow,
+                         spec.mscale)
+
+
+def outlier_channels(config, outliers):
+    """Per KV head, the channels scaled x8 (1% of all Hkv * D columns)."""
+    if not outliers:
+        return [np.zeros(0, np.int64)] * HKV
+    cols = synth.outlier_columns(synth.rng(config, 51), HKV, D)
+    return [cols[cols // D == h] % D for h in range(HKV)]
+
+
+def table_f32(spec, pos):
+    """The oracle's fp64 YaRN rows as the boundary stores them (fp32): the
+    rotation of a pipeline applies the stored table, and F4 codes are
+    discontinuous in their input, so both sides rotate with the same rows."""
+    cs, sn = oyarn.yarn_table(spec, pos)
+    return cs.astype(np.float32).astype(np.float64), sn.astype(np.float32).astype(np.float64)
+
+
+def draw_block(config, seq, head, j, n, kind, chans):
+    x = synth.normal_f32(synth.rng(config, 50, seq, head, j, kind), (n, D))
+    if len(chans):
+        x[:, chans] *= np.float32(8.0)
+    return x
+
+
+class Layer:
+    """One layer of B sequences in one pool; filled on the GPU block by block."""
+
+    def __init__(self, config, lengths, factor, outliers, with_query=True):
+        self.config, self.lengths = config, [int(n) for n in lengths]
+        self.spec = spec_for(factor)
+        self.chans = outlier_channels(config, outliers)
+        pages = [(n + PAGE - 1) // PAGE for n in self.lengths]
+        self.num_pages = sum(pages)
+        self.max_pages = max(pages)
+        perm = synth.page_permutation(synth.rng(config, 53), self.num_pages)
+        self.pt = synth.page_table_for(self.lengths, perm, self.max_pages)
+        self.cache = f4.F4Cache(self.num_pages, HKV, D)
+        yp = gpu_params(self.spec)
+        for b, n in enumerate(self.lengths):
+            for j, t0 in enumerate(range(0, n, BLK)):
+                nb = min(BLK, n - t0)
+                k = np.stack([draw_block(config, b, h, j, nb, 0, self.chans[h]) for h in range(HKV)], axis=1)
+                v = np.stack([draw_block(config, b, h, j, nb, 1, self.chans[h]) for h in range(HKV)], axis=1)
+                kt = torch.from_numpy(k).cuda()
+                pos = torch.arange(t0, t0 + nb, dtype=torch.int32, device="cuda")
+                c, s = f4.yarn_rope_table(yp, pos)
+                f4.yarn_rope_apply(c, s, kt, y=kt)
+                t = np.arange(t0, t0 + nb)
+                slots = (self.pt[b, t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+                f4.kv_cache_write_f4(self.cache, kt, torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        if with_query:
+            # one decode query per sequence, rotated at position ctx - 1
+            self.qbits = np.stack([synth.f32_to_bf16_bits(synth.normal_f32(synth.rng(config, 52, b), (HQ, D)))
+                                   for b in range(len(self.lengths))])
+            pos = torch.tensor([n - 1 for n in self.lengths], dtype=torch.int32, device="cuda")
+            c, s = f4.yarn_rope_table(yp, pos)
+            self.q = f4.yarn_rope_apply(c, s, bf16_tensor(self.qbits))
+
+    # ---- oracle side: its own draws, table, rotation, quantiser and attention ----
+    def oracle_kv(self, b, h, t_end=None, t_begin=0):
+        """Dequantised K, V [t_end - t_begin, D] (fp64) of sequence b, KV head h."""
+        n = self.lengths[b] if t_end is None else t_end
+        Ks, Vs = [], []
+        for j in range(t_begin // BLK, (n + BLK - 1) // BLK):
+            t0 = j * BLK
+            nb = min(BLK, self.lengths[b] - t0)
+            k = draw_block(self.config, b, h, j, nb, 0, self.chans[h]).astype(np.float64)
+            v = draw_block(self.config, b, h, j, nb, 1, self.chans[h])
+            cs, sn = table_f32(self.spec, np.arange(t0, t0 + nb))
+            kr = oyarn.rope_apply(k[:, None, :], cs, sn, self.spec.rotary_dim)[:, 0].astype(np.float32)
+            lo, hi = max(t_begin, t0) - t0, min(n, t0 + nb) - t0
+            Ks.append(oatt.dequantize_rows(kr[lo:hi]))
+            Vs.append(oatt.dequantize_rows(v[lo:hi]))
+        return np.concatenate(Ks), np.concatenate(Vs)
+
+    def oracle_query(self, b, h):
+        """The 4 query rows of KV head h's group, rotated at ctx - 1 and stored as bf16."""
+        qv = bf16_values(self.qbits[b, h * G:(h + 1) * G])
+        cs, sn = table_f32(self.spec, np.array([self.lengths[b] - 1]))
+        qr = oyarn.rope_apply(qv[None], cs, sn, self.spec.rotary_dim)[0]
+        return bf16_values(synth.f32_to_bf16_bits(qr.astype(np.float32)))
+
+
+def check_group(out, m, l, ref, what):
+    ro, rm, rl = ref
+    assert_attention_close(out, ro, what)
+    assert np.all(np.abs(m - rm) <= 1e-3 * np.maximum(1.0, np.abs(rm))), f"{what}: m"
+    assert np.all(np.abs(l - rl) <= 2e-3 * rl), f"{what}: l"
+
+
+def decode_call(layer, W=1, wt=0, max_ctx=None):
+    B = len(layer.lengths)
+    max_ctx = max(layer.lengths) if max_ctx is None else max_ctx
+    ws = torch.empty(max(16, f4.decode_workspace_size(B, HQ, HKV, D, max_ctx, W, wt)), dtype=torch.uint8,
+                     device="cuda")
+    out, m, l = f4.paged_attn_decode_f4(layer.cache, layer.q, torch.from_numpy(layer.pt).cuda(),
+                                        torch.tensor(layer.lengths, dtype=torch.int32, device="cuda"), max_ctx, SM,
+                                        num_windows=W, window_tokens=wt, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
+
+
+def test_config1_layer_3x262144_yarn4_outliers():
+    print("case: 3 lanes x 262,144 tokens, YaRN x4, 1% outlier channels x8", flush=True)
+    layer = Layer(1, [262144] * 3, 4.0, outliers=True)
+    out, m, l = decode_call(layer)
+    assert np.isfinite(out).all()
+    for b, h in [(1, 2), (2, 0)]:
+        K, V = layer.oracle_kv(b, h)
+        ref = oatt.decode_head_from_values(layer.oracle_query(b, h), K, V, SM)
+        check_group(out[0, b, h * G:(h + 1) * G], m[0, b, h * G:(h + 1) * G], l[0, b, h * G:(h + 1) * G],
+                    (ref[0][0], ref[1][0], ref[2][0]), f"lane {b} kv head {h}")
+
+
+def test_config2_1048576_in_16_windows():
+    print("case: 1 x 1,048,576 tokens, 16 windows of 65,536, YaRN x4", flush=True)
+    W, wt, n = 16, 65536, 1048576
+    layer = Layer(2, [n], 4.0, outliers=False)
+    out, m, l = decode_call(layer, W=W, wt=wt)
+    for w, h in [(3, 1), (15, 3)]:  # window 15 ends at position 1,048,575
+        K, V = layer.oracle_kv(0, h, t_begin=w * wt, t_end=(w + 1) * wt)
+        ref = oatt.decode_head_from_values(layer.oracle_query(0, h), K, V, SM)
+        check_group(out[w, 0, h * G:(h + 1) * G], m[w, 0, h * G:(h + 1) * G], l[w, 0, h * G:(h + 1) * G],
+                    (ref[0][0], ref[1][0], ref[2][0]), f"window {w} kv head {h}")
+    # the 16 windows folded by lse_merge give the unwindowed answer
+    fo, fm, fl = f4.lse_merge(torch.from_numpy(m).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(out).cuda())
+    wo, wm, wl = decode_call(layer)
+    fo, fm, fl = fo.cpu().numpy(), fm.cpu().numpy(), fl.cpu().numpy()
+    assert_attention_close(fo, wo[0], "fold of 16 windows vs whole context")
+    assert np.all(np.abs(fm - wm[0]) <= 1e-5 * np.maximum(1.0, np.abs(wm[0])))
+    assert np.all(np.abs(fl - wl[0]) <= 1e-4 * wl[0])
+
+
+def test_config4_ragged_8():
+    lengths = synth.ragged_lengths(4)
+    print(f"case: ragged batch {lengths}, YaRN x1.220703125", flush=True)
+    layer = Layer(4, lengths, 1.220703125, outliers=False)
+    out, m, l = decode_call(layer)
+    order = np.argsort(lengths)
+    for b, h in [(int(order[-1]), 1), (int(order[0]), 2), (int(order[3]), 0)]:
+        K, V = layer.oracle_kv(b, h)
+        ref = oatt.decode_head_from_values(layer.oracle_query(b, h), K, V, SM)
+        check_group(out[0, b, h * G:(h + 1) * G], m[0, b, h * G:(h + 1) * G], l[0, b, h * G:(h + 1) * G],
+                    (ref[0][0], ref[1][0], ref[2][0]), f"sequence {b} (len {lengths[b]}) kv head {h}")
+
+
+def test_config3_prefill_2048_at_129024():
+    print("case: prefill of 2,048 queries at 129,024 over a 131,072-token window", flush=True)
+    T, window = 2048, 131072
+    pos0 = window - T
+    spec = spec_for(4.0)
+    none = np.zeros(0, np.int64)
+    # one sequence whose window of 2,048 pages is placed by a permutation of the pool
+    n_pages = window // PAGE
+    pt = synth.page_permutation(synth.rng(3, 54), n_pages).astype(np.int32)
+    cache = f4.F4Cache(n_pages, HKV, D)
+    yp = gpu_params(spec)
+    for j, t0 in enumerate(range(0, pos0, BLK)):
+        nb = min(BLK, pos0 - t0)
+        k = np.stack([draw_block(3, 0, h, j, nb, 0, none) for h in range(HKV)], axis=1)
+        v = np.stack([draw_block(3, 0, h, j, nb, 1, none) for h in range(HKV)], axis=1)
+        kt = torch.from_numpy(k).cuda()
+        c, s = f4.yarn_rope_table(yp, torch.arange(t0, t0 + nb, dtype=torch.int32, device="cuda"))
+        f4.yarn_rope_apply(c, s, kt, y=kt)
+        t = np.arange(t0, t0 + nb)
+        slots = (pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+        f4.kv_cache_write_f4(cache, kt, torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda())
+    g = synth.rng(3, 55)
+    kn = synth.normal_f32(g, (T, HKV, D))
+    vn = synth.normal_f32(g, (T, HKV, D))
+    qbits = synth.f32_to_bf16_bits(synth.normal_f32(g, (T, HQ, D)))
+    ws = torch.empty(max(16, f4.prefill_workspace_size(T, HQ, HKV, D, pos0)), dtype=torch.uint8, device="cuda")
+    out, m, l = f4.paged_attn_prefill_f4(cache, bf16_tensor(qbits), torch.from_numpy(kn).cuda(),
+                                         torch.from_numpy(vn).cuda(), torch.from_numpy(pt).cuda(), pos0, SM,
+                                         workspace=ws)
+    torch.cuda.synchronize()
+    out, m, l = out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
+    assert np.isfinite(out).all()
+    qv = bf16_values(qbits)
+    rows = [0, 1, 63, 64, 1000, 2046, 2047]
+    for h in (0, 3):
+        # oracle keys: rotated prefix + the chunk's raw keys, both quantised by the oracle
+        Ks, Vs = [], []
+        for j, t0 in enumerate(range(0, pos0, BLK)):
+            nb = min(BLK, pos0 - t0)
+            k = draw_block(3, 0, h, j, nb, 0, none).astype(np.float64)
+            cs, sn = table_f32(spec, np.arange(t0, t0 + nb))
+            Ks.append(oatt.dequantize_rows(oyarn.rope_apply(k[:, None, :], cs, sn, 256)[:, 0].astype(np.float32)))
+            Vs.append(oatt.dequantize_rows(draw_block(3, 0, h, j, nb, 1, none)))
+        Ks.append(oatt.dequantize_rows(kn[:, h]))
+        Vs.append(oatt.dequantize_rows(vn[:, h]))
+        K, V = np.concatenate(Ks), np.concatenate(Vs)
+        for i in rows:
+            n = pos0 + i + 1
+            ro, rm, rl = oatt.decode_head_from_values(qv[i, h * G:(h + 1) * G], K[:n], V[:n], SM)
+            check_group(out[i, h * G:(h + 1) * G], m[i, h * G:(h + 1) * G], l[i, h * G:(h + 1) * G],
+                        (ro[0], rm[0], rl[0]), f"prefill row {i} kv head {h}")
