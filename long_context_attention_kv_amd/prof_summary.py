@@ -1,0 +1,134 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels.
+
+    python -m long_context_attention_kv_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..."
+        per-kernel time table (the library's kernels first) from a
+        ``rocprofv3 --kernel-trace --stats -f csv`` run.
+
+    python -m long_context_attention_kv_amd.prof_summary traffic --fetch CSV --write CSV \\
+            --copy-bytes N --kernel NAME --source FILE --cmd-fetch "..." --cmd-write "..."
+        HBM bytes per launch of one kernel from a ``--pmc FETCH_SIZE`` run and a
+        ``--pmc WRITE_SIZE`` run (counter values in KiB per dispatch).  Each
+        counter is scaled by what it reads for a plain device copy of N bytes in
+        the same run (N read, N written), and the result is tagged with the
+        SHA-256 of the kernel's source file so that a reader can tell whether
+        the figure still belongs to the current kernel.
+
+Output is Markdown on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import statistics
+import sys
+
+
+def _short(name: str) -> str:
+    name = name.replace("f4kv::(anonymous namespace)::", "")
+    if "(" in name:
+        name = name[:name.index("(")]
+    return name.replace("void ", "").strip()
+
+
+def stats_table(path: str, cmd: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    lines = ["# Kernel time summary", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    ours = [r for r in rows if "f4kv::" in r["Name"]]
+    other = [r for r in rows if "f4kv::" not in r["Name"]]
+    for r in ours + other[:5]:
+        lines.append(f"| `{_short(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f}% |")
+    if len(other) > 5:
+        lines.append(f"| ({len(other) - 5} more kernels of the harness) | | | | | |")
+    return "\n".join(lines) + "\n"
+
+
+def _counter(path: str, counter: str):
+    by_kernel = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        by_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return by_kernel
+
+
+def _copy_value(by_kernel, nbytes: int) -> float:
+    """Median counter value (KiB) of the copy dispatches of nbytes: the largest
+    values among the blit/copy kernels."""
+    cand = []
+    for name, vals in by_kernel.items():
+        if "copyBuffer" in name or "copy" in name.lower():
+            cand.extend(vals)
+    cand.sort(reverse=True)
+    top = cand[:3]
+    if not top:
+        raise SystemExit("no copy dispatch found in the counter file")
+    return statistics.median(top)
+
+
+def _kernel_values(by_kernel, kernel: str):
+    vals = []
+    for name, v in by_kernel.items():
+        if kernel in name:
+            vals.extend(v)
+    if not vals:
+        raise SystemExit(f"kernel {kernel!r} not found in the counter file")
+    return vals
+
+
+def traffic(a) -> str:
+    fetch = _counter(a.fetch, "FETCH_SIZE")
+    write = _counter(a.write, "WRITE_SIZE")
+    copy_kib = a.copy_bytes / 1024.0
+    f_copy = _copy_value(fetch, a.copy_bytes)
+    w_copy = _copy_value(write, a.copy_bytes)
+    f_scale = copy_kib / f_copy
+    w_scale = copy_kib / w_copy
+    fk = _kernel_values(fetch, a.kernel)
+    wk = _kernel_values(write, a.kernel)
+    f_bytes = statistics.mean(fk) * f_scale * 1024.0
+    w_bytes = statistics.mean(wk) * w_scale * 1024.0
+    sha = hashlib.sha256(open(a.source, "rb").read()).hexdigest()
+    out = [f"# HBM traffic of `{a.kernel}`", "",
+           "Commands (FETCH_SIZE run, then WRITE_SIZE run):", "", "```", a.cmd_fetch, a.cmd_write, "```", "",
+           f"Copy calibration: a device copy of {a.copy_bytes} bytes ({copy_kib:.0f} KiB read and written) "
+           f"reads FETCH_SIZE = {f_copy:.1f} KiB and WRITE_SIZE = {w_copy:.1f} KiB per dispatch, so the "
+           f"counters are scaled by {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+           "| counter | dispatches | mean KiB | min KiB | max KiB | scaled bytes per launch |",
+           "|---|---:|---:|---:|---:|---:|",
+           f"| FETCH_SIZE | {len(fk)} | {statistics.mean(fk):.1f} | {min(fk):.1f} | {max(fk):.1f} | {f_bytes:.0f} |",
+           f"| WRITE_SIZE | {len(wk)} | {statistics.mean(wk):.1f} | {min(wk):.1f} | {max(wk):.1f} | {w_bytes:.0f} |",
+           "",
+           f"- fetch bytes per launch: {f_bytes:.0f}",
+           f"- write bytes per launch: {w_bytes:.0f}",
+           f"- traffic bytes per launch: {f_bytes + w_bytes:.0f}",
+           f"- copy scale fetch: {f_scale:.6f}",
+           f"- copy scale write: {w_scale:.6f}",
+           f"- {a.source.split('/')[-1]} sha256: `{sha}`", ""]
+    return "\n".join(out)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    a = ap.parse_args(argv)
+    sys.stdout.write(stats_table(a.csv, a.cmd) if a.what == "stats" else traffic(a))
+
+
+if __name__ == "__main__":
+    main()
