@@ -274,6 +274,18 @@ __device__ __forceinline__ void pin(uint4& v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
+// Raw buffer resource over `bytes` bytes at a wave-uniform address (gfx9
+// descriptor: 32-bit data, no swizzle); loads beyond `bytes` return 0 without
+// touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes at lane_offset + uniform_offset (the latter in a scalar register).
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int lane_offset, int uniform_offset = 0) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_offset, uniform_offset, 0));
+}
+
 __device__ __forceinline__ void lds_wave_sync() {
   // LDS writes of other lanes of this wave must land before it reads them
   // (LDS executes one wave's instructions in order; this keeps the compiler
@@ -398,14 +410,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   const int item = blockIdx.x;
   const int g = blockIdx.y;
   if (item >= *a.n_items) return;
-  const int4 it = a.items[item];
-  const int b = it.x % a.B;
-  const int win = it.x / a.B;
+  const int4 it_v = a.items[item];
+  // the work item is wave-uniform: keep it (and all that derives from it) in SGPRs
+  const int4 it = make_int4(__builtin_amdgcn_readfirstlane(it_v.x), __builtin_amdgcn_readfirstlane(it_v.y),
+                            __builtin_amdgcn_readfirstlane(it_v.z), __builtin_amdgcn_readfirstlane(it_v.w));
+  const int b = __builtin_amdgcn_readfirstlane(it.x % a.B);
+  const int win = __builtin_amdgcn_readfirstlane(it.x / a.B);
   const int pbeg = it.y, pend = it.z;
   const int nchunks = a.count[it.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so page ids load as scalars
   const int64_t out_row = static_cast<int64_t>(item) * a.Hq + g * G;  // first partial row of this group
 
   int ctx = a.ctx[b];
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     t1 = min(ctx, t0 + a.window_tokens);
   }
 
-  const QPrep<G>* QP = qprep + static_cast<int64_t>(b) * a.Hkv + g;
+  const QPrep<G>* QP = qprep + __builtin_amdgcn_readfirstlane(b * a.Hkv + g);
   float m_run[G], l_lane[G], o[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -428,6 +443,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   const int cj = lane >> 3;  // block holding this lane's 4 value channels
   const int sub = lane & 7;
   const int32_t* ptrow = a.pt + static_cast<int64_t>(b) * a.max_pages;
+  const int lane16 = lane * 16;
 
   for (int lp = pbeg + wave; lp < pend; lp += kWaves) {
     // The query operands are re-read (scalar loads) every page.  An offset the
@@ -436,18 +452,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     int qoff = 0;
     asm volatile("" : "+s"(qoff));
     const QPrep<G>* qp = reinterpret_cast<const QPrep<G>*>(reinterpret_cast<const char*>(QP) + qoff);
-    int32_t pid = ptrow[lp];
-    // an out-of-range page id reads page 0 and contributes nothing
+    // Tiles of this page through buffer resources with a scalar base: the lane
+    // offsets are constants, so no per-page address arithmetic runs on the VALU.
+    // An out-of-range page id gets empty resources (loads return 0, no traffic)
+    // and a mask that drops its tokens.
+    const int32_t pid = ptrow[lp];
     const bool pvalid = static_cast<uint32_t>(pid) < static_cast<uint32_t>(a.num_pages);
-    pid = pvalid ? pid : 0;
-    const int64_t ph = static_cast<int64_t>(pid) * a.Hkv + g;
-    const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
-    const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
+    const int64_t ph = static_cast<int64_t>(pvalid ? pid : 0) * a.Hkv + g;
+    const int tile_bytes = pvalid ? kPage * kHeadDim / 2 : 0;
+    const int scale_bytes = pvalid ? kPage * 8 * 2 : 0;
+    const auto rk = tile_rsrc(a.k_nib + ph * (kPage * kHeadDim / 2), tile_bytes);
+    const auto rv = tile_rsrc(a.v_nib + ph * (kPage * kHeadDim / 2), tile_bytes);
     uint4 kq[8], vq[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kq[c] = kt[c * 64 + lane];
-    const uint4 ks = reinterpret_cast<const uint4*>(a.k_scale + ph * (kPage * 8))[lane];
-    const uint4 vs = reinterpret_cast<const uint4*>(a.v_scale + ph * (kPage * 8))[lane];
+    for (int c = 0; c < 8; ++c) kq[c] = load16(rk, lane16, c * 1024);
+    const uint4 ks = load16(tile_rsrc(a.k_scale + ph * (kPage * 8), scale_bytes), lane16);
+    const uint4 vs = load16(tile_rsrc(a.v_scale + ph * (kPage * 8), scale_bytes), lane16);
 
     const int tok = lp * kPage + lane;
     const float tmask = (pvalid && tok >= t0 && tok < t1) ? 0.0f : -INFINITY;
@@ -493,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     // the key phase (other waves cover their latency)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vq[c] = vt[c * 64 + lane];
+    for (int c = 0; c < 8; ++c) vq[c] = load16(rv, lane16, c * 1024);
 
     // online softmax (log2 units), wave-uniform running max per head
     float alpha[G], p[G];
