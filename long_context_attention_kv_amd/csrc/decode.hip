@@ -48,6 +48,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWRow = 68;  // fp32 weights per (head, block) row: 64 tokens + 16 B pad
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the running max by
 
 // Query operands of one (sequence, KV head), prepared once per call and read by
 // the decode kernel with scalar loads (the same for every lane).
@@ -432,10 +433,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   }
 
   const QPrep<G>* QP = qprep + __builtin_amdgcn_readfirstlane(b * a.Hkv + g);
-  float m_run[G], l_lane[G], o[G][4];
+  float m_run[G], s_max[G], l_lane[G], o[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
+    s_max[h] = -INFINITY;
     l_lane[h] = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
@@ -466,6 +468,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     uint4 kq[8], vq[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) kq[c] = load16(rk, lane16, c * 1024);
+    __builtin_amdgcn_s_setprio(0);
     const uint4 ks = load16(tile_rsrc(a.k_scale + ph * (kPage * 8), scale_bytes), lane16);
     const uint4 vs = load16(tile_rsrc(a.v_scale + ph * (kPage * 8), scale_bytes), lane16);
 
@@ -515,20 +518,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 #pragma unroll
     for (int c = 0; c < 8; ++c) vq[c] = load16(rv, lane16, c * 1024);
 
-    // online softmax (log2 units), wave-uniform running max per head
-    float alpha[G], p[G];
+    // Online softmax in log2 units with a lazily raised running max: m_run
+    // moves (and the state is rescaled) only when some logit of the page
+    // exceeds it by more than kSlack, so weights stay below 2^kSlack and
+    // most pages skip the wave-wide max and the rescale.  The exact maximum is
+    // tracked per lane and restored at the end.
+    float p[G], s[G];
+    bool raise = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       // additive mask: written as a select, the compiler turns the whole key
       // phase into a branch on the token's validity
-      const float s = fmaf(logit[h], qp->kscale[h], tmask);
-      const float mn = fmaxf(m_run[h], wave_max(s));
-      // mn == -inf only while no valid token has been seen: keep everything at 0
-      const float ms = mn == -INFINITY ? 0.0f : mn;
-      alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - ms);
-      p[h] = __builtin_amdgcn_exp2f(s - ms);
-      l_lane[h] = fmaf(l_lane[h], alpha[h], p[h]);
-      m_run[h] = mn;
+      s[h] = fmaf(logit[h], qp->kscale[h], tmask);
+      s_max[h] = fmaxf(s_max[h], s[h]);
+      raise |= s[h] > m_run[h] + kSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m_run[h], wave_max(s[h]));
+        // mn == -inf only while no valid token has been seen: nothing to rescale
+        const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - mn);
+        l_lane[h] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[h][d] *= alpha;
+        m_run[h] = mn;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      p[h] = __builtin_amdgcn_exp2f(s[h] - (m_run[h] == -INFINITY ? 0.0f : m_run[h]));
+      l_lane[h] += p[h];
     }
 
     // weights p * s_v per (head, block) to LDS in fp32, transposed to [head][block][token]
@@ -541,11 +561,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     }
     lds_wave_sync();
 
-    // values: lane = channels 4*lane .. 4*lane+3 (block cj)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) o[h][d] *= alpha[h];
+    // values: lane = channels 4*lane .. 4*lane+3 (block cj); this wave's VALU
+    // stream goes first while it holds its operands
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if ((ct & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two token groups' weights in flight
@@ -591,10 +609,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     }
   }
 
-  // ---- epilogue: fold the 4 waves -------------------------------------------
+  // ---- epilogue: restore the exact maximum, fold the 4 waves ---------------
+  __builtin_amdgcn_s_setprio(0);
   float l_w[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_lane[h]);
+  for (int h = 0; h < G; ++h) {
+    const float mx = wave_max(s_max[h]);  // <= m_run + kSlack
+    if (mx != -INFINITY) {
+      const float f = __builtin_amdgcn_exp2f(m_run[h] - mx);
+      l_lane[h] *= f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[h][d] *= f;
+      m_run[h] = mx;
+    }
+    l_w[h] = wave_sum(l_lane[h]);
+  }
   __syncthreads();  // every wave is done with the weight buffers
 #pragma unroll
   for (int h = 0; h < G; ++h) {
