@@ -20,6 +20,12 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-file flags.  The prefill kernel rescales its MFMA accumulators with VALU
+# multiplies; MFMA in the VGPR form keeps them in VGPRs instead of copying them
+# between AGPRs and VGPRs every iteration.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -39,7 +45,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIP_FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -12,20 +12,30 @@
 // group are stacked (32 per wave), and a range of key pages.  Per page of 64 keys:
 //  1. the workgroup dequantises the page's K and V cells into LDS as fp16,
 //     K as [token][channel] and V transposed as [channel][token], each as an
-//     fp16 pair hi + lo (hi = fp16(x), lo = fp16(x - hi)): a single fp16
-//     rounding of the dequantised keys alone moves the output by up to ~2e-3
-//     of its RMS, and of V or P by ~1e-3 each;
+//     exact pair hi + lo: the block scale s is split into s_hi (its top 8
+//     significant bits) and s_lo = s - s_hi, so (n - 8) * s_hi and
+//     (n - 8) * s_lo are both exact in fp16 and the dequantisation runs on
+//     packed fp16 arithmetic (two values per instruction).  A single fp16
+//     rounding of the dequantised keys alone would move the output by up to
+//     ~2e-3 of its RMS, and of V or P by ~1e-3 each;
 //  2. each wave forms S^T = K Q^T for its 32 query rows with fp16 MFMA
 //     (v_mfma_f32_32x32x16_f16, fp32 accumulate) as K_hi Q + K_lo Q, so one
 //     lane owns one query row and its row max / sum are mostly lane-local;
-//  3. online softmax in log2 units;
-//  4. O^T += V^T P^T with the same MFMA as V_hi P_hi + V_lo P_hi + V_hi P_lo,
-//     P split into fp16 hi + lo like V, so only K's fp16 rounding remains.
+//  3. online softmax in log2 units with a lazily raised running max; the
+//     causal mask only on pages that reach past the tile's first position;
+//  4. O^T += V^T P^T with the same MFMA as V_hi P_hi + V_hi P_lo + V_lo P,
+//     P split into fp16 hi + lo like V, so only fp32 rounding remains.
 //     The exp'd scores already sit in the B-operand lanes; the token order
 //     inside a k-step is permuted to match and the V^T reads use the same
 //     permutation.
-// Queries keep their 64 fp16 operand registers for the whole loop.  Longer
-// key ranges are split over several workgroups and folded by the merge kernel.
+// The dequantisation overlaps the matrix work of the other operand: V of a
+// page is unpacked while the waves multiply its K, and K of the next page
+// while they multiply V (two barriers per page).  The raw cells of the next
+// page are requested a page ahead.  Queries keep their 64 fp16 operand
+// registers for the whole loop; K's channels sit in LDS in the order the
+// unpack produces them (0, 4, 1, 5, 2, 6, 3, 7 within each group of 8) and the
+// query operands use the same order.  Longer key ranges are split over
+// several workgroups and folded by the merge kernel.
 #include "f4kv_internal.h"
 
 namespace f4kv {
@@ -41,9 +51,9 @@ constexpr int kCT = 1;             // 32-row column tiles per wave
 constexpr int kQPos = kWaves * kCT * 8;  // query positions per workgroup
 constexpr int kG = 4;              // query heads per KV head
 constexpr int kKStride = kHeadDim + 8;   // fp16 per K row in LDS (528 B)
-constexpr int kVStride = kPage + 8;      // fp16 per V^T row in LDS (144 B, 16-byte aligned rows)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 4.0f;  // log2 units a score may exceed its row's running max by
 
 struct PrefillArgs {
   const uint8_t* k_nib;
@@ -61,15 +71,113 @@ struct PrefillArgs {
 };
 
 struct __align__(16) PrefillSmem {
-  _Float16 k[2][kPage][kKStride];      // K as hi, lo * 2^10
-  _Float16 vt[2][kHeadDim][kVStride];  // V^T as hi, lo
+  _Float16 k[2][kPage][kKStride];  // K as hi, lo * 2^10
+  _Float16 vt[2][kHeadDim][kPage]; // V^T as hi, lo * 2^10, tokens in MFMA order, 16-byte chunks swizzled
 };
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+
+// Exact split of a pair of fp16 scales: hi keeps the top 8 significant bits of
+// each, lo = (s - hi) * 2^10 the rest (at most 3 significant bits; the fp16
+// difference is exact, subnormal or not, and the power-of-two factor keeps the
+// products below out of the subnormal range).
+__device__ __forceinline__ void split_scales(uint32_t bits2, half2v_t& hi, half2v_t& lo1024) {
+  hi = __builtin_bit_cast(half2v_t, bits2 & 0xFFF8FFF8u);
+  lo1024 = (__builtin_bit_cast(half2v_t, bits2) - hi) *
+           half2v_t{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+}
+
+// Two nibbles at bit offsets sh and 16 + sh of w as the fp16 pair (n0 - 8, n1 - 8).
+__device__ __forceinline__ half2v_t nibble_pair(uint32_t w, int sh) {
+  const uint32_t b = ((w >> sh) & 0x000F000Fu) | 0x64006400u;  // 1024 + n in each half
+  return __builtin_bit_cast(half2v_t, b) + half2v_t{static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+}
+
+__device__ __forceinline__ uint32_t as_u32(half2v_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// V^T rows.  Within each group of 16 tokens the tokens are stored in the order
+// the PV MFMA consumes them, 0-3, 8-11, 4-7, 12-15, so that a lane's 8 operand
+// tokens of a k-step are one 16-byte chunk; the row's 8 chunks are
+// XOR-permuted by row so that neither the writers of one instruction
+// (channel quads, rows 4 apart) nor the readers (consecutive rows) meet on a
+// bank.
+__device__ __forceinline__ int vt_chunk(int row, int chunk) { return chunk ^ (((row >> 2) ^ (row << 1)) & 7); }
+
+// Raw cells of one page for this thread: two 16-byte K units, two V units and
+// their scales.  The scales stay as loaded (one 16-bit value per register) and
+// are paired at their use, so no load waits on another.
+struct PageRaw {
+  uint4 k[2], v[2];
+  uint32_t ks[2];     // scale of each K unit (block c, token t)
+  uint32_t vs[2][8];  // scales of the 8 tokens of each V unit (block j / 8)
+};
+
+__device__ __forceinline__ void load_page(const PrefillArgs& a, int64_t ph, int tid, PageRaw& r) {
+  const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
+  const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
+  const uint16_t* ksc = a.k_scale + ph * (kPage * 8);
+  const uint16_t* vsc = a.v_scale + ph * (kPage * 8);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int unit = tid + u * kThreads;
+    r.k[u] = kt[unit];
+    const int vunit = (2 * (tid >> 6) + u) * 64 + (tid & 63);  // V: octets 2w, 2w+1 of channel quad tid%64
+    r.v[u] = vt[vunit];
+    r.ks[u] = ksc[(unit & 63) * 8 + (unit >> 6)];  // K unit (block unit/64, token unit%64)
+    const int c = vunit >> 6, j = vunit & 63;      // V unit (tokens 8c.., channels 4j..)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.vs[u][e] = vsc[(8 * c + e) * 8 + (j >> 3)];
+  }
+}
+
+// Dword j of K unit u -> 8 channels of one LDS row [token][channel in unpack
+// order], hi and lo * 2^10.
+__device__ __forceinline__ void unpack_k(PrefillSmem& sm, const PageRaw& r, int tid, int u, int j) {
+  const int unit = tid + u * kThreads;
+  const int c = unit >> 6, t = unit & 63;
+  half2v_t kh, kl;
+  split_scales(r.ks[u] | (r.ks[u] << 16), kh, kl);
+  const half2v_t s2h = kh, s2l = kl;
+  const uint32_t w = word(r.k[u], j);
+  uint4 hi, lo;
+  half2v_t n;
+  n = nibble_pair(w, 0);  hi.x = as_u32(n * s2h); lo.x = as_u32(n * s2l);
+  n = nibble_pair(w, 4);  hi.y = as_u32(n * s2h); lo.y = as_u32(n * s2l);
+  n = nibble_pair(w, 8);  hi.z = as_u32(n * s2h); lo.z = as_u32(n * s2l);
+  n = nibble_pair(w, 12); hi.w = as_u32(n * s2h); lo.w = as_u32(n * s2l);
+  *reinterpret_cast<uint4*>(&sm.k[0][t][32 * c + 8 * j]) = hi;
+  *reinterpret_cast<uint4*>(&sm.k[1][t][32 * c + 8 * j]) = lo;
+}
+
+// Channel 4 j + i of this thread's two V units (tokens 16 g .. 16 g + 15,
+// g = wave) -> two 16-byte chunks of V^T row 4 j + i, hi and lo * 2^10.
+__device__ __forceinline__ void unpack_v(PrefillSmem& sm, const PageRaw& r, int tid, int i) {
+  const int g = tid >> 6, j = tid & 63;
+  uint32_t hv[2][4], lv[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // tokens 16 g + 8 u + 2k, + 1
+      half2v_t sh, sl;
+      split_scales(r.vs[u][2 * k] | (r.vs[u][2 * k + 1] << 16), sh, sl);
+      const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i);
+      hv[u][k] = as_u32(n * sh);
+      lv[u][k] = as_u32(n * sl);
+    }
+  const int row = 4 * j + i;
+  // chunk 2g: tokens 0-3 and 8-11 of the group; chunk 2g+1: tokens 4-7 and 12-15
+  const int c0 = vt_chunk(row, 2 * g), c1 = vt_chunk(row, 2 * g + 1);
+  *reinterpret_cast<uint4*>(&sm.vt[0][row][8 * c0]) = make_uint4(hv[0][0], hv[0][1], hv[1][0], hv[1][1]);
+  *reinterpret_cast<uint4*>(&sm.vt[0][row][8 * c1]) = make_uint4(hv[0][2], hv[0][3], hv[1][2], hv[1][3]);
+  *reinterpret_cast<uint4*>(&sm.vt[1][row][8 * c0]) = make_uint4(lv[0][0], lv[0][1], lv[1][0], lv[1][1]);
+  *reinterpret_cast<uint4*>(&sm.vt[1][row][8 * c1]) = make_uint4(lv[0][2], lv[0][3], lv[1][2], lv[1][3]);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ pt) {
   __shared__ PrefillSmem sm;
   const int qt = blockIdx.x;     // query tile
   const int g = blockIdx.y;      // KV head
@@ -87,15 +195,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     qvalid[c] = qi[c] < a.T;
     qpos[c] = a.pos0 + qi[c];
   }
+  const int qpos_first = a.pos0 + qt * kQPos;  // no key below it needs a mask
 
   // key pages this workgroup covers: up to the tile's last position, split evenly
   const int tile_last = min(a.T, (qt + 1) * kQPos) - 1;
   const int npages = (a.pos0 + tile_last) / kPage + 1;
   const int per = (npages + a.kv_splits - 1) / a.kv_splits;
-  const int pbeg = split * per;
-  const int pend = min(npages, pbeg + per);
+  // uniform: the division runs on the vector unit, keep the range in scalar registers
+  const int pbeg = __builtin_amdgcn_readfirstlane(split * per);
+  const int pend = __builtin_amdgcn_readfirstlane(min(npages, pbeg + per));
 
-  // Q^T operands: lane holds q[row][16 s + 8 half + 0..7] for s = 0..15
+  // Q^T operands: lane holds q[row][channels of LDS positions 16 s + 8 half + 0..7]
+  // for s = 0..15, i.e. channels 8 (2 s + half) + {0, 4, 1, 5, 2, 6, 3, 7}
   half8_t qf[kCT][16];
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
@@ -106,8 +217,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t w = word(raw, j);
-        qf[c][s][2 * j] = static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w)));
-        qf[c][s][2 * j + 1] = static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w >> 16)));
+        // channels 2j, 2j + 1 of the group go to positions 2j and 2j - 7 (+8 for the odd half)
+        qf[c][s][(2 * j) < 4 ? 4 * j : 4 * j - 7] = static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w)));
+        qf[c][s][(2 * j + 1) < 4 ? 4 * j + 2 : 4 * j - 5] =
+            static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w >> 16)));
       }
     }
   }
@@ -117,150 +230,152 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   for (int c = 0; c < kCT; ++c)
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[c][d] = float16_t{};
-  float m_run[kCT], l_lane[kCT];
+  float m_run[kCT], s_max[kCT], l_lane[kCT];
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
     m_run[c] = -INFINITY;
+    s_max[c] = -INFINITY;
     l_lane[c] = 0.0f;
   }
 
-  for (int lp = pbeg; lp < pend; ++lp) {
-    int32_t pid = a.pt[lp];
-    const bool pvalid = static_cast<uint32_t>(pid) < static_cast<uint32_t>(a.num_pages);
-    pid = pvalid ? pid : 0;
-    const int64_t ph = static_cast<int64_t>(pid) * a.Hkv + g;
-    const uint4* ktile = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
-    const uint4* vtile = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
-    uint4 kraw[2], vraw[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      kraw[r] = ktile[tid + r * kThreads];
-      vraw[r] = vtile[tid + r * kThreads];
-    }
-    __syncthreads();  // previous page's LDS reads are done
-    // ---- dequantise K: units (block c, token t) of 16 bytes ----
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int u = tid + r * kThreads;
-      const int c = u >> 6, t = u & 63;
-      const float s = static_cast<float>(__builtin_bit_cast(_Float16, a.k_scale[(ph * kPage + t) * 8 + c]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = word(kraw[r], j);
-        half8_t v8, l8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = static_cast<float>(static_cast<int>((w >> (4 * e)) & 0xFu) - 8) * s;  // exact
-          const _Float16 hi = static_cast<_Float16>(x);
-          v8[e] = hi;
-          l8[e] = static_cast<_Float16>((x - static_cast<float>(hi)) * 1024.0f);
-        }
-        *reinterpret_cast<half8_t*>(&sm.k[0][t][32 * c + 8 * j]) = v8;
-        *reinterpret_cast<half8_t*>(&sm.k[1][t][32 * c + 8 * j]) = l8;
-      }
-    }
-    // ---- dequantise V: units (c, j) = tokens 8c..8c+7 x channels 4j..4j+3 ----
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int u = tid + r * kThreads;
-      const int c = u >> 6, j = u & 63;
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        half8_t v8, l8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {  // token 8c + e sits in dword e/2, half e%2
-          const int t = 8 * c + e;
-          const uint32_t w = word(vraw[r], e >> 1);
-          const int n = static_cast<int>((w >> (16 * (e & 1) + 4 * dd)) & 0xFu) - 8;
-          const float s = static_cast<float>(__builtin_bit_cast(_Float16, a.v_scale[(ph * kPage + t) * 8 + (j >> 3)]));
-          const float x = static_cast<float>(n) * s;  // exact in fp32
-          const _Float16 hi = static_cast<_Float16>(x);
-          v8[e] = hi;
-          l8[e] = static_cast<_Float16>((x - static_cast<float>(hi)) * 1024.0f);
-        }
-        *reinterpret_cast<half8_t*>(&sm.vt[0][4 * j + dd][8 * c]) = v8;
-        *reinterpret_cast<half8_t*>(&sm.vt[1][4 * j + dd][8 * c]) = l8;
-      }
-    }
-    __syncthreads();
+  auto page_handle = [&](int lp, bool& valid) {
+    int32_t pid = pt[lp];
+    valid = static_cast<uint32_t>(pid) < static_cast<uint32_t>(a.num_pages);
+    return static_cast<int64_t>(valid ? pid : 0) * a.Hkv + g;
+  };
 
-    // ---- per 32-token tile: S^T = K Q^T, online softmax, O^T += V^T P^T ----
+  // Cells in flight: `raw` holds page lp + 1 (its K is unpacked during this
+  // iteration's PV work, its V during the next iteration's S work) and `ahead`
+  // page lp + 2, requested two pages before their first use.
+  // The page id of page lp + 3 is read one iteration before its cells are.
+  PageRaw cur, raw, ahead;
+  bool cur_valid = false, raw_valid = false, ahead_valid = false;
+  int32_t pid_next = pt[min(pbeg + 2, max(pend - 1, 0))];
+  if (pbeg < pend) {
+    load_page(a, page_handle(pbeg, cur_valid), tid, cur);
+    if (pbeg + 1 < pend) load_page(a, page_handle(pbeg + 1, raw_valid), tid, raw);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) unpack_k(sm, cur, tid, x >> 2, x & 3);
+  }
+
+  for (int lp = pbeg; lp < pend; ++lp) {
+    // read before this iteration's cell loads, so that waiting for it next
+    // iteration does not wait for them (a clamped index keeps the read in range)
+    const int32_t pid_after = pt[min(lp + 3, pend - 1)];
+    if (lp + 2 < pend) {
+      ahead_valid = static_cast<uint32_t>(pid_next) < static_cast<uint32_t>(a.num_pages);
+      load_page(a, static_cast<int64_t>(ahead_valid ? pid_next : 0) * a.Hkv + g, tid, ahead);
+    }
+    pid_next = pid_after;
+    __syncthreads();  // K of this page is in LDS; every wave is done with the previous V
+
+    // ---- S^T = K Q^T for both 32-token tiles, V of this page unpacked meanwhile ----
+    // K_lo (held times 2^10) goes first, the accumulator is scaled by 2^-10, then K_hi.
+    float16_t st[2][kCT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int c = 0; c < kCT; ++c) st[tt][c] = float16_t{};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      float16_t st[kCT], sl[kCT];
 #pragma unroll
-      for (int c = 0; c < kCT; ++c) {
-        st[c] = float16_t{};
-        sl[c] = float16_t{};
-      }
+      for (int part = 1; part >= 0; --part) {
+        if (part == 0) {
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound the K operand reads in flight
-        const half8_t ka = *reinterpret_cast<const half8_t*>(&sm.k[0][tt * 32 + col][16 * s + 8 * half]);
-        const half8_t kl = *reinterpret_cast<const half8_t*>(&sm.k[1][tt * 32 + col][16 * s + 8 * half]);
+          for (int c = 0; c < kCT; ++c) st[tt][c] *= 1.0f / 1024.0f;
+        }
 #pragma unroll
-        for (int c = 0; c < kCT; ++c) {
-          st[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[c][s], st[c], 0, 0, 0);
-          sl[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qf[c][s], sl[c], 0, 0, 0);
+        for (int s = 0; s < 16; ++s) {
+          if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound the K operand reads in flight
+          if (s == 0) unpack_v(sm, cur, tid, tt * 2 + (1 - part));  // one V channel per 16 MFMAs
+          const half8_t ka = *reinterpret_cast<const half8_t*>(&sm.k[part][tt * 32 + col][16 * s + 8 * half]);
+#pragma unroll
+          for (int c = 0; c < kCT; ++c)
+            st[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[c][s], st[tt][c], 0, 0, 0);
         }
       }
+    }
+    __syncthreads();  // V of this page is in LDS; every wave is done with this K
+
+    // ---- softmax and O^T += V^T P^T per tile, K of the next page unpacked meanwhile ----
+    const bool more = lp + 1 < pend;
+    const bool need_mask = !cur_valid || lp * kPage + kPage - 1 > qpos_first;
 #pragma unroll
-      for (int c = 0; c < kCT; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st[c][i] = fmaf(sl[c][i], 1.0f / 1024.0f, st[c][i]);
-      // B operands per [column tile][k-step of this token tile]: P * 2^15 as hi and lo
-      // (for V hi), and P * 2^5 (for V lo, which LDS holds times 2^10).  The power-of-two
-      // offsets keep every fp16 operand out of the subnormal range; the accumulator
-      // carries P * 2^15 throughout and the epilogue divides it out.
+    for (int tt = 0; tt < 2; ++tt) {
+      // B operands per [column tile][k-step of this token tile]: P * 2^11 as hi and lo
+      // (for V hi), and P * 2 (for V lo, which LDS holds times 2^10).  P stays below
+      // 2^kSlack, so P * 2^11 fits fp16; the power-of-two offsets keep the operands of
+      // all but negligible weights out of the subnormal range.  The accumulator carries
+      // P * 2^11 throughout and the epilogue divides it out.
       half8_t pb[kCT][2], pl[kCT][2], pv5[kCT][2];
 #pragma unroll
       for (int c = 0; c < kCT; ++c) {
-        // scores of this lane's query row (log2 units), causal mask
+        // scores of this lane's query row (log2 units), causal mask where the page needs it
         float mx = -INFINITY;
+        if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-          const bool ok = pvalid && qvalid[c] && tok <= qpos[c];
-          st[c][i] = ok ? st[c][i] * a.qk_scale : -INFINITY;
-          mx = fmaxf(mx, st[c][i]);
+          for (int i = 0; i < 16; ++i) {
+            const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+            const bool ok = cur_valid && qvalid[c] && tok <= qpos[c];
+            st[tt][c][i] = ok ? st[tt][c][i] * a.qk_scale : -INFINITY;
+            mx = fmaxf(mx, st[tt][c][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            st[tt][c][i] *= a.qk_scale;
+            mx = fmaxf(mx, st[tt][c][i]);
+          }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m_run[c], mx);
-        const float ms = mn == -INFINITY ? 0.0f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[c] - ms);
-        m_run[c] = mn;
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(st[c][i] - ms);
-          psum += pv;
-          const float ps = pv * 32768.0f;
-          const _Float16 ph = static_cast<_Float16>(ps);
-          pb[c][i / 8][i % 8] = ph;
-          pl[c][i / 8][i % 8] = static_cast<_Float16>(ps - static_cast<float>(ph));
-          pv5[c][i / 8][i % 8] = static_cast<_Float16>(pv * 32.0f);
-        }
-        l_lane[c] = fmaf(l_lane[c], alpha, psum);
-        if (__ballot(alpha != 1.0f)) {  // rescale only when some row's max moved
+        // the row's running max is raised only when a score exceeds it by more than
+        // kSlack, so the accumulator is rescaled on few pages; the exact maximum is
+        // tracked and restored at the end
+        s_max[c] = fmaxf(s_max[c], mx);
+        const bool raise = mx > m_run[c] + kSlack;
+        if (__ballot(raise)) {
+          const float mn = raise ? mx : m_run[c];
+          const float alpha = m_run[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[c] - mn);
+          m_run[c] = mn;
+          l_lane[c] *= alpha;
 #pragma unroll
           for (int d = 0; d < 8; ++d) acc[c][d] *= alpha;
         }
+        const float ms = m_run[c] == -INFINITY ? 0.0f : m_run[c];
+        float psum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(st[tt][c][i] - ms);
+          const float p1 = __builtin_amdgcn_exp2f(st[tt][c][i + 1] - ms);
+          psum += p0 + p1;
+          const float s0 = p0 * 2048.0f, s1 = p1 * 2048.0f;
+          const auto h = __builtin_amdgcn_cvt_pkrtz(s0, s1);  // hi, rounded toward zero
+          const auto l = __builtin_amdgcn_cvt_pkrtz(s0 - static_cast<float>(h[0]), s1 - static_cast<float>(h[1]));
+          const auto v1 = __builtin_amdgcn_cvt_pkrtz(p0 * 2.0f, p1 * 2.0f);
+          pb[c][i / 8][i % 8] = static_cast<_Float16>(h[0]);
+          pb[c][i / 8][i % 8 + 1] = static_cast<_Float16>(h[1]);
+          pl[c][i / 8][i % 8] = static_cast<_Float16>(l[0]);
+          pl[c][i / 8][i % 8 + 1] = static_cast<_Float16>(l[1]);
+          pv5[c][i / 8][i % 8] = static_cast<_Float16>(v1[0]);
+          pv5[c][i / 8][i % 8 + 1] = static_cast<_Float16>(v1[1]);
+        }
+        l_lane[c] += psum;
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        // k-step covers tokens base + {0..3, 8..11} (+4 for the upper half lanes)
-        const int base = tt * 32 + s2 * 16 + 4 * half;
+        // k-step covers tokens 16 (2 tt + s2) + {0..3, 8..11} (+4 for the upper half lanes)
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           __builtin_amdgcn_sched_barrier(0);  // bound the V^T operand reads in flight
+          if ((d & 3) == 0 && more) {         // K unpack chunk of the next page overlapping these MFMAs
+            const int x = tt * 4 + s2 * 2 + d / 4;
+            unpack_k(sm, raw, tid, x >> 2, x & 3);
+          }
 #pragma unroll
           for (int part = 0; part < 2; ++part) {
-            const _Float16* vrow = &sm.vt[part][d * 32 + col][0];
-            const half4_t a0 = *reinterpret_cast<const half4_t*>(vrow + base);
-            const half4_t a1 = *reinterpret_cast<const half4_t*>(vrow + base + 8);
-            half8_t va;
-            va[0] = a0[0]; va[1] = a0[1]; va[2] = a0[2]; va[3] = a0[3];
-            va[4] = a1[0]; va[5] = a1[1]; va[6] = a1[2]; va[7] = a1[3];
+            const int row = d * 32 + col;
+            const half8_t va =
+                *reinterpret_cast<const half8_t*>(&sm.vt[part][row][8 * vt_chunk(row, (tt * 2 + s2) * 2 + half)]);
 #pragma unroll
             for (int c = 0; c < kCT; ++c) {
               if (part == 0) {  // V hi x (P hi + P lo); P lo x V lo is below fp32 rounding
@@ -274,16 +389,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
+    cur = raw;
+    cur_valid = raw_valid;
+    raw = ahead;
+    raw_valid = ahead_valid;
   }
 
   // ---- epilogue: this lane's two query rows ----
   const int R = a.T * a.Hq;
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
-    const float L = l_lane[c] + __shfl_xor(l_lane[c], 32, 64);
+    // restore the exact maximum: the normalised output is unchanged, the sum scales
+    const float f = s_max[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[c] - s_max[c]);
+    const float Lr = l_lane[c] + __shfl_xor(l_lane[c], 32, 64);  // in units of exp2(m_run)
+    const float L = Lr * f;
     if (!qvalid[c]) continue;
     const int64_t row = static_cast<int64_t>(split) * R + static_cast<int64_t>(qi[c]) * a.Hq + hq;
-    const float inv = L > 0.0f ? 1.0f / (L * 32768.0f) : 0.0f;  // P was carried times 2^15
+    const float inv = Lr > 0.0f ? 1.0f / (Lr * 2048.0f) : 0.0f;  // P was carried times 2^11
     float* dst = a.o + row * kHeadDim;
 #pragma unroll
     for (int d = 0; d < 8; ++d)
@@ -297,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<float4_t*>(dst + d * 32 + i4 * 8 + half * 4) = v;
       }
     if (half == 0) {
-      if (a.m) a.m[row] = L > 0.0f ? m_run[c] * kLn2 : -INFINITY;
+      if (a.m) a.m[row] = L > 0.0f ? s_max[c] * kLn2 : -INFINITY;
       if (a.l) a.l[row] = L;
     }
   }
@@ -354,7 +476,7 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
     a.l = out_l;
   }
   timing_begin(F4KV_KERNEL_PREFILL, s);
-  hipLaunchKernelGGL(prefill_kernel, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_kernel, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a, pt);
   hipError_t e = hipGetLastError();
   timing_end(F4KV_KERNEL_PREFILL, s);
   if (e != hipSuccess || plan.kv_splits == 1) return e;
