@@ -276,22 +276,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int c = 0; c < kCT; ++c) st[tt][c] = float16_t{};
+    // the two tiles' MFMAs alternate, so consecutive MFMAs never depend on each other
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int part = 1; part >= 0; --part) {
+      if (part == 0) {
 #pragma unroll
-      for (int part = 1; part >= 0; --part) {
-        if (part == 0) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int c = 0; c < kCT; ++c) st[tt][c] *= 1.0f / 1024.0f;
-        }
+      }
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound the K operand reads in flight
-          if (s == 0) unpack_v(sm, cur, tid, tt * 2 + (1 - part));  // one V channel per 16 MFMAs
-          const half8_t ka = *reinterpret_cast<const half8_t*>(&sm.k[part][tt * 32 + col][16 * s + 8 * half]);
+      for (int s = 0; s < 16; ++s) {
+        if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound the K operand reads in flight
+        if ((s & 7) == 0) unpack_v(sm, cur, tid, (1 - part) * 2 + s / 8);  // one V channel per 16 MFMAs
+        const half8_t ka0 = *reinterpret_cast<const half8_t*>(&sm.k[part][col][16 * s + 8 * half]);
+        const half8_t ka1 = *reinterpret_cast<const half8_t*>(&sm.k[part][32 + col][16 * s + 8 * half]);
 #pragma unroll
-          for (int c = 0; c < kCT; ++c)
-            st[tt][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[c][s], st[tt][c], 0, 0, 0);
+        for (int c = 0; c < kCT; ++c) {
+          st[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka0, qf[c][s], st[0][c], 0, 0, 0);
+          st[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka1, qf[c][s], st[1][c], 0, 0, 0);
         }
       }
     }
@@ -365,26 +368,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       for (int s2 = 0; s2 < 2; ++s2) {
         // k-step covers tokens 16 (2 tt + s2) + {0..3, 8..11} (+4 for the upper half lanes)
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
+        for (int dp = 0; dp < 4; ++dp) {  // channel tiles d = 2 dp, 2 dp + 1, their MFMAs alternating
           __builtin_amdgcn_sched_barrier(0);  // bound the V^T operand reads in flight
-          if ((d & 3) == 0 && more) {         // K unpack chunk of the next page overlapping these MFMAs
-            const int x = tt * 4 + s2 * 2 + d / 4;
+          if ((dp & 1) == 0 && more) {        // K unpack chunk of the next page overlapping these MFMAs
+            const int x = tt * 4 + s2 * 2 + dp / 2;
             unpack_k(sm, raw, tid, x >> 2, x & 3);
           }
+          half8_t vh[2], vl[2];
 #pragma unroll
-          for (int part = 0; part < 2; ++part) {
-            const int row = d * 32 + col;
-            const half8_t va =
-                *reinterpret_cast<const half8_t*>(&sm.vt[part][row][8 * vt_chunk(row, (tt * 2 + s2) * 2 + half)]);
+          for (int e = 0; e < 2; ++e) {
+            const int row = (2 * dp + e) * 32 + col;
+            const int ch = 8 * vt_chunk(row, (tt * 2 + s2) * 2 + half);
+            vh[e] = *reinterpret_cast<const half8_t*>(&sm.vt[0][row][ch]);
+            vl[e] = *reinterpret_cast<const half8_t*>(&sm.vt[1][row][ch]);
+          }
 #pragma unroll
-            for (int c = 0; c < kCT; ++c) {
-              if (part == 0) {  // V hi x (P hi + P lo); P lo x V lo is below fp32 rounding
-                acc[c][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[c][s2], acc[c][d], 0, 0, 0);
-                acc[c][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pl[c][s2], acc[c][d], 0, 0, 0);
-              } else {          // (V lo * 2^10) x (P * 2^5)
-                acc[c][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pv5[c][s2], acc[c][d], 0, 0, 0);
-              }
-            }
+          for (int c = 0; c < kCT; ++c) {
+            // V hi x (P hi + P lo), then (V lo * 2^10) x (P * 2); P lo x V lo is below fp32 rounding
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh[e], pb[c][s2], acc[c][2 * dp + e], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh[e], pl[c][s2], acc[c][2 * dp + e], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl[e], pv5[c][s2], acc[c][2 * dp + e], 0, 0, 0);
           }
         }
       }
