@@ -107,16 +107,36 @@ __device__ __forceinline__ uint32_t as_u32(half2v_t v) { return __builtin_bit_ca
 // bank.
 __device__ __forceinline__ int vt_chunk(int row, int chunk) { return chunk ^ (((row >> 2) ^ (row << 1)) & 7); }
 
-// Raw cells of one page for this thread: two 16-byte K units, two V units and
-// their scales.  The scales stay as loaded (one 16-bit value per register) and
-// are paired at their use, so no load waits on another.
-struct PageRaw {
+// Cells of one page for this thread: two 16-byte K units, two V units and
+// their scales.  A load leaves each scale in a register of its own, so that no
+// load waits on another; `packed` pairs them once they have arrived.
+struct PageLoad {
   uint4 k[2], v[2];
   uint32_t ks[2];     // scale of each K unit (block c, token t)
   uint32_t vs[2][8];  // scales of the 8 tokens of each V unit (block j / 8)
 };
 
-__device__ __forceinline__ void load_page(const PrefillArgs& a, int64_t ph, int tid, PageRaw& r) {
+struct PageRaw {
+  uint4 k[2], v[2];
+  uint32_t ks;        // the two K unit scales, one per half
+  uint32_t vs[2][4];  // V scales of tokens (2k, 2k + 1), one per half
+};
+
+__device__ __forceinline__ PageRaw packed(const PageLoad& l) {
+  PageRaw r;
+  r.k[0] = l.k[0];
+  r.k[1] = l.k[1];
+  r.v[0] = l.v[0];
+  r.v[1] = l.v[1];
+  r.ks = l.ks[0] | (l.ks[1] << 16);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.vs[u][k] = l.vs[u][2 * k] | (l.vs[u][2 * k + 1] << 16);
+  return r;
+}
+
+__device__ __forceinline__ void load_page(const PrefillArgs& a, int64_t ph, int tid, PageLoad& r) {
   const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
   const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
   const uint16_t* ksc = a.k_scale + ph * (kPage * 8);
@@ -140,8 +160,8 @@ __device__ __forceinline__ void unpack_k(PrefillSmem& sm, const PageRaw& r, int 
   const int unit = tid + u * kThreads;
   const int c = unit >> 6, t = unit & 63;
   half2v_t kh, kl;
-  split_scales(r.ks[u] | (r.ks[u] << 16), kh, kl);
-  const half2v_t s2h = kh, s2l = kl;
+  split_scales(r.ks, kh, kl);
+  const half2v_t s2h{kh[u], kh[u]}, s2l{kl[u], kl[u]};
   const uint32_t w = word(r.k[u], j);
   uint4 hi, lo;
   half2v_t n;
@@ -163,7 +183,7 @@ __device__ __forceinline__ void unpack_v(PrefillSmem& sm, const PageRaw& r, int 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // tokens 16 g + 8 u + 2k, + 1
       half2v_t sh, sl;
-      split_scales(r.vs[u][2 * k] | (r.vs[u][2 * k + 1] << 16), sh, sl);
+      split_scales(r.vs[u][k], sh, sl);
       const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i);
       hv[u][k] = as_u32(n * sh);
       lv[u][k] = as_u32(n * sl);
@@ -248,12 +268,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   // iteration's PV work, its V during the next iteration's S work) and `ahead`
   // page lp + 2, requested two pages before their first use.
   // The page id of page lp + 3 is read one iteration before its cells are.
-  PageRaw cur, raw, ahead;
+  PageRaw cur, raw;
+  PageLoad ahead;
   bool cur_valid = false, raw_valid = false, ahead_valid = false;
   int32_t pid_next = pt[min(pbeg + 2, max(pend - 1, 0))];
   if (pbeg < pend) {
-    load_page(a, page_handle(pbeg, cur_valid), tid, cur);
-    if (pbeg + 1 < pend) load_page(a, page_handle(pbeg + 1, raw_valid), tid, raw);
+    load_page(a, page_handle(pbeg, cur_valid), tid, ahead);
+    cur = packed(ahead);
+    if (pbeg + 1 < pend) {
+      load_page(a, page_handle(pbeg + 1, raw_valid), tid, ahead);
+      raw = packed(ahead);
+    }
 #pragma unroll
     for (int x = 0; x < 8; ++x) unpack_k(sm, cur, tid, x >> 2, x & 3);
   }
@@ -276,35 +301,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int c = 0; c < kCT; ++c) st[tt][c] = float16_t{};
-    // the two tiles' MFMAs alternate, so consecutive MFMAs never depend on each other
+    // 32 steps (K_lo k-steps 0..15, then K_hi), the two tiles' MFMAs alternating
+    // so consecutive MFMAs never depend on each other; K operands are read from
+    // LDS a step ahead of their MFMAs
+    half8_t kbuf[2][2];
+    auto kread = [&](int step, half8_t* dst) {
+      const int part = step < 16 ? 1 : 0, ks = step & 15;
+      dst[0] = *reinterpret_cast<const half8_t*>(&sm.k[part][col][16 * ks + 8 * half]);
+      dst[1] = *reinterpret_cast<const half8_t*>(&sm.k[part][32 + col][16 * ks + 8 * half]);
+    };
+    kread(0, kbuf[0]);
 #pragma unroll
-    for (int part = 1; part >= 0; --part) {
-      if (part == 0) {
+    for (int step = 0; step < 32; ++step) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + 1 < 32) kread(step + 1, kbuf[(step + 1) & 1]);
+      if ((step & 7) == 0) unpack_v(sm, cur, tid, step / 8);  // one V channel per 16 MFMAs
+      if (step == 16) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int c = 0; c < kCT; ++c) st[tt][c] *= 1.0f / 1024.0f;
       }
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // bound the K operand reads in flight
-        if ((s & 7) == 0) unpack_v(sm, cur, tid, (1 - part) * 2 + s / 8);  // one V channel per 16 MFMAs
-        const half8_t ka0 = *reinterpret_cast<const half8_t*>(&sm.k[part][col][16 * s + 8 * half]);
-        const half8_t ka1 = *reinterpret_cast<const half8_t*>(&sm.k[part][32 + col][16 * s + 8 * half]);
-#pragma unroll
-        for (int c = 0; c < kCT; ++c) {
-          st[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka0, qf[c][s], st[0][c], 0, 0, 0);
-          st[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka1, qf[c][s], st[1][c], 0, 0, 0);
-        }
+      for (int c = 0; c < kCT; ++c) {
+        st[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kbuf[step & 1][0], qf[c][step & 15], st[0][c], 0, 0, 0);
+        st[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kbuf[step & 1][1], qf[c][step & 15], st[1][c], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // V of this page is in LDS; every wave is done with this K
 
     // ---- softmax and O^T += V^T P^T per tile, K of the next page unpacked meanwhile ----
     const bool more = lp + 1 < pend;
     const bool need_mask = !cur_valid || lp * kPage + kPage - 1 > qpos_first;
+    // V operands of PV step (tile tt, step = 4 s2 + dp): hi and lo of channel tiles 2 dp, 2 dp + 1
+    auto vread = [&](int tt, int step, half8_t* dst) {
+      const int s2 = step >> 2, dp = step & 3;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = (2 * dp + e) * 32 + col;
+        const int ch = 8 * vt_chunk(row, (tt * 2 + s2) * 2 + half);
+        dst[e] = *reinterpret_cast<const half8_t*>(&sm.vt[0][row][ch]);
+        dst[2 + e] = *reinterpret_cast<const half8_t*>(&sm.vt[1][row][ch]);
+      }
+    };
+    half8_t vbuf[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      vread(tt, 0, vbuf[0]);  // in flight during the softmax
       // B operands per [column tile][k-step of this token tile]: P * 2^11 as hi and lo
       // (for V hi), and P * 2 (for V lo, which LDS holds times 2^10).  P stays below
       // 2^kSlack, so P * 2^11 fits fp16; the power-of-two offsets keep the operands of
@@ -313,24 +357,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       half8_t pb[kCT][2], pl[kCT][2], pv5[kCT][2];
 #pragma unroll
       for (int c = 0; c < kCT; ++c) {
-        // scores of this lane's query row (log2 units), causal mask where the page needs it
+        // raw scores of this lane's query row; the scale sm_scale * log2(e) > 0 is
+        // applied inside the exponent, the causal mask where the page needs it
         float mx = -INFINITY;
         if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
             const bool ok = cur_valid && qvalid[c] && tok <= qpos[c];
-            st[tt][c][i] = ok ? st[tt][c][i] * a.qk_scale : -INFINITY;
+            st[tt][c][i] = ok ? st[tt][c][i] : -INFINITY;
             mx = fmaxf(mx, st[tt][c][i]);
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            st[tt][c][i] *= a.qk_scale;
-            mx = fmaxf(mx, st[tt][c][i]);
-          }
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[tt][c][i]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.qk_scale;  // log2 units
         // the row's running max is raised only when a score exceeds it by more than
         // kSlack, so the accumulator is rescaled on few pages; the exact maximum is
         // tracked and restored at the end
@@ -344,24 +386,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
 #pragma unroll
           for (int d = 0; d < 8; ++d) acc[c][d] *= alpha;
         }
-        const float ms = m_run[c] == -INFINITY ? 0.0f : m_run[c];
+        // P * 2^11 = exp2(s * scale - m + 11)
+        const float off = 11.0f - (m_run[c] == -INFINITY ? 0.0f : m_run[c]);
         float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(st[tt][c][i] - ms);
-          const float p1 = __builtin_amdgcn_exp2f(st[tt][c][i + 1] - ms);
-          psum += p0 + p1;
-          const float s0 = p0 * 2048.0f, s1 = p1 * 2048.0f;
+          const float s0 = __builtin_amdgcn_exp2f(fmaf(st[tt][c][i], a.qk_scale, off));
+          const float s1 = __builtin_amdgcn_exp2f(fmaf(st[tt][c][i + 1], a.qk_scale, off));
+          psum += s0 + s1;
           const auto h = __builtin_amdgcn_cvt_pkrtz(s0, s1);  // hi, rounded toward zero
           const auto l = __builtin_amdgcn_cvt_pkrtz(s0 - static_cast<float>(h[0]), s1 - static_cast<float>(h[1]));
-          const auto v1 = __builtin_amdgcn_cvt_pkrtz(p0 * 2.0f, p1 * 2.0f);
+          // P * 2 for V lo from the hi part alone: the dropped P lo x V lo is ~2^-23 relative
+          const half2v_t v1 = __builtin_bit_cast(half2v_t, h) *
+                              half2v_t{static_cast<_Float16>(1.0f / 1024.0f), static_cast<_Float16>(1.0f / 1024.0f)};
           pb[c][i / 8][i % 8] = static_cast<_Float16>(h[0]);
           pb[c][i / 8][i % 8 + 1] = static_cast<_Float16>(h[1]);
           pl[c][i / 8][i % 8] = static_cast<_Float16>(l[0]);
           pl[c][i / 8][i % 8 + 1] = static_cast<_Float16>(l[1]);
-          pv5[c][i / 8][i % 8] = static_cast<_Float16>(v1[0]);
-          pv5[c][i / 8][i % 8 + 1] = static_cast<_Float16>(v1[1]);
+          pv5[c][i / 8][i % 8] = v1[0];
+          pv5[c][i / 8][i % 8 + 1] = v1[1];
         }
+        psum *= 1.0f / 2048.0f;
         l_lane[c] += psum;
       }
 #pragma unroll
@@ -369,38 +414,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
         // k-step covers tokens 16 (2 tt + s2) + {0..3, 8..11} (+4 for the upper half lanes)
 #pragma unroll
         for (int dp = 0; dp < 4; ++dp) {  // channel tiles d = 2 dp, 2 dp + 1, their MFMAs alternating
-          __builtin_amdgcn_sched_barrier(0);  // bound the V^T operand reads in flight
-          if ((dp & 1) == 0 && more) {        // K unpack chunk of the next page overlapping these MFMAs
+          const int step = s2 * 4 + dp;
+          __builtin_amdgcn_sched_barrier(0);
+          if (step + 1 < 8) vread(tt, step + 1, vbuf[(step + 1) & 1]);  // next step's V operands
+          if ((dp & 1) == 0 && more) {  // K unpack chunk of the next page overlapping these MFMAs
             const int x = tt * 4 + s2 * 2 + dp / 2;
             unpack_k(sm, raw, tid, x >> 2, x & 3);
           }
-          half8_t vh[2], vl[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int row = (2 * dp + e) * 32 + col;
-            const int ch = 8 * vt_chunk(row, (tt * 2 + s2) * 2 + half);
-            vh[e] = *reinterpret_cast<const half8_t*>(&sm.vt[0][row][ch]);
-            vl[e] = *reinterpret_cast<const half8_t*>(&sm.vt[1][row][ch]);
-          }
+          const half8_t* vb = vbuf[step & 1];
 #pragma unroll
           for (int c = 0; c < kCT; ++c) {
             // V hi x (P hi + P lo), then (V lo * 2^10) x (P * 2); P lo x V lo is below fp32 rounding
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh[e], pb[c][s2], acc[c][2 * dp + e], 0, 0, 0);
+              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[e], pb[c][s2], acc[c][2 * dp + e], 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vh[e], pl[c][s2], acc[c][2 * dp + e], 0, 0, 0);
+              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[e], pl[c][s2], acc[c][2 * dp + e], 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vl[e], pv5[c][s2], acc[c][2 * dp + e], 0, 0, 0);
+              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[2 + e], pv5[c][s2], acc[c][2 * dp + e], 0, 0, 0);
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     cur = raw;
     cur_valid = raw_valid;
-    raw = ahead;
+    if (lp + 2 < pend) raw = packed(ahead);
     raw_valid = ahead_valid;
   }
 
