@@ -73,6 +73,7 @@ struct PrefillArgs {
 struct __align__(16) PrefillSmem {
   _Float16 k[2][kPage][kKStride];  // K as hi, lo * 2^10
   _Float16 vt[2][kHeadDim][kPage]; // V^T as hi, lo * 2^10, tokens in MFMA order, 16-byte chunks swizzled
+  uint16_t vsc[2][8][kPage];       // V scales [page parity][block][token]
 };
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
@@ -107,58 +108,42 @@ __device__ __forceinline__ uint32_t as_u32(half2v_t v) { return __builtin_bit_ca
 // bank.
 __device__ __forceinline__ int vt_chunk(int row, int chunk) { return chunk ^ (((row >> 2) ^ (row << 1)) & 7); }
 
-// Cells of one page for this thread: two 16-byte K units, two V units and
-// their scales.  A load leaves each scale in a register of its own, so that no
-// load waits on another; `packed` pairs them once they have arrived.
-struct PageLoad {
-  uint4 k[2], v[2];
-  uint32_t ks[2];     // scale of each K unit (block c, token t)
-  uint32_t vs[2][8];  // scales of the 8 tokens of each V unit (block j / 8)
-};
-
+// Cells of one page for this thread: K units (block 2 w + u, token t) and V
+// units (tokens 8 (2 w + u) .., channel quad j) for u = 0, 1 (w = wave, t = j =
+// lane), the two K scales (adjacent in memory) and one dword of the page's V
+// scale tile (token tid / 4, blocks 2 (tid % 4), + 1), which goes through LDS.
 struct PageRaw {
   uint4 k[2], v[2];
-  uint32_t ks;        // the two K unit scales, one per half
-  uint32_t vs[2][4];  // V scales of tokens (2k, 2k + 1), one per half
+  uint32_t ks;   // scales of the two K units, one per half
+  uint32_t vsd;  // two V scales of one token
 };
 
-__device__ __forceinline__ PageRaw packed(const PageLoad& l) {
-  PageRaw r;
-  r.k[0] = l.k[0];
-  r.k[1] = l.k[1];
-  r.v[0] = l.v[0];
-  r.v[1] = l.v[1];
-  r.ks = l.ks[0] | (l.ks[1] << 16);
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) r.vs[u][k] = l.vs[u][2 * k] | (l.vs[u][2 * k + 1] << 16);
-  return r;
-}
-
-__device__ __forceinline__ void load_page(const PrefillArgs& a, int64_t ph, int tid, PageLoad& r) {
+__device__ __forceinline__ void load_page(const PrefillArgs& a, int64_t ph, int tid, PageRaw& r) {
   const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
   const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
   const uint16_t* ksc = a.k_scale + ph * (kPage * 8);
   const uint16_t* vsc = a.v_scale + ph * (kPage * 8);
+  const int w = tid >> 6, t = tid & 63;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int unit = tid + u * kThreads;
-    r.k[u] = kt[unit];
-    const int vunit = (2 * (tid >> 6) + u) * 64 + (tid & 63);  // V: octets 2w, 2w+1 of channel quad tid%64
-    r.v[u] = vt[vunit];
-    r.ks[u] = ksc[(unit & 63) * 8 + (unit >> 6)];  // K unit (block unit/64, token unit%64)
-    const int c = vunit >> 6, j = vunit & 63;      // V unit (tokens 8c.., channels 4j..)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.vs[u][e] = vsc[(8 * c + e) * 8 + (j >> 3)];
+    r.k[u] = kt[(2 * w + u) * 64 + t];
+    r.v[u] = vt[(2 * w + u) * 64 + t];
   }
+  r.ks = *reinterpret_cast<const uint32_t*>(ksc + t * 8 + 2 * w);
+  r.vsd = *reinterpret_cast<const uint32_t*>(vsc + (tid >> 2) * 8 + 2 * (tid & 3));
+}
+
+// This thread's dword of the page's V scale tile -> LDS [block][token].
+__device__ __forceinline__ void store_vscales(PrefillSmem& sm, const PageRaw& r, int tid, int parity) {
+  const int t = tid >> 2, b = 2 * (tid & 3);
+  sm.vsc[parity][b][t] = static_cast<uint16_t>(r.vsd);
+  sm.vsc[parity][b + 1][t] = static_cast<uint16_t>(r.vsd >> 16);
 }
 
 // Dword j of K unit u -> 8 channels of one LDS row [token][channel in unpack
 // order], hi and lo * 2^10.
 __device__ __forceinline__ void unpack_k(PrefillSmem& sm, const PageRaw& r, int tid, int u, int j) {
-  const int unit = tid + u * kThreads;
-  const int c = unit >> 6, t = unit & 63;
+  const int c = 2 * (tid >> 6) + u, t = tid & 63;
   half2v_t kh, kl;
   split_scales(r.ks, kh, kl);
   const half2v_t s2h{kh[u], kh[u]}, s2l{kl[u], kl[u]};
@@ -174,16 +159,19 @@ __device__ __forceinline__ void unpack_k(PrefillSmem& sm, const PageRaw& r, int 
 }
 
 // Channel 4 j + i of this thread's two V units (tokens 16 g .. 16 g + 15,
-// g = wave) -> two 16-byte chunks of V^T row 4 j + i, hi and lo * 2^10.
-__device__ __forceinline__ void unpack_v(PrefillSmem& sm, const PageRaw& r, int tid, int i) {
+// g = wave) -> two 16-byte chunks of V^T row 4 j + i, hi and lo * 2^10.  The
+// scales of those 16 tokens come from LDS already paired (tokens 2k, 2k + 1).
+__device__ __forceinline__ void unpack_v(PrefillSmem& sm, const PageRaw& r, int tid, int i, int parity) {
   const int g = tid >> 6, j = tid & 63;
+  const uint4 sa = *reinterpret_cast<const uint4*>(&sm.vsc[parity][j >> 3][16 * g]);
+  const uint4 sb = *reinterpret_cast<const uint4*>(&sm.vsc[parity][j >> 3][16 * g + 8]);
   uint32_t hv[2][4], lv[2][4];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // tokens 16 g + 8 u + 2k, + 1
       half2v_t sh, sl;
-      split_scales(r.vs[u][k], sh, sl);
+      split_scales(word(u ? sb : sa, k), sh, sl);
       const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i);
       hv[u][k] = as_u32(n * sh);
       lv[u][k] = as_u32(n * sl);
@@ -268,19 +256,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   // iteration's PV work, its V during the next iteration's S work) and `ahead`
   // page lp + 2, requested two pages before their first use.
   // The page id of page lp + 3 is read one iteration before its cells are.
-  PageRaw cur, raw;
-  PageLoad ahead;
+  PageRaw cur, raw, ahead;
   bool cur_valid = false, raw_valid = false, ahead_valid = false;
   int32_t pid_next = pt[min(pbeg + 2, max(pend - 1, 0))];
   if (pbeg < pend) {
-    load_page(a, page_handle(pbeg, cur_valid), tid, ahead);
-    cur = packed(ahead);
-    if (pbeg + 1 < pend) {
-      load_page(a, page_handle(pbeg + 1, raw_valid), tid, ahead);
-      raw = packed(ahead);
-    }
+    load_page(a, page_handle(pbeg, cur_valid), tid, cur);
+    if (pbeg + 1 < pend) load_page(a, page_handle(pbeg + 1, raw_valid), tid, raw);
 #pragma unroll
     for (int x = 0; x < 8; ++x) unpack_k(sm, cur, tid, x >> 2, x & 3);
+    store_vscales(sm, cur, tid, pbeg & 1);
   }
 
   for (int lp = pbeg; lp < pend; ++lp) {
@@ -315,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     for (int step = 0; step < 32; ++step) {
       __builtin_amdgcn_sched_barrier(0);
       if (step + 1 < 32) kread(step + 1, kbuf[(step + 1) & 1]);
-      if ((step & 7) == 0) unpack_v(sm, cur, tid, step / 8);  // one V channel per 16 MFMAs
+      if ((step & 7) == 0) unpack_v(sm, cur, tid, step / 8, lp & 1);  // one V channel per 16 MFMAs
       if (step == 16) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
@@ -420,6 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
           if ((dp & 1) == 0 && more) {  // K unpack chunk of the next page overlapping these MFMAs
             const int x = tt * 4 + s2 * 2 + dp / 2;
             unpack_k(sm, raw, tid, x >> 2, x & 3);
+            if (x == 7) store_vscales(sm, raw, tid, (lp + 1) & 1);
           }
           const half8_t* vb = vbuf[step & 1];
 #pragma unroll
@@ -441,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     }
     cur = raw;
     cur_valid = raw_valid;
-    if (lp + 2 < pend) raw = packed(ahead);
+    raw = ahead;
     raw_valid = ahead_valid;
   }
 
