@@ -71,8 +71,8 @@ struct PrefillArgs {
 };
 
 struct __align__(16) PrefillSmem {
-  _Float16 k[2][kPage][kKStride];  // K as hi, lo * 2^10
-  _Float16 vt[2][kHeadDim][kPage]; // V^T as hi, lo * 2^10, tokens in MFMA order, 16-byte chunks swizzled
+  _Float16 k[2][kPage][kKStride];  // K as hi, lo
+  _Float16 vt[2][kHeadDim][kPage]; // V^T as hi, lo, tokens in MFMA order, 16-byte chunks swizzled
   uint16_t vsc[2][8][kPage];       // V scales [page parity][block][token]
 };
 
@@ -83,13 +83,13 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
 
 // Exact split of a pair of fp16 scales: hi keeps the top 8 significant bits of
-// each, lo = (s - hi) * 2^10 the rest (at most 3 significant bits; the fp16
-// difference is exact, subnormal or not, and the power-of-two factor keeps the
-// products below out of the subnormal range).
-__device__ __forceinline__ void split_scales(uint32_t bits2, half2v_t& hi, half2v_t& lo1024) {
+// each, lo = s - hi the rest (at most 3 significant bits).  Both products with
+// n - 8 are exact in fp16: they are integer multiples of the scale's last place
+// (at least 2^-24, the fp16 subnormal step) with at most 11 and 6 significant
+// bits; the matrix cores take fp16 subnormals exactly.
+__device__ __forceinline__ void split_scales(uint32_t bits2, half2v_t& hi, half2v_t& lo) {
   hi = __builtin_bit_cast(half2v_t, bits2 & 0xFFF8FFF8u);
-  lo1024 = (__builtin_bit_cast(half2v_t, bits2) - hi) *
-           half2v_t{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  lo = __builtin_bit_cast(half2v_t, bits2) - hi;
 }
 
 // Two nibbles at bit offsets sh and 16 + sh of w as the fp16 pair (n0 - 8, n1 - 8).
@@ -108,41 +108,48 @@ __device__ __forceinline__ uint32_t as_u32(half2v_t v) { return __builtin_bit_ca
 // bank.
 __device__ __forceinline__ int vt_chunk(int row, int chunk) { return chunk ^ (((row >> 2) ^ (row << 1)) & 7); }
 
-// Cells of one page for this thread: K units (block 2 w + u, token t) and V
-// units (tokens 8 (2 w + u) .., channel quad j) for u = 0, 1 (w = wave, t = j =
-// lane), the two K scales (adjacent in memory) and one dword of the page's V
-// scale tile (token tid / 4, blocks 2 (tid % 4), + 1), which goes through LDS.
-struct PageRaw {
-  uint4 k[2], v[2];
+// Cells of one page for this thread, in two parts that are requested at
+// different times: the K part (K units (block 2 w + u, token t) for u = 0, 1,
+// w = wave, t = lane; the two K scales, adjacent in memory; one dword of the
+// page's V scale tile (token tid / 4, blocks 2 (tid % 4), + 1), which goes
+// through LDS) and the V part (V units: tokens 8 (2 w + u) .., channel quad j = lane).
+struct KRaw {
+  uint4 k[2];
   uint32_t ks;   // scales of the two K units, one per half
   uint32_t vsd;  // two V scales of one token
 };
+struct VRaw {
+  uint4 v[2];
+};
 
-__device__ __forceinline__ void load_page(const PrefillArgs& a, int64_t ph, int tid, PageRaw& r) {
+__device__ __forceinline__ void load_k(const PrefillArgs& a, int64_t ph, int tid, KRaw& r) {
   const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
-  const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
   const uint16_t* ksc = a.k_scale + ph * (kPage * 8);
   const uint16_t* vsc = a.v_scale + ph * (kPage * 8);
   const int w = tid >> 6, t = tid & 63;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    r.k[u] = kt[(2 * w + u) * 64 + t];
-    r.v[u] = vt[(2 * w + u) * 64 + t];
-  }
+  for (int u = 0; u < 2; ++u) r.k[u] = kt[(2 * w + u) * 64 + t];
   r.ks = *reinterpret_cast<const uint32_t*>(ksc + t * 8 + 2 * w);
   r.vsd = *reinterpret_cast<const uint32_t*>(vsc + (tid >> 2) * 8 + 2 * (tid & 3));
 }
 
+__device__ __forceinline__ void load_v(const PrefillArgs& a, int64_t ph, int tid, VRaw& r) {
+  const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
+  const int w = tid >> 6, t = tid & 63;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) r.v[u] = vt[(2 * w + u) * 64 + t];
+}
+
 // This thread's dword of the page's V scale tile -> LDS [block][token].
-__device__ __forceinline__ void store_vscales(PrefillSmem& sm, const PageRaw& r, int tid, int parity) {
+__device__ __forceinline__ void store_vscales(PrefillSmem& sm, const KRaw& r, int tid, int parity) {
   const int t = tid >> 2, b = 2 * (tid & 3);
   sm.vsc[parity][b][t] = static_cast<uint16_t>(r.vsd);
   sm.vsc[parity][b + 1][t] = static_cast<uint16_t>(r.vsd >> 16);
 }
 
 // Dword j of K unit u -> 8 channels of one LDS row [token][channel in unpack
-// order], hi and lo * 2^10.
-__device__ __forceinline__ void unpack_k(PrefillSmem& sm, const PageRaw& r, int tid, int u, int j) {
+// order], hi and lo.
+__device__ __forceinline__ void unpack_k(PrefillSmem& sm, const KRaw& r, int tid, int u, int j) {
   const int c = 2 * (tid >> 6) + u, t = tid & 63;
   half2v_t kh, kl;
   split_scales(r.ks, kh, kl);
@@ -158,31 +165,41 @@ __device__ __forceinline__ void unpack_k(PrefillSmem& sm, const PageRaw& r, int 
   *reinterpret_cast<uint4*>(&sm.k[1][t][32 * c + 8 * j]) = lo;
 }
 
-// Channel 4 j + i of this thread's two V units (tokens 16 g .. 16 g + 15,
-// g = wave) -> two 16-byte chunks of V^T row 4 j + i, hi and lo * 2^10.  The
-// scales of those 16 tokens come from LDS already paired (tokens 2k, 2k + 1).
-__device__ __forceinline__ void unpack_v(PrefillSmem& sm, const PageRaw& r, int tid, int i, int parity) {
+// V unpack, channel 4 j + i of this thread's two V units (tokens 16 g .. 16 g +
+// 15, g = wave) -> two 16-byte chunks of V^T row 4 j + i, hi and lo.
+// The scales of those 16 tokens come from LDS already paired (tokens 2k, 2k +
+// 1), read and split once per page.  The work is cut into 8 pieces of one token pair of
+// one unit each: pieces 0-3 fill chunk 2g (tokens 0-3 and 8-11 of the group),
+// pieces 4-7 chunk 2g + 1 (tokens 4-7 and 12-15), each chunk written to LDS
+// after its fourth piece.
+struct VScales {
+  half2v_t hi[8], lo[8];  // split scales of tokens 16 g + 2k, + 1 (k = 0..7), block j / 8
+};
+
+__device__ __forceinline__ void read_vscales(const PrefillSmem& sm, int tid, int parity, VScales& s) {
   const int g = tid >> 6, j = tid & 63;
   const uint4 sa = *reinterpret_cast<const uint4*>(&sm.vsc[parity][j >> 3][16 * g]);
   const uint4 sb = *reinterpret_cast<const uint4*>(&sm.vsc[parity][j >> 3][16 * g + 8]);
-  uint32_t hv[2][4], lv[2][4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {  // tokens 16 g + 8 u + 2k, + 1
-      half2v_t sh, sl;
-      split_scales(word(u ? sb : sa, k), sh, sl);
-      const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i);
-      hv[u][k] = as_u32(n * sh);
-      lv[u][k] = as_u32(n * sl);
-    }
-  const int row = 4 * j + i;
-  // chunk 2g: tokens 0-3 and 8-11 of the group; chunk 2g+1: tokens 4-7 and 12-15
-  const int c0 = vt_chunk(row, 2 * g), c1 = vt_chunk(row, 2 * g + 1);
-  *reinterpret_cast<uint4*>(&sm.vt[0][row][8 * c0]) = make_uint4(hv[0][0], hv[0][1], hv[1][0], hv[1][1]);
-  *reinterpret_cast<uint4*>(&sm.vt[0][row][8 * c1]) = make_uint4(hv[0][2], hv[0][3], hv[1][2], hv[1][3]);
-  *reinterpret_cast<uint4*>(&sm.vt[1][row][8 * c0]) = make_uint4(lv[0][0], lv[0][1], lv[1][0], lv[1][1]);
-  *reinterpret_cast<uint4*>(&sm.vt[1][row][8 * c1]) = make_uint4(lv[0][2], lv[0][3], lv[1][2], lv[1][3]);
+  for (int k = 0; k < 4; ++k) {
+    split_scales(word(sa, k), s.hi[k], s.lo[k]);
+    split_scales(word(sb, k), s.hi[4 + k], s.lo[4 + k]);
+  }
+}
+
+__device__ __forceinline__ void v_piece(PrefillSmem& sm, const VRaw& r, const VScales& s, int tid, int i, int p,
+                                        uint32_t* hv, uint32_t* lv) {
+  const int g = tid >> 6, j = tid & 63;
+  const int u = (p >> 1) & 1, k = (p & 1) + 2 * (p >> 2), slot = p & 3;
+  const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i);
+  hv[slot] = as_u32(n * s.hi[4 * u + k]);
+  lv[slot] = as_u32(n * s.lo[4 * u + k]);
+  if (slot == 3) {
+    const int row = 4 * j + i;
+    const int c = vt_chunk(row, 2 * g + (p >> 2));
+    *reinterpret_cast<uint4*>(&sm.vt[0][row][8 * c]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    *reinterpret_cast<uint4*>(&sm.vt[1][row][8 * c]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ pt) {
@@ -233,6 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     }
   }
 
+  static_assert(kCT == 1, "the page loop below is written for one column tile per wave");
   float16_t acc[kCT][8];  // O^T per column tile: 8 channel tiles of 32
 #pragma unroll
   for (int c = 0; c < kCT; ++c)
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   float m_run[kCT], s_max[kCT], l_lane[kCT];
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
-    m_run[c] = -INFINITY;
+    m_run[c] = -INFINITY;  // an integer (log2 units) once finite, so rescale factors are powers of two
     s_max[c] = -INFINITY;
     l_lane[c] = 0.0f;
   }
@@ -252,183 +270,229 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     return static_cast<int64_t>(valid ? pid : 0) * a.Hkv + g;
   };
 
-  // Cells in flight: `raw` holds page lp + 1 (its K is unpacked during this
-  // iteration's PV work, its V during the next iteration's S work) and `ahead`
-  // page lp + 2, requested two pages before their first use.
-  // The page id of page lp + 3 is read one iteration before its cells are.
-  PageRaw cur, raw, ahead;
-  bool cur_valid = false, raw_valid = false, ahead_valid = false;
+  // Cells in flight at the top of iteration lp: vcur = V of page lp (unpacked
+  // during this page's S work), kraw = K of page lp + 1 (unpacked during this
+  // page's PV work); requested now: vnext = V of page lp + 1 and kahead = K of
+  // page lp + 2.  The page id of page lp + 3 is read one iteration before its
+  // cells are.  Cells past the range are unpacked into buffers nobody reads.
+  KRaw kraw{}, kahead{};
+  VRaw vcur{}, vnext{};
+  bool cur_valid = false, kraw_valid = false, kahead_valid = false;
+  int64_t kraw_ph = 0, kahead_ph = 0;
   int32_t pid_next = pt[min(pbeg + 2, max(pend - 1, 0))];
   if (pbeg < pend) {
-    load_page(a, page_handle(pbeg, cur_valid), tid, cur);
-    if (pbeg + 1 < pend) load_page(a, page_handle(pbeg + 1, raw_valid), tid, raw);
+    KRaw k0;
+    const int64_t ph0 = page_handle(pbeg, cur_valid);
+    load_k(a, ph0, tid, k0);
+    load_v(a, ph0, tid, vcur);
+    if (pbeg + 1 < pend) {
+      kraw_ph = page_handle(pbeg + 1, kraw_valid);
+      load_k(a, kraw_ph, tid, kraw);
+    }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) unpack_k(sm, cur, tid, x >> 2, x & 3);
-    store_vscales(sm, cur, tid, pbeg & 1);
+    for (int x = 0; x < 8; ++x) unpack_k(sm, k0, tid, x >> 2, x & 3);
+    store_vscales(sm, k0, tid, pbeg & 1);
   }
+
+  // V^T operand addresses of this lane: row col (+ 32 d), chunk (2 (2 tt + s2) + half) swizzled
+  const char* vt_lane = reinterpret_cast<const char*>(&sm.vt[0][col][0]);
+  int voff[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) voff[c4] = 16 * vt_chunk(col, 2 * c4 + half);
+
+  // ---- the page loop ----------------------------------------------------
+  // One wave per SIMD issues everything in order, so the dequantisation and
+  // softmax work is cut into small pieces placed between the MFMAs (one piece
+  // per MFMA step, each step a scheduling region of its own): the VALU pieces
+  // issue while the matrix core works on the step's MFMAs.
+
+  // S^T of one 32-token tile: the K_lo chain, then the K_hi chain into the same
+  // accumulator (dependent MFMAs issue back to back).  K operands are read from
+  // LDS two steps ahead.
+  auto s_phase = [&](int tt, float16_t& st, auto&& piece) {
+    auto kread = [&](int step) {
+      return *reinterpret_cast<const half8_t*>(&sm.k[step < 16 ? 1 : 0][32 * tt + col][16 * (step & 15) + 8 * half]);
+    };
+    half8_t kb[3];
+    kb[0] = kread(0);
+    kb[1] = kread(1);
+#pragma unroll
+    for (int step = 0; step < 32; ++step) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + 2 < 32) kb[(step + 2) % 3] = kread(step + 2);
+      piece(step);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_f16(kb[step % 3], qf[0][step & 15], st, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // O^T += V^T P^T for one token tile: step = 8 s2 + d covers k-step s2 (tokens
+  // 16 (2 tt + s2) + {0..3, 8..11}, +4 for the upper half lanes) and channel
+  // tile d with the MFMAs V_hi P_hi, V_hi P_lo and V_lo P_hi (P_lo V_lo is
+  // below fp32 rounding).  V
+  // operands are read from LDS a step ahead.
+  auto pv_phase = [&](int tt, const half8_t* pb, const half8_t* pl, auto&& piece) {
+    auto vread = [&](int step, half8_t* dst) {
+      // row d * 32 + col: the swizzle of rows col + 32 d does not depend on d,
+      // so the address is a per-lane base plus a constant
+      const char* p = vt_lane + voff[tt * 2 + (step >> 3)] + (step & 7) * (32 * kPage * 2);
+      dst[0] = *reinterpret_cast<const half8_t*>(p);
+      dst[1] = *reinterpret_cast<const half8_t*>(p + kHeadDim * kPage * 2);
+    };
+    half8_t vbuf[2][2];
+    vread(0, vbuf[0]);
+#pragma unroll
+    for (int step = 0; step < 16; ++step) {
+      const int s2 = step >> 3, d = step & 7;
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + 1 < 16) vread(step + 1, vbuf[(step + 1) & 1]);
+      const half8_t* vb = vbuf[step & 1];
+      acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[0], pb[s2], acc[0][d], 0, 0, 0);
+      acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[0], pl[s2], acc[0][d], 0, 0, 0);
+      acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[1], pb[s2], acc[0][d], 0, 0, 0);
+      piece(step);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Softmax, first part: causal mask where the tile needs it, the row max, and
+  // the lazy raise of the running max.  The max moves (and the accumulator and
+  // any P operands not yet multiplied are rescaled) only when a score exceeds it
+  // by more than kSlack; the new max is rounded up to an integer, so the rescale
+  // factor is an exact power of two.  The exact maximum is tracked and restored
+  // at the end.
+  auto softmax_max = [&](float16_t& st, int lp, int tt, half8_t* pb_prev, half8_t* pl_prev) {
+    float mx = -INFINITY;
+    const bool need_mask = !cur_valid || lp * kPage + tt * 32 + 31 > qpos_first;
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+        const bool ok = cur_valid && qvalid[0] && tok <= qpos[0];
+        st[i] = ok ? st[i] : -INFINITY;
+        mx = fmaxf(mx, st[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.qk_scale;  // log2 units
+    s_max[0] = fmaxf(s_max[0], mx);
+    const bool raise = mx > m_run[0] + kSlack;
+    if (__ballot(raise)) {
+      const float mn = raise ? ceilf(mx) : m_run[0];
+      // 2^(m_run - mn), exact; 0 while nothing has been accumulated
+      const float alpha = m_run[0] == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_run[0] - mn));
+      m_run[0] = mn;
+      l_lane[0] *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[0][d] *= alpha;
+      if (pb_prev) {  // the other tile's P operands, computed with the old max
+        const _Float16 ah = static_cast<_Float16>(alpha);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          pb_prev[s2] *= ah;
+          pl_prev[s2] *= ah;
+        }
+      }
+    }
+  };
+
+  // Softmax, second part, in half-pieces of one score pair (2j, 2j + 1): the
+  // even half exponentiates, the odd half splits.  B operands per k-step: P *
+  // 2^11 as hi and lo (rounded toward zero).  P stays below 2^kSlack, so P *
+  // 2^11 fits fp16; the power-of-two offset keeps all but negligible weights
+  // out of the subnormal range.  The accumulator carries P * 2^11 throughout
+  // and the epilogue divides it out.
+  auto p_half = [&](const float16_t& st, float off, int h, float* e, float& psum, half8_t* pb, half8_t* pl) {
+    const int j = h >> 1;
+    if ((h & 1) == 0) {
+      e[0] = __builtin_amdgcn_exp2f(fmaf(st[2 * j], a.qk_scale, off));
+      e[1] = __builtin_amdgcn_exp2f(fmaf(st[2 * j + 1], a.qk_scale, off));
+    } else {
+      psum += e[0] + e[1];
+      const auto hh = __builtin_amdgcn_cvt_pkrtz(e[0], e[1]);
+      const auto ll = __builtin_amdgcn_cvt_pkrtz(e[0] - static_cast<float>(hh[0]), e[1] - static_cast<float>(hh[1]));
+      pb[j / 4][2 * (j % 4)] = static_cast<_Float16>(hh[0]);
+      pb[j / 4][2 * (j % 4) + 1] = static_cast<_Float16>(hh[1]);
+      pl[j / 4][2 * (j % 4)] = static_cast<_Float16>(ll[0]);
+      pl[j / 4][2 * (j % 4) + 1] = static_cast<_Float16>(ll[1]);
+    }
+  };
+  auto p_offset = [&]() { return 11.0f - (m_run[0] == -INFINITY ? 0.0f : m_run[0]); };
 
   for (int lp = pbeg; lp < pend; ++lp) {
     // read before this iteration's cell loads, so that waiting for it next
     // iteration does not wait for them (a clamped index keeps the read in range)
     const int32_t pid_after = pt[min(lp + 3, pend - 1)];
     if (lp + 2 < pend) {
-      ahead_valid = static_cast<uint32_t>(pid_next) < static_cast<uint32_t>(a.num_pages);
-      load_page(a, static_cast<int64_t>(ahead_valid ? pid_next : 0) * a.Hkv + g, tid, ahead);
+      kahead_valid = static_cast<uint32_t>(pid_next) < static_cast<uint32_t>(a.num_pages);
+      kahead_ph = static_cast<int64_t>(kahead_valid ? pid_next : 0) * a.Hkv + g;
+      load_k(a, kahead_ph, tid, kahead);
     }
+    if (lp + 1 < pend) load_v(a, kraw_ph, tid, vnext);
     pid_next = pid_after;
     __syncthreads();  // K of this page is in LDS; every wave is done with the previous V
-
-    // ---- S^T = K Q^T for both 32-token tiles, V of this page unpacked meanwhile ----
-    // K_lo (held times 2^10) goes first, the accumulator is scaled by 2^-10, then K_hi.
-    float16_t st[2][kCT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int c = 0; c < kCT; ++c) st[tt][c] = float16_t{};
-    // 32 steps (K_lo k-steps 0..15, then K_hi), the two tiles' MFMAs alternating
-    // so consecutive MFMAs never depend on each other; K operands are read from
-    // LDS a step ahead of their MFMAs
-    half8_t kbuf[2][2];
-    auto kread = [&](int step, half8_t* dst) {
-      const int part = step < 16 ? 1 : 0, ks = step & 15;
-      dst[0] = *reinterpret_cast<const half8_t*>(&sm.k[part][col][16 * ks + 8 * half]);
-      dst[1] = *reinterpret_cast<const half8_t*>(&sm.k[part][32 + col][16 * ks + 8 * half]);
-    };
-    kread(0, kbuf[0]);
-#pragma unroll
-    for (int step = 0; step < 32; ++step) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (step + 1 < 32) kread(step + 1, kbuf[(step + 1) & 1]);
-      if ((step & 7) == 0) unpack_v(sm, cur, tid, step / 8, lp & 1);  // one V channel per 16 MFMAs
-      if (step == 16) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int c = 0; c < kCT; ++c) st[tt][c] *= 1.0f / 1024.0f;
-      }
-#pragma unroll
-      for (int c = 0; c < kCT; ++c) {
-        st[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kbuf[step & 1][0], qf[c][step & 15], st[0][c], 0, 0, 0);
-        st[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kbuf[step & 1][1], qf[c][step & 15], st[1][c], 0, 0, 0);
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();  // V of this page is in LDS; every wave is done with this K
 
-    // ---- softmax and O^T += V^T P^T per tile, K of the next page unpacked meanwhile ----
-    const bool more = lp + 1 < pend;
-    const bool need_mask = !cur_valid || lp * kPage + kPage - 1 > qpos_first;
-    // V operands of PV step (tile tt, step = 4 s2 + dp): hi and lo of channel tiles 2 dp, 2 dp + 1
-    auto vread = [&](int tt, int step, half8_t* dst) {
-      const int s2 = step >> 2, dp = step & 3;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = (2 * dp + e) * 32 + col;
-        const int ch = 8 * vt_chunk(row, (tt * 2 + s2) * 2 + half);
-        dst[e] = *reinterpret_cast<const half8_t*>(&sm.vt[0][row][ch]);
-        dst[2 + e] = *reinterpret_cast<const half8_t*>(&sm.vt[1][row][ch]);
+    // ---- tile 0: S^T, V channels 0-2 of this page unpacked meanwhile ----
+    VScales vs;
+    read_vscales(sm, tid, lp & 1, vs);
+    uint32_t hv[4], lv[4];
+    float16_t st0{};
+    s_phase(0, st0, [&](int step) {
+      if (step < 24) v_piece(sm, vcur, vs, tid, step >> 3, step & 7, hv, lv);
+    });
+    softmax_max(st0, lp, 0, nullptr, nullptr);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- tile 1: S^T, the last V channel and tile 0's P meanwhile ----
+    half8_t pb0[2], pl0[2], pb1[2], pl1[2];
+    float e[2], psum = 0.0f;
+    const float off0 = p_offset();
+    float16_t st1{};
+    s_phase(1, st1, [&](int step) {
+      if (step < 8)
+        v_piece(sm, vcur, vs, tid, 3, step, hv, lv);
+      else if (step < 24)
+        p_half(st0, off0, step - 8, e, psum, pb0, pl0);
+    });
+    l_lane[0] += psum * (1.0f / 2048.0f);
+    // keeps tile 0's P inside that phase (it would otherwise sink to its first use)
+    asm volatile("" ::"v"(pb0[0]), "v"(pb0[1]), "v"(pl0[0]), "v"(pl0[1]));
+    softmax_max(st1, lp, 1, pb0, pl0);
+    __syncthreads();  // V of this page is in LDS; every wave is done with this K
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- PV of tile 0, tile 1's P and K channels of the next page meanwhile ----
+    const float off1 = p_offset();
+    psum = 0.0f;
+    pv_phase(0, pb0, pl0, [&](int step) {
+      if (step < 8) {
+        p_half(st1, off1, 2 * step, e, psum, pb1, pl1);
+        p_half(st1, off1, 2 * step + 1, e, psum, pb1, pl1);
+      } else if (step < 13) {
+        unpack_k(sm, kraw, tid, (step - 8) >> 2, (step - 8) & 3);
       }
-    };
-    half8_t vbuf[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      vread(tt, 0, vbuf[0]);  // in flight during the softmax
-      // B operands per [column tile][k-step of this token tile]: P * 2^11 as hi and lo
-      // (for V hi), and P * 2 (for V lo, which LDS holds times 2^10).  P stays below
-      // 2^kSlack, so P * 2^11 fits fp16; the power-of-two offsets keep the operands of
-      // all but negligible weights out of the subnormal range.  The accumulator carries
-      // P * 2^11 throughout and the epilogue divides it out.
-      half8_t pb[kCT][2], pl[kCT][2], pv5[kCT][2];
-#pragma unroll
-      for (int c = 0; c < kCT; ++c) {
-        // raw scores of this lane's query row; the scale sm_scale * log2(e) > 0 is
-        // applied inside the exponent, the causal mask where the page needs it
-        float mx = -INFINITY;
-        if (need_mask) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-            const bool ok = cur_valid && qvalid[c] && tok <= qpos[c];
-            st[tt][c][i] = ok ? st[tt][c][i] : -INFINITY;
-            mx = fmaxf(mx, st[tt][c][i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[tt][c][i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.qk_scale;  // log2 units
-        // the row's running max is raised only when a score exceeds it by more than
-        // kSlack, so the accumulator is rescaled on few pages; the exact maximum is
-        // tracked and restored at the end
-        s_max[c] = fmaxf(s_max[c], mx);
-        const bool raise = mx > m_run[c] + kSlack;
-        if (__ballot(raise)) {
-          const float mn = raise ? mx : m_run[c];
-          const float alpha = m_run[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[c] - mn);
-          m_run[c] = mn;
-          l_lane[c] *= alpha;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) acc[c][d] *= alpha;
-        }
-        // P * 2^11 = exp2(s * scale - m + 11)
-        const float off = 11.0f - (m_run[c] == -INFINITY ? 0.0f : m_run[c]);
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float s0 = __builtin_amdgcn_exp2f(fmaf(st[tt][c][i], a.qk_scale, off));
-          const float s1 = __builtin_amdgcn_exp2f(fmaf(st[tt][c][i + 1], a.qk_scale, off));
-          psum += s0 + s1;
-          const auto h = __builtin_amdgcn_cvt_pkrtz(s0, s1);  // hi, rounded toward zero
-          const auto l = __builtin_amdgcn_cvt_pkrtz(s0 - static_cast<float>(h[0]), s1 - static_cast<float>(h[1]));
-          // P * 2 for V lo from the hi part alone: the dropped P lo x V lo is ~2^-23 relative
-          const half2v_t v1 = __builtin_bit_cast(half2v_t, h) *
-                              half2v_t{static_cast<_Float16>(1.0f / 1024.0f), static_cast<_Float16>(1.0f / 1024.0f)};
-          pb[c][i / 8][i % 8] = static_cast<_Float16>(h[0]);
-          pb[c][i / 8][i % 8 + 1] = static_cast<_Float16>(h[1]);
-          pl[c][i / 8][i % 8] = static_cast<_Float16>(l[0]);
-          pl[c][i / 8][i % 8 + 1] = static_cast<_Float16>(l[1]);
-          pv5[c][i / 8][i % 8] = v1[0];
-          pv5[c][i / 8][i % 8 + 1] = v1[1];
-        }
-        psum *= 1.0f / 2048.0f;
-        l_lane[c] += psum;
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        // k-step covers tokens 16 (2 tt + s2) + {0..3, 8..11} (+4 for the upper half lanes)
-#pragma unroll
-        for (int dp = 0; dp < 4; ++dp) {  // channel tiles d = 2 dp, 2 dp + 1, their MFMAs alternating
-          const int step = s2 * 4 + dp;
-          __builtin_amdgcn_sched_barrier(0);
-          if (step + 1 < 8) vread(tt, step + 1, vbuf[(step + 1) & 1]);  // next step's V operands
-          if ((dp & 1) == 0 && more) {  // K unpack chunk of the next page overlapping these MFMAs
-            const int x = tt * 4 + s2 * 2 + dp / 2;
-            unpack_k(sm, raw, tid, x >> 2, x & 3);
-            if (x == 7) store_vscales(sm, raw, tid, (lp + 1) & 1);
-          }
-          const half8_t* vb = vbuf[step & 1];
-#pragma unroll
-          for (int c = 0; c < kCT; ++c) {
-            // V hi x (P hi + P lo), then (V lo * 2^10) x (P * 2); P lo x V lo is below fp32 rounding
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[e], pb[c][s2], acc[c][2 * dp + e], 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[e], pl[c][s2], acc[c][2 * dp + e], 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              acc[c][2 * dp + e] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[2 + e], pv5[c][s2], acc[c][2 * dp + e], 0, 0, 0);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    cur = raw;
-    cur_valid = raw_valid;
-    raw = ahead;
-    raw_valid = ahead_valid;
+    });
+    l_lane[0] += psum * (1.0f / 2048.0f);
+    asm volatile("" ::"v"(pb1[0]), "v"(pb1[1]), "v"(pl1[0]), "v"(pl1[1]));
+
+    // ---- PV of tile 1, the rest of the next page's K meanwhile ----
+    pv_phase(1, pb1, pl1, [&](int step) {
+      if (step < 3)
+        unpack_k(sm, kraw, tid, (step + 5) >> 2, (step + 5) & 3);
+      else if (step == 3)
+        store_vscales(sm, kraw, tid, (lp + 1) & 1);
+    });
+
+    vcur = vnext;
+    cur_valid = kraw_valid;
+    kraw = kahead;
+    kraw_ph = kahead_ph;
+    kraw_valid = kahead_valid;
   }
+
 
   // ---- epilogue: this lane's two query rows ----
   const int R = a.T * a.Hq;
