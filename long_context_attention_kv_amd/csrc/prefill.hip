@@ -93,8 +93,10 @@ __device__ __forceinline__ void split_scales(uint32_t bits2, half2v_t& hi, half2
 }
 
 // Two nibbles at bit offsets sh and 16 + sh of w as the fp16 pair (n0 - 8, n1 - 8).
-__device__ __forceinline__ half2v_t nibble_pair(uint32_t w, int sh) {
-  const uint32_t b = ((w >> sh) & 0x000F000Fu) | 0x64006400u;  // 1024 + n in each half
+// magic holds 0x64006400 in a VGPR, so the mask and the OR are one v_and_or_b32
+// (an instruction takes one literal constant only).
+__device__ __forceinline__ half2v_t nibble_pair(uint32_t w, int sh, uint32_t magic) {
+  const uint32_t b = ((w >> sh) & 0x000F000Fu) | magic;  // 1024 + n in each half
   return __builtin_bit_cast(half2v_t, b) + half2v_t{static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
 }
 
@@ -149,7 +151,7 @@ __device__ __forceinline__ void store_vscales(PrefillSmem& sm, const KRaw& r, in
 
 // Dword j of K unit u -> 8 channels of one LDS row [token][channel in unpack
 // order], hi and lo.
-__device__ __forceinline__ void unpack_k(PrefillSmem& sm, const KRaw& r, int tid, int u, int j) {
+__device__ __forceinline__ void unpack_k(PrefillSmem& sm, const KRaw& r, int tid, int u, int j, uint32_t magic) {
   const int c = 2 * (tid >> 6) + u, t = tid & 63;
   half2v_t kh, kl;
   split_scales(r.ks, kh, kl);
@@ -157,10 +159,10 @@ __device__ __forceinline__ void unpack_k(PrefillSmem& sm, const KRaw& r, int tid
   const uint32_t w = word(r.k[u], j);
   uint4 hi, lo;
   half2v_t n;
-  n = nibble_pair(w, 0);  hi.x = as_u32(n * s2h); lo.x = as_u32(n * s2l);
-  n = nibble_pair(w, 4);  hi.y = as_u32(n * s2h); lo.y = as_u32(n * s2l);
-  n = nibble_pair(w, 8);  hi.z = as_u32(n * s2h); lo.z = as_u32(n * s2l);
-  n = nibble_pair(w, 12); hi.w = as_u32(n * s2h); lo.w = as_u32(n * s2l);
+  n = nibble_pair(w, 0, magic);  hi.x = as_u32(n * s2h); lo.x = as_u32(n * s2l);
+  n = nibble_pair(w, 4, magic);  hi.y = as_u32(n * s2h); lo.y = as_u32(n * s2l);
+  n = nibble_pair(w, 8, magic);  hi.z = as_u32(n * s2h); lo.z = as_u32(n * s2l);
+  n = nibble_pair(w, 12, magic); hi.w = as_u32(n * s2h); lo.w = as_u32(n * s2l);
   *reinterpret_cast<uint4*>(&sm.k[0][t][32 * c + 8 * j]) = hi;
   *reinterpret_cast<uint4*>(&sm.k[1][t][32 * c + 8 * j]) = lo;
 }
@@ -188,10 +190,10 @@ __device__ __forceinline__ void read_vscales(const PrefillSmem& sm, int tid, int
 }
 
 __device__ __forceinline__ void v_piece(PrefillSmem& sm, const VRaw& r, const VScales& s, int tid, int i, int p,
-                                        uint32_t* hv, uint32_t* lv) {
+                                        uint32_t* hv, uint32_t* lv, uint32_t magic) {
   const int g = tid >> 6, j = tid & 63;
   const int u = (p >> 1) & 1, k = (p & 1) + 2 * (p >> 2), slot = p & 3;
-  const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i);
+  const half2v_t n = nibble_pair(word(r.v[u], k), 4 * i, magic);
   hv[slot] = as_u32(n * s.hi[4 * u + k]);
   lv[slot] = as_u32(n * s.lo[4 * u + k]);
   if (slot == 3) {
@@ -275,6 +277,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   // page's PV work); requested now: vnext = V of page lp + 1 and kahead = K of
   // page lp + 2.  The page id of page lp + 3 is read one iteration before its
   // cells are.  Cells past the range are unpacked into buffers nobody reads.
+  uint32_t nmagic = 0x64006400u;
+  asm volatile("" : "+v"(nmagic));  // kept in a VGPR (see nibble_pair)
   KRaw kraw{}, kahead{};
   VRaw vcur{}, vnext{};
   bool cur_valid = false, kraw_valid = false, kahead_valid = false;
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       load_k(a, kraw_ph, tid, kraw);
     }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) unpack_k(sm, k0, tid, x >> 2, x & 3);
+    for (int x = 0; x < 8; ++x) unpack_k(sm, k0, tid, x >> 2, x & 3, nmagic);
     store_vscales(sm, k0, tid, pbeg & 1);
   }
 
@@ -412,7 +416,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     } else {
       psum += e[0] + e[1];
       const auto hh = __builtin_amdgcn_cvt_pkrtz(e[0], e[1]);
-      const auto ll = __builtin_amdgcn_cvt_pkrtz(e[0] - static_cast<float>(hh[0]), e[1] - static_cast<float>(hh[1]));
+      // e - hi as one mixed-precision FMA each (fp16 operand from the packed pair)
+      const uint32_t hb = __builtin_bit_cast(uint32_t, hh);
+      float d0, d1;
+      asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d0) : "v"(hb), "v"(e[0]));
+      asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d1) : "v"(hb), "v"(e[1]));
+      const auto ll = __builtin_amdgcn_cvt_pkrtz(d0, d1);
       pb[j / 4][2 * (j % 4)] = static_cast<_Float16>(hh[0]);
       pb[j / 4][2 * (j % 4) + 1] = static_cast<_Float16>(hh[1]);
       pl[j / 4][2 * (j % 4)] = static_cast<_Float16>(ll[0]);
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     uint32_t hv[4], lv[4];
     float16_t st0{};
     s_phase(0, st0, [&](int step) {
-      if (step < 24) v_piece(sm, vcur, vs, tid, step >> 3, step & 7, hv, lv);
+      if (step < 24) v_piece(sm, vcur, vs, tid, step >> 3, step & 7, hv, lv, nmagic);
     });
     softmax_max(st0, lp, 0, nullptr, nullptr);
     __builtin_amdgcn_sched_barrier(0);
@@ -453,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     float16_t st1{};
     s_phase(1, st1, [&](int step) {
       if (step < 8)
-        v_piece(sm, vcur, vs, tid, 3, step, hv, lv);
+        v_piece(sm, vcur, vs, tid, 3, step, hv, lv, nmagic);
       else if (step < 24)
         p_half(st0, off0, step - 8, e, psum, pb0, pl0);
     });
@@ -472,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
         p_half(st1, off1, 2 * step, e, psum, pb1, pl1);
         p_half(st1, off1, 2 * step + 1, e, psum, pb1, pl1);
       } else if (step < 13) {
-        unpack_k(sm, kraw, tid, (step - 8) >> 2, (step - 8) & 3);
+        unpack_k(sm, kraw, tid, (step - 8) >> 2, (step - 8) & 3, nmagic);
       }
     });
     l_lane[0] += psum * (1.0f / 2048.0f);
@@ -481,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     // ---- PV of tile 1, the rest of the next page's K meanwhile ----
     pv_phase(1, pb1, pl1, [&](int step) {
       if (step < 3)
-        unpack_k(sm, kraw, tid, (step + 5) >> 2, (step + 5) & 3);
+        unpack_k(sm, kraw, tid, (step + 5) >> 2, (step + 5) & 3, nmagic);
       else if (step == 3)
         store_vscales(sm, kraw, tid, (lp + 1) & 1);
     });
