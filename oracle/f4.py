@@ -2,9 +2,11 @@
 
 The format (mistral.rs PR #2375, "Changes by area" item 2): symmetric 4-bit
 values stored as ``(nibble - 8) * scale``, 32 values per 16-byte row, one
-scale per 32-value block (the V scale granularity follows the workload
-description: one fp16 scale per 32 contiguous values).  "Known limitations"
-on the same page states the per-value error bound max_abs / 16.
+scale per 32-value K cell.  For V the same item gives one scale per token per
+V head; the default layout here gives V one fp16 scale per 32 contiguous
+values like K (the workload description's granularity), and the per-token
+variant (``v_per_token``) follows the page.  "Known limitations" on the same
+page states the per-value error bound max_abs / 16.
 
 Readings taken where the page is silent:
 * scale s = fp16_round_nearest_even(absmax / 8), saturated to 65504; half a
@@ -27,7 +29,7 @@ Physical layout (one layer; P pages of 64 tokens, H kv heads, D = head_dim):
                                         4j..4j+3; byte 4k + 2r + h holds dims
                                         4j+2h (low) and 4j+2h+1 (high) of token
                                         8c + 2k + r
-  v_scale fp16   [P][H][64][D/32]
+  v_scale fp16   [P][H][64][D/32]        (per-token variant: [P][H][64])
 """
 from __future__ import annotations
 
@@ -44,10 +46,11 @@ def fp16_round(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float16)
 
 
-def quantize_blocks(x: np.ndarray):
-    """Quantise x[..., 32] (fp32 values).  Returns (codes int8 in [-8, 7], scale fp16)."""
+def quantize_group(x: np.ndarray):
+    """Quantise x[..., n] (fp32 values) with one scale per group along the last
+    axis (n = 32 for a cell, head_dim for a per-token V row).  Returns (codes
+    int8 in [-8, 7], scale fp16)."""
     x = np.asarray(x)
-    assert x.shape[-1] == BLOCK
     xd = x.astype(np.float32).astype(np.float64)
     assert np.isfinite(xd).all(), "non-finite input to the F4 quantiser"
     a = np.abs(xd).max(axis=-1)
@@ -59,7 +62,14 @@ def quantize_blocks(x: np.ndarray):
     return q, s16
 
 
+def quantize_blocks(x: np.ndarray):
+    """Quantise x[..., 32] (fp32 values), one scale per 32-value cell."""
+    assert np.shape(x)[-1] == BLOCK
+    return quantize_group(x)
+
+
 def dequantize_blocks(q: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """(code) * scale with one scale per group along the last axis."""
     return q.astype(np.float64) * s16.astype(np.float64)[..., None]
 
 
@@ -81,17 +91,20 @@ def unpack_block_bytes(b: np.ndarray) -> np.ndarray:
 class Cache:
     """The four arrays of one layer's paged F4 cache, in the physical layout above."""
 
-    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int):
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, v_per_token: bool = False):
         assert head_dim % BLOCK == 0
         P, H, D = num_pages, num_kv_heads, head_dim
         self.P, self.H, self.D = P, H, D
+        self.v_per_token = bool(v_per_token)
         self.k_nib = np.zeros((P, H, D // BLOCK, PAGE, 16), dtype=np.uint8)
         self.v_nib = np.zeros((P, H, PAGE // 8, D // 4, 16), dtype=np.uint8)
         self.k_scale = np.zeros((P, H, PAGE, D // BLOCK), dtype=np.float16)
-        self.v_scale = np.zeros((P, H, PAGE, D // BLOCK), dtype=np.float16)
+        vs_shape = (P, H, PAGE) if self.v_per_token else (P, H, PAGE, D // BLOCK)
+        self.v_scale = np.zeros(vs_shape, dtype=np.float16)
 
     def put_codes(self, pages, offs, kq, ks, vq, vs):
-        """Store codes kq, vq [N, H, D] and scales ks, vs [N, H, D/32] at (page, offset) pairs."""
+        """Store codes kq, vq [N, H, D] and scales ks [N, H, D/32], vs [N, H, D/32]
+        (per-token variant: [N, H]) at (page, offset) pairs."""
         pages = np.asarray(pages, dtype=np.int64)
         offs = np.asarray(offs, dtype=np.int64)
         N, H, D = kq.shape
@@ -109,7 +122,7 @@ class Cache:
         for h in range(2):
             self.v_nib[pages[:, None, None], np.arange(H)[None, :, None], c[:, None, None],
                        np.arange(D // 4)[None, None, :], (base + h)[:, None, None]] = vb[..., h]
-        self.v_scale[pages, :, offs, :] = vs
+        self.v_scale[pages, :, offs] = vs
 
     def write(self, k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray):
         """Quantise k, v [T, H, D] (fp32) into the slots; slot -1 skips the token."""
@@ -124,12 +137,16 @@ class Cache:
             return
         nb = D // BLOCK
         kq, ks = quantize_blocks(k[live].reshape(len(live), H, nb, BLOCK))
-        vq, vs = quantize_blocks(v[live].reshape(len(live), H, nb, BLOCK))
+        if self.v_per_token:
+            vq, vs = quantize_group(v[live])  # one scale per (token, head) over all D values
+        else:
+            vq, vs = quantize_blocks(v[live].reshape(len(live), H, nb, BLOCK))
         self.put_codes(slots[live] // PAGE, slots[live] % PAGE,
                        kq.reshape(len(live), H, D), ks, vq.reshape(len(live), H, D), vs)
 
     def page_codes(self, page: int, head: int):
-        """Codes [64, D] and fp16 scales [64, D/32] of K and V for one page-head tile."""
+        """Codes [64, D] and fp16 scales [64, D/32] of K and V for one page-head
+        tile (V scales [64] in the per-token variant)."""
         D, nb = self.D, self.D // BLOCK
         kb = self.k_nib[page, head]                                  # [nb, 64, 16]
         kc = unpack_block_bytes(kb).transpose(1, 0, 2).reshape(PAGE, D)
@@ -148,7 +165,10 @@ class Cache:
         kc, ks, vc, vs = self.page_codes(page, head)
         nb = self.D // BLOCK
         kd = dequantize_blocks(kc.reshape(PAGE, nb, BLOCK), ks).reshape(PAGE, self.D)
-        vd = dequantize_blocks(vc.reshape(PAGE, nb, BLOCK), vs).reshape(PAGE, self.D)
+        if self.v_per_token:
+            vd = dequantize_blocks(vc, vs)
+        else:
+            vd = dequantize_blocks(vc.reshape(PAGE, nb, BLOCK), vs).reshape(PAGE, self.D)
         return kd, vd
 
     def arrays(self):

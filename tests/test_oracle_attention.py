@@ -197,3 +197,28 @@ def test_prefill_causal_matches_textbook():
     # the last row is a decode at position pos0 + T - 1
     dec, _, _ = att.decode(cache, q[-1][None], pt, [n], 0.2)
     np.testing.assert_allclose(out[-1], dec[0, 0], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("C", [1, 65, 130])
+def test_decode_over_per_token_v_scales_matches_textbook_attention(C):
+    # the same definition over a cache whose V rows carry one scale per token
+    rng = np.random.default_rng(900 + C)
+    Hkv, D, G = 2, 64, 4
+    c = f4.Cache(4, Hkv, D, v_per_token=True)
+    pt = np.full((1, 3), -1, np.int32)
+    npg = (C + PAGE - 1) // PAGE
+    pt[0, :npg] = rng.permutation(4)[:npg]
+    k = rng.standard_normal((C, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((C, Hkv, D)).astype(np.float32)
+    v[:, :, 5] *= 8
+    t = np.arange(C)
+    c.write(k, v, pt[0, t // PAGE].astype(np.int64) * PAGE + t % PAGE)
+    q = rng.standard_normal((1, G * Hkv, D))
+    out, m, l = att.decode(c, q, pt, [C], 0.125)
+    Kd = att.dequantize_rows(k).transpose(1, 0, 2)
+    vq, vs = f4.quantize_group(v)
+    Vd = f4.dequantize_blocks(vq, vs).transpose(1, 0, 2)
+    ref = _sdpa(q[0][:, None, :], np.repeat(Kd, G, axis=0), np.repeat(Vd, G, axis=0), 0.125)[:, 0]
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-12)
+    if C == 1:  # one token: the output is that token's dequantised V row
+        np.testing.assert_array_equal(out[0, 0], np.repeat(Vd[:, 0], G, axis=0))

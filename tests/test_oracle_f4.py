@@ -203,3 +203,82 @@ def test_cache_round_trip_and_skip():
     for sl in np.nonzero(~written)[0][:20]:
         a, b = c.page_values(sl // 64, 0)
         assert np.all(a[sl % 64] == 0) and np.all(b[sl % 64] == 0)
+
+
+# ---- per-token V scales (one scale per token per V head, mistral.rs PR #2375,
+# "Changes by area" item 2) ---------------------------------------------------
+
+def test_per_token_rows_follow_the_same_rule():
+    # a whole 256-value row quantised as one group: scale from the row's absmax,
+    # on-grid rows come back unchanged, zero rows give s = 0 / nibble 8, and the
+    # error bound is half a step of the row's scale
+    rng = np.random.default_rng(11)
+    s16 = rng.uniform(1e-3, 100, size=64).astype(np.float16)
+    q = rng.integers(-8, 8, size=(64, 256)).astype(np.int8)
+    q[:, 17] = -8
+    x = (q.astype(np.float64) * s16.astype(np.float64)[:, None]).astype(np.float32)
+    q2, s2 = f4.quantize_group(x)
+    assert np.array_equal(s2, s16) and np.array_equal(q2, q)
+    z, sz = f4.quantize_group(np.zeros((3, 256), dtype=np.float32))
+    assert np.all(z == 0) and np.all(sz == 0)
+    y = (rng.standard_normal((500, 256)) * rng.uniform(1e-4, 1e3, (500, 1))).astype(np.float32)
+    y[:, 9] *= 8  # an outlier channel sets the row's scale
+    qy, sy = f4.quantize_group(y)
+    yd = y.astype(np.float64)
+    sd = sy.astype(np.float64)[:, None]
+    assert np.array_equal(sy, f4.fp16_round(np.abs(yd).max(axis=1) * 0.125))
+    err = np.abs(yd - f4.dequantize_blocks(qy, sy))
+    clamped = yd > 7.5 * sd
+    assert np.all(err[~clamped] <= np.broadcast_to(sd, err.shape)[~clamped] / 2)
+    assert np.all(qy[clamped] == 7)
+    # power-of-two scaling moves only the scale (scales kept inside fp16's normal range)
+    w = rng.standard_normal((200, 256)).astype(np.float32)
+    qw, sw = f4.quantize_group(w)
+    for k in (-3, 5):
+        qk, sk = f4.quantize_group((w * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(qk, qw) and np.array_equal(sk.astype(np.float64), sw.astype(np.float64) * 2.0 ** k)
+
+
+def test_per_token_row_differs_from_cells_when_blocks_differ():
+    # a row whose 32-value cells have different absmax: per-cell scales differ,
+    # the per-token row has one scale (its absmax / 8) for all cells
+    x = np.zeros((1, 256), dtype=np.float32)
+    x[0, ::32] = np.arange(1, 9, dtype=np.float32)  # cell c has absmax c + 1
+    qc, sc = f4.quantize_blocks(x.reshape(1, 8, 32))
+    qr, sr = f4.quantize_group(x)
+    assert np.array_equal(sc[0].astype(np.float64), np.arange(1, 9) / 8.0)
+    assert float(sr[0]) == 1.0
+    assert np.array_equal(qr[0, ::32], np.clip(np.arange(1, 9), -8, 7))
+    assert np.array_equal(qc.reshape(1, 256)[0, ::32], np.full(8, 7))
+
+
+def test_per_token_cache_layout_and_round_trip():
+    rng = np.random.default_rng(12)
+    P, H, D, T = 4, 2, 256, 50
+    c = f4.Cache(P, H, D, v_per_token=True)
+    assert c.v_scale.shape == (P, H, 64)
+    # per token and head: 128 bytes of V nibbles and one 2-byte scale
+    assert c.v_nib[0, 0].size // 64 + c.v_scale[0, 0].nbytes // 64 == 130
+    k = rng.standard_normal((T, H, D)).astype(np.float32)
+    v = rng.standard_normal((T, H, D)).astype(np.float32)
+    v[:, :, 40] *= 8
+    slots = rng.permutation(P * 64)[:T]
+    slots[7] = -1
+    c.write(k, v, slots)
+    kd = f4.dequantize_blocks(*f4.quantize_blocks(k.reshape(T, H, D // 32, 32))).reshape(T, H, D)
+    vq, vs = f4.quantize_group(v)
+    vd = f4.dequantize_blocks(vq, vs)
+    for t in range(T):
+        if slots[t] < 0:
+            continue
+        for h in range(H):
+            a, b = c.page_values(slots[t] // 64, h)
+            assert np.array_equal(a[slots[t] % 64], kd[t, h])
+            assert np.array_equal(b[slots[t] % 64], vd[t, h])
+            assert c.v_scale[slots[t] // 64, h, slots[t] % 64] == vs[t, h]
+    # the nibble bytes are laid out exactly as in the per-cell layout
+    cb = f4.Cache(P, H, D)
+    cb.put_codes(slots[slots >= 0] // 64, slots[slots >= 0] % 64, np.zeros_like(vq[slots >= 0]),
+                 np.zeros((int((slots >= 0).sum()), H, D // 32), np.float16), vq[slots >= 0],
+                 np.zeros((int((slots >= 0).sum()), H, D // 32), np.float16))
+    assert np.array_equal(cb.v_nib, c.v_nib)
