@@ -37,6 +37,7 @@ PAGE = 64
 HQ, HKV, D = 16, 4, 256
 SM = 1.0 / 16.0
 BYTES_PER_TOKEN_HEAD = 2 * (D // 2 + 2 * (D // 32))  # K and V: 128 B nibbles + 8 fp16 scales each
+BYTES_PER_TOKEN_HEAD_VTOK = (D // 2 + 2 * (D // 32)) + (D // 2 + 2)  # V with one fp16 scale per token
 
 
 def log(*a):
@@ -50,7 +51,7 @@ def yarn_params(factor):
 class DecodeLayer:
     """One layer's cache for B lanes of given lengths, filled from seeded N(0,1) draws."""
 
-    def __init__(self, lengths, factor, gen, outliers, chunk=65536, dev="cuda"):
+    def __init__(self, lengths, factor, gen, outliers, chunk=65536, dev="cuda", v_per_token=False):
         self.lengths = [int(x) for x in lengths]
         pages = [(n + PAGE - 1) // PAGE for n in self.lengths]
         self.num_pages = sum(pages)
@@ -59,7 +60,7 @@ class DecodeLayer:
         self.pt_np = synth.page_table_for(self.lengths, perm, self.max_pages)
         self.pt = torch.from_numpy(self.pt_np).to(dev)
         self.ctx = torch.tensor(self.lengths, dtype=torch.int32, device=dev)
-        self.cache = f4.F4Cache(self.num_pages, HKV, D, device=dev)
+        self.cache = f4.F4Cache(self.num_pages, HKV, D, device=dev, v_scale_per_token=v_per_token)
         yp = yarn_params(factor)
         cols = None
         if outliers:
@@ -88,8 +89,8 @@ def gb(x):
     return x / 1e9
 
 
-def decode_algorithmic_bytes(lengths, windows=1):
-    kv = sum(lengths) * HKV * BYTES_PER_TOKEN_HEAD
+def decode_algorithmic_bytes(lengths, windows=1, per_token_head=None):
+    kv = sum(lengths) * HKV * (BYTES_PER_TOKEN_HEAD if per_token_head is None else per_token_head)
     q = len(lengths) * HQ * D * 2
     pt = sum((n + PAGE - 1) // PAGE for n in lengths) * 4
     out = windows * len(lengths) * HQ * (D + 2) * 4
@@ -263,6 +264,36 @@ def bench_1m(iters=10):
     return {"workload": "1 x 1,048,576 tokens, 16 windows of 65,536 + lse_merge", "ms": ms,
             "kv_tokens_per_s": ctx / (ms / 1e3), "gbs": by / (ms / 1e3) / 1e9,
             "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_vtok(iters=20):
+    """The config-1 layer shape over a cache with one V scale per token and head."""
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 5)
+    lengths = [262144] * 3
+    L = DecodeLayer(lengths, 4.0, gen, outliers=True, v_per_token=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 15)
+    q = torch.randn((3, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(max(16, f4.decode_workspace_size(3, HQ, HKV, D, 262144)), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, 3, HQ, D), device=dev)
+    for _ in range(3):
+        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=iters) as t:
+        e0.record()
+        for _ in range(iters):
+            f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    by = decode_algorithmic_bytes(lengths, per_token_head=BYTES_PER_TOKEN_HEAD_VTOK)
+    del L
+    return {"workload": "decode, 3 x 262,144 tokens, one layer, V scale per token and head (1,096 B per token)",
+            "kernel_ms": t.avg_ms, "kernel_gbs": by / (t.avg_ms / 1e3) / 1e9,
+            "kernel_hbm_frac": by / (t.avg_ms / 1e3) / 1e9 / HBM_PEAK_GBS, "call_ms": ms,
+            "kv_tokens_per_s": sum(lengths) / (ms / 1e3), "call_gbs": by / (ms / 1e3) / 1e9}
 
 
 def bench_ragged(iters=20):
@@ -450,6 +481,9 @@ def main():
         torch.cuda.empty_cache()
         extra["prefill"] = bench_prefill()
         log("prefill:", extra["prefill"])
+        torch.cuda.empty_cache()
+        extra["decode_v_per_token"] = bench_vtok()
+        log("v per token:", extra["decode_v_per_token"])
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(args.cpu_tokens)

@@ -43,7 +43,12 @@
  *                                         4j..4j+3; byte 4k+2r+h holds dims
  *                                         4j+2h (low) and 4j+2h+1 (high) of
  *                                         token 8c+2k+r
- *   v_scale fp16    [P][H][64][D/32]
+ *   v_scale fp16    [P][H][64][D/32]      one scale per 32 values, like K; or,
+ *                   [P][H][64]            with v_scale_per_token = 1, one
+ *                                         scale per token and V head (the V
+ *                                         format of [MRS item 2]), taken from
+ *                                         the absmax of the token's whole V
+ *                                         row
  *   Logical value of element e of block c of token t: (nibble - 8) * scale.
  *   Token i of a sequence lives in page page_table[i / 64], slot i % 64.
  */
@@ -58,7 +63,7 @@
 extern "C" {
 #endif
 
-#define F4KV_ABI_VERSION 1
+#define F4KV_ABI_VERSION 2
 
 enum {
   F4KV_OK = 0,
@@ -100,7 +105,9 @@ typedef struct {
  * One layer's paged F4 cache (layout above).  All four pointers are device
  * memory aligned to 16 bytes.  page_size must be 64 [IGN
  * --model-adapt-context-step: pages are multiples of 64 tokens]; head_dim a
- * multiple of 32.
+ * multiple of 32.  v_scale_per_token selects the V scale granularity: 0 = one
+ * fp16 scale per 32 values (as K), 1 = one per token and V head; every entry
+ * point reads and writes the cache in the layout it names.
  */
 typedef struct {
   uint8_t* k_nib;
@@ -111,12 +118,13 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t page_size;
+  int32_t v_scale_per_token;
 } f4kv_cache;
 
-/* Bytes of each of the four cache arrays for the given geometry (host helper,
- * no device work).  Any output pointer may be NULL.  Returns the total, or 0
- * for an invalid geometry. */
-size_t f4kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+/* Bytes of each of the four cache arrays for the given geometry and V scale
+ * granularity (host helper, no device work).  Any output pointer may be NULL.
+ * Returns the total, or 0 for an invalid geometry. */
+size_t f4kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, int32_t v_scale_per_token,
                         size_t* k_nib, size_t* k_scale, size_t* v_nib, size_t* v_scale);
 
 /*

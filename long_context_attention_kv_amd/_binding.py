@@ -33,7 +33,7 @@ class _YarnParamsC(C.Structure):
 class _CacheC(C.Structure):
     _fields_ = [("k_nib", C.c_void_p), ("k_scale", C.c_void_p), ("v_nib", C.c_void_p),
                 ("v_scale", C.c_void_p), ("num_pages", C.c_int32), ("num_kv_heads", C.c_int32),
-                ("head_dim", C.c_int32), ("page_size", C.c_int32)]
+                ("head_dim", C.c_int32), ("page_size", C.c_int32), ("v_scale_per_token", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -41,7 +41,7 @@ _I = C.c_int32
 _SIGS = {
     "f4kv_abi_version": (C.c_int, []),
     "f4kv_last_error": (C.c_char_p, []),
-    "f4kv_cache_bytes": (C.c_size_t, [_I, _I, _I, _P, _P, _P, _P]),
+    "f4kv_cache_bytes": (C.c_size_t, [_I, _I, _I, _I, _P, _P, _P, _P]),
     "yarn_rope_table": (C.c_int, [C.POINTER(_YarnParamsC), _P, _I, _P, _P, _P]),
     "yarn_rope_apply": (C.c_int, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
     "kv_cache_write_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _P]),
@@ -112,11 +112,11 @@ def abi_version() -> int:
     return load_library().f4kv_abi_version()
 
 
-def cache_bytes(num_pages: int, num_kv_heads: int, head_dim: int):
+def cache_bytes(num_pages: int, num_kv_heads: int, head_dim: int, v_scale_per_token: bool = False):
     lib = load_library()
     a, b, c, d = (C.c_size_t() for _ in range(4))
-    total = lib.f4kv_cache_bytes(num_pages, num_kv_heads, head_dim, C.byref(a), C.byref(b), C.byref(c),
-                                 C.byref(d))
+    total = lib.f4kv_cache_bytes(num_pages, num_kv_heads, head_dim, int(bool(v_scale_per_token)), C.byref(a),
+                                 C.byref(b), C.byref(c), C.byref(d))
     return total, (a.value, b.value, c.value, d.value)
 
 
@@ -136,20 +136,25 @@ class YarnParams:
 
 
 class F4Cache:
-    """One layer's paged F4 cache: four device tensors in the library's layout."""
+    """One layer's paged F4 cache: four device tensors in the library's layout
+    (``v_scale_per_token``: one V scale per token and head instead of per 32 values)."""
 
-    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int = 256, device="cuda"):
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int = 256, device="cuda",
+                 v_scale_per_token: bool = False):
         nb = head_dim // 32
         self.num_pages, self.num_kv_heads, self.head_dim = num_pages, num_kv_heads, head_dim
+        self.v_scale_per_token = bool(v_scale_per_token)
         self.k_nib = torch.zeros((num_pages, num_kv_heads, nb, PAGE, 16), dtype=torch.uint8, device=device)
         self.k_scale = torch.zeros((num_pages, num_kv_heads, PAGE, nb), dtype=torch.int16, device=device)
         self.v_nib = torch.zeros((num_pages, num_kv_heads, PAGE // 8, head_dim // 4, 16), dtype=torch.uint8,
                                  device=device)
-        self.v_scale = torch.zeros((num_pages, num_kv_heads, PAGE, nb), dtype=torch.int16, device=device)
+        vs_shape = (num_pages, num_kv_heads, PAGE) if self.v_scale_per_token else (num_pages, num_kv_heads, PAGE, nb)
+        self.v_scale = torch.zeros(vs_shape, dtype=torch.int16, device=device)
 
     def _c(self):
         return _CacheC(self.k_nib.data_ptr(), self.k_scale.data_ptr(), self.v_nib.data_ptr(),
-                       self.v_scale.data_ptr(), self.num_pages, self.num_kv_heads, self.head_dim, PAGE)
+                       self.v_scale.data_ptr(), self.num_pages, self.num_kv_heads, self.head_dim, PAGE,
+                       int(self.v_scale_per_token))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.k_nib, self.k_scale, self.v_nib, self.v_scale))

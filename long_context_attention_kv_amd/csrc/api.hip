@@ -41,6 +41,8 @@ int check_cache(const f4kv_cache* c, const char* fn) {
     return fail(F4KV_ERR_INVALID, "%s: cache arrays must be 16-byte aligned", fn);
   if (c->page_size != f4kv::kPage)
     return fail(F4KV_ERR_INVALID, "%s: page_size must be 64 (got %d)", fn, c->page_size);
+  if (c->v_scale_per_token != 0 && c->v_scale_per_token != 1)
+    return fail(F4KV_ERR_INVALID, "%s: v_scale_per_token must be 0 or 1 (got %d)", fn, c->v_scale_per_token);
   if (c->num_pages <= 0 || c->num_kv_heads <= 0)
     return fail(F4KV_ERR_INVALID, "%s: num_pages and num_kv_heads must be positive", fn);
   if (c->num_pages > INT32_MAX / f4kv::kPage)
@@ -81,17 +83,19 @@ int f4kv_abi_version(void) { return F4KV_ABI_VERSION; }
 
 const char* f4kv_last_error(void) { return g_error.c_str(); }
 
-size_t f4kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, size_t* k_nib,
-                        size_t* k_scale, size_t* v_nib, size_t* v_scale) {
+size_t f4kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t head_dim, int32_t v_scale_per_token,
+                        size_t* k_nib, size_t* k_scale, size_t* v_nib, size_t* v_scale) {
   if (num_pages <= 0 || num_kv_heads <= 0 || head_dim <= 0 || head_dim % 32 != 0) return 0;
+  if (v_scale_per_token != 0 && v_scale_per_token != 1) return 0;
   const size_t cells = static_cast<size_t>(num_pages) * num_kv_heads * f4kv::kPage;
   const size_t nib = cells * head_dim / 2;
   const size_t sc = cells * (head_dim / 32) * 2;
+  const size_t vsc = v_scale_per_token ? cells * 2 : sc;
   if (k_nib) *k_nib = nib;
   if (v_nib) *v_nib = nib;
   if (k_scale) *k_scale = sc;
-  if (v_scale) *v_scale = sc;
-  return 2 * (nib + sc);
+  if (v_scale) *v_scale = vsc;
+  return 2 * nib + sc + vsc;
 }
 
 int yarn_rope_table(const f4kv_yarn_params* params, const int32_t* positions, int32_t n, float* cos_out,

@@ -405,7 +405,10 @@ __device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, 
 
 static_assert((kWRow * 4) % 16 == 0, "weight rows must be 16-byte aligned");
 
-template <int G>
+// VT: V scales are one per token and head (v_scale [P][H][64]) instead of one
+// per 32 values; the weight of a token is then the same for all blocks, so a
+// single row of weights per head goes through LDS.
+template <int G, bool VT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QPrep<G>* __restrict__ qprep) {
   __shared__ DecodeSmem<G> sm;
   const int item = blockIdx.x;
@@ -470,7 +473,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int c = 0; c < 8; ++c) kq[c] = load16(rk, lane16, c * 1024);
     __builtin_amdgcn_s_setprio(0);
     const uint4 ks = load16(tile_rsrc(a.k_scale + ph * (kPage * 8), scale_bytes), lane16);
-    const uint4 vs = load16(tile_rsrc(a.v_scale + ph * (kPage * 8), scale_bytes), lane16);
+    uint4 vs = make_uint4(0, 0, 0, 0);
+    uint32_t vs1 = 0;  // this token's V scale (VT)
+    if (VT)
+      vs1 = __builtin_amdgcn_raw_buffer_load_b16(tile_rsrc(a.v_scale + ph * kPage, pvalid ? kPage * 2 : 0),
+                                                 lane * 2, 0, 0);
+    else
+      vs = load16(tile_rsrc(a.v_scale + ph * (kPage * 8), scale_bytes), lane16);
 
     const int tok = lp * kPage + lane;
     const float tmask = (pvalid && tok >= t0 && tok < t1) ? 0.0f : -INFINITY;
@@ -551,15 +560,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       l_lane[h] += p[h];
     }
 
-    // weights p * s_v per (head, block) to LDS in fp32, transposed to [head][block][token]
+    // weights p * s_v per (head, block) to LDS in fp32, transposed to
+    // [head][block][token] (VT: one block row per head)
+    if (VT) {
+      const float sv = f16_lo(vs1);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t sw = word(vs, c >> 1);
-      const float sv = (c & 1) ? f16_hi(sw) : f16_lo(sw);
+      for (int h = 0; h < G; ++h) sm.u.w[wave][h][0][lane] = p[h] * sv;
+    } else {
 #pragma unroll
-      for (int h = 0; h < G; ++h) sm.u.w[wave][h][c][lane] = p[h] * sv;
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sw = word(vs, c >> 1);
+        const float sv = (c & 1) ? f16_hi(sw) : f16_lo(sw);
+#pragma unroll
+        for (int h = 0; h < G; ++h) sm.u.w[wave][h][c][lane] = p[h] * sv;
+      }
     }
     lds_wave_sync();
+    const int wrow = VT ? 0 : cj;  // weight row of this lane's value block
 
     // values: lane = channels 4*lane .. 4*lane+3 (block cj); this wave's VALU
     // stream goes first while it holds its operands
@@ -571,8 +588,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       float4_t wa[G], wb[G];  // weights of tokens 8ct..8ct+3 and 8ct+4..8ct+7
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        wa[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][ct * 8]);
-        wb[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][ct * 8 + 4]);
+        wa[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][ct * 8]);
+        wb[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][ct * 8 + 4]);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -598,8 +615,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     // "- 8" correction: the page's summed weights of block cj
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float4_t x = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][sub * 8]);
-      const float4_t y = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][cj][sub * 8 + 4]);
+      const float4_t x = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8]);
+      const float4_t y = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8 + 4]);
       const float ws = sum8(((x.x + x.y) + (x.z + x.w)) + ((y.x + y.y) + (y.z + y.w)));
       const float c1 = ws * 4.76837158203125e-07f;  // 8 * 2^-24
       o[h][0] -= c1;
@@ -714,7 +731,7 @@ __global__ __launch_bounds__(64 * kFoldWaves) void decode_fold_kernel(const floa
   }
 }
 
-template <int G>
+template <int G, bool VT>
 hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, const PlanArgs& plan, int max_items,
                            hipStream_t s) {
   QPrep<G>* qp = static_cast<QPrep<G>*>(qprep);
@@ -723,7 +740,7 @@ hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, const PlanArgs& pla
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_begin(F4KV_KERNEL_DECODE, s);
-  hipLaunchKernelGGL(decode_kernel<G>, dim3(max_items, a.Hkv), dim3(kThreads), 0, s, a,
+  hipLaunchKernelGGL((decode_kernel<G, VT>), dim3(max_items, a.Hkv), dim3(kThreads), 0, s, a,
                      static_cast<const QPrep<G>*>(qp));
   e = hipGetLastError();
   timing_end(F4KV_KERNEL_DECODE, s);
@@ -748,10 +765,10 @@ int64_t resident_workgroups(int G) {
   }
   hipError_t e = hipErrorUnknown;
   switch (G) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<1>, kThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<2>, kThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<4>, kThreads, 0); break;
-    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<8>, kThreads, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<1, false>, kThreads, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<2, false>, kThreads, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<4, false>, kThreads, 0); break;
+    default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<8, false>, kThreads, 0); break;
   }
   if (e != hipSuccess || per <= 0) per = 2;
   const int64_t total = static_cast<int64_t>(cus) * per;
@@ -851,11 +868,16 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
   void* qprep = base + plan.qprep_offset;
   const int G = Hq / a.Hkv;
   hipError_t e;
+  const bool vt = c.v_scale_per_token != 0;
   switch (G) {
-    case 1: e = launch_decode_g<1>(a, qprep, pa, plan.max_items, s); break;
-    case 2: e = launch_decode_g<2>(a, qprep, pa, plan.max_items, s); break;
-    case 4: e = launch_decode_g<4>(a, qprep, pa, plan.max_items, s); break;
-    default: e = launch_decode_g<8>(a, qprep, pa, plan.max_items, s); break;
+    case 1: e = vt ? launch_decode_g<1, true>(a, qprep, pa, plan.max_items, s)
+                   : launch_decode_g<1, false>(a, qprep, pa, plan.max_items, s); break;
+    case 2: e = vt ? launch_decode_g<2, true>(a, qprep, pa, plan.max_items, s)
+                   : launch_decode_g<2, false>(a, qprep, pa, plan.max_items, s); break;
+    case 4: e = vt ? launch_decode_g<4, true>(a, qprep, pa, plan.max_items, s)
+                   : launch_decode_g<4, false>(a, qprep, pa, plan.max_items, s); break;
+    default: e = vt ? launch_decode_g<8, true>(a, qprep, pa, plan.max_items, s)
+                    : launch_decode_g<8, false>(a, qprep, pa, plan.max_items, s); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_fold_kernel, dim3(static_cast<unsigned>(wb * Hq)), dim3(64 * kFoldWaves), 0, s, a.o,

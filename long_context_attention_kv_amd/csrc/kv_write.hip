@@ -12,7 +12,11 @@
 //
 // One thread owns one 32-value block of one token's K or V row: it writes the
 // block's 16 bytes (K) or eight 2-byte pieces (V) and its scale, so no byte is
-// shared between threads.
+// shared between threads.  When V carries one scale per token and head (the
+// per-token V scale of the same item), each V thread takes the absmax of the
+// token's whole V row (the 8 threads of a row read it each; the
+// writer is not on the decode clock), quantises its own block against that
+// scale, and the thread of block 0 writes the scale.
 #include "f4kv_internal.h"
 
 namespace f4kv {
@@ -30,6 +34,7 @@ struct KvWriteArgs {
   int32_t pos0;
   int64_t per_kind;  // T * H * (D / 32)
   int32_t H, D, num_pages;
+  int32_t v_per_token;  // V scale per (token, head) instead of per 32 values
 };
 
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
@@ -67,8 +72,16 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     x[4 * i + 3] = f.w;
   }
   float amax = 0.0f;
+  if (kind == 1 && a.v_per_token) {
+    const float4_t* row = reinterpret_cast<const float4_t*>(a.v + (t * a.H + h) * a.D);
+    for (int i = 0; i < a.D / 4; ++i) {
+      const float4_t f = row[i];
+      amax = fmaxf(fmaxf(amax, fabsf(f.x)), fmaxf(fabsf(f.y), fmaxf(fabsf(f.z), fabsf(f.w))));
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  }
 
   // absmax * 0.125 is exact in fp32; a single rounding to fp16 follows.
   const _Float16 s16 = static_cast<_Float16>(fminf(amax * 0.125f, 65504.0f));
@@ -114,7 +127,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
           tile + (static_cast<int64_t>(unit_c) * quads + j) * 16 + byte_in_unit);
       *dst = static_cast<uint16_t>(b0 | (b1 << 8));
     }
-    a.v_scale[(ph * kPage + off) * nb + c] = sbits;
+    if (!a.v_per_token)
+      a.v_scale[(ph * kPage + off) * nb + c] = sbits;
+    else if (c == 0)
+      a.v_scale[ph * kPage + off] = sbits;
   }
 }
 
@@ -137,6 +153,7 @@ hipError_t launch_common(const f4kv_cache& c, const float* k, const float* v, co
   a.H = c.num_kv_heads;
   a.D = c.head_dim;
   a.num_pages = c.num_pages;
+  a.v_per_token = c.v_scale_per_token;
   a.per_kind = static_cast<int64_t>(T) * a.H * (a.D / kBlock);
   const int64_t total = 2 * a.per_kind;
   const int threads = 256;

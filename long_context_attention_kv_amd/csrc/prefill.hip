@@ -113,8 +113,9 @@ __device__ __forceinline__ int vt_chunk(int row, int chunk) { return chunk ^ (((
 // Cells of one page for this thread, in two parts that are requested at
 // different times: the K part (K units (block 2 w + u, token t) for u = 0, 1,
 // w = wave, t = lane; the two K scales, adjacent in memory; one dword of the
-// page's V scale tile (token tid / 4, blocks 2 (tid % 4), + 1), which goes
-// through LDS) and the V part (V units: tokens 8 (2 w + u) .., channel quad j = lane).
+// page's V scale tile (token tid / 4, blocks 2 (tid % 4), + 1; with one V
+// scale per token (VT) tokens 2 (tid % 32), + 1), which goes through LDS) and
+// the V part (V units: tokens 8 (2 w + u) .., channel quad j = lane).
 struct KRaw {
   uint4 k[2];
   uint32_t ks;   // scales of the two K units, one per half
@@ -124,15 +125,18 @@ struct VRaw {
   uint4 v[2];
 };
 
+template <bool VT>
 __device__ __forceinline__ void load_k(const PrefillArgs& a, int64_t ph, int tid, KRaw& r) {
   const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
   const uint16_t* ksc = a.k_scale + ph * (kPage * 8);
-  const uint16_t* vsc = a.v_scale + ph * (kPage * 8);
   const int w = tid >> 6, t = tid & 63;
 #pragma unroll
   for (int u = 0; u < 2; ++u) r.k[u] = kt[(2 * w + u) * 64 + t];
   r.ks = *reinterpret_cast<const uint32_t*>(ksc + t * 8 + 2 * w);
-  r.vsd = *reinterpret_cast<const uint32_t*>(vsc + (tid >> 2) * 8 + 2 * (tid & 3));
+  if (VT)
+    r.vsd = *reinterpret_cast<const uint32_t*>(a.v_scale + ph * kPage + 2 * (tid & 31));
+  else
+    r.vsd = *reinterpret_cast<const uint32_t*>(a.v_scale + ph * (kPage * 8) + (tid >> 2) * 8 + 2 * (tid & 3));
 }
 
 __device__ __forceinline__ void load_v(const PrefillArgs& a, int64_t ph, int tid, VRaw& r) {
@@ -142,11 +146,17 @@ __device__ __forceinline__ void load_v(const PrefillArgs& a, int64_t ph, int tid
   for (int u = 0; u < 2; ++u) r.v[u] = vt[(2 * w + u) * 64 + t];
 }
 
-// This thread's dword of the page's V scale tile -> LDS [block][token].
+// This thread's dword of the page's V scale tile -> LDS [block][token] (VT:
+// row 0 holds the token scales, written by the first 32 threads).
+template <bool VT>
 __device__ __forceinline__ void store_vscales(PrefillSmem& sm, const KRaw& r, int tid, int parity) {
-  const int t = tid >> 2, b = 2 * (tid & 3);
-  sm.vsc[parity][b][t] = static_cast<uint16_t>(r.vsd);
-  sm.vsc[parity][b + 1][t] = static_cast<uint16_t>(r.vsd >> 16);
+  if (VT) {
+    if (tid < 32) *reinterpret_cast<uint32_t*>(&sm.vsc[parity][0][2 * tid]) = r.vsd;
+  } else {
+    const int t = tid >> 2, b = 2 * (tid & 3);
+    sm.vsc[parity][b][t] = static_cast<uint16_t>(r.vsd);
+    sm.vsc[parity][b + 1][t] = static_cast<uint16_t>(r.vsd >> 16);
+  }
 }
 
 // Dword j of K unit u -> 8 channels of one LDS row [token][channel in unpack
@@ -178,10 +188,12 @@ struct VScales {
   half2v_t hi[8], lo[8];  // split scales of tokens 16 g + 2k, + 1 (k = 0..7), block j / 8
 };
 
+template <bool VT>
 __device__ __forceinline__ void read_vscales(const PrefillSmem& sm, int tid, int parity, VScales& s) {
   const int g = tid >> 6, j = tid & 63;
-  const uint4 sa = *reinterpret_cast<const uint4*>(&sm.vsc[parity][j >> 3][16 * g]);
-  const uint4 sb = *reinterpret_cast<const uint4*>(&sm.vsc[parity][j >> 3][16 * g + 8]);
+  const int row = VT ? 0 : j >> 3;  // the lane's block, or the token scales
+  const uint4 sa = *reinterpret_cast<const uint4*>(&sm.vsc[parity][row][16 * g]);
+  const uint4 sb = *reinterpret_cast<const uint4*>(&sm.vsc[parity][row][16 * g + 8]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     split_scales(word(sa, k), s.hi[k], s.lo[k]);
@@ -204,6 +216,8 @@ __device__ __forceinline__ void v_piece(PrefillSmem& sm, const VRaw& r, const VS
   }
 }
 
+// VT: the cache's V scales are one per token and head.
+template <bool VT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ pt) {
   __shared__ PrefillSmem sm;
   const int qt = blockIdx.x;     // query tile
@@ -287,15 +301,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   if (pbeg < pend) {
     KRaw k0;
     const int64_t ph0 = page_handle(pbeg, cur_valid);
-    load_k(a, ph0, tid, k0);
+    load_k<VT>(a, ph0, tid, k0);
     load_v(a, ph0, tid, vcur);
     if (pbeg + 1 < pend) {
       kraw_ph = page_handle(pbeg + 1, kraw_valid);
-      load_k(a, kraw_ph, tid, kraw);
+      load_k<VT>(a, kraw_ph, tid, kraw);
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) unpack_k(sm, k0, tid, x >> 2, x & 3, nmagic);
-    store_vscales(sm, k0, tid, pbeg & 1);
+    store_vscales<VT>(sm, k0, tid, pbeg & 1);
   }
 
   // V^T operand addresses of this lane: row col (+ 32 d), chunk (2 (2 tt + s2) + half) swizzled
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     if (lp + 2 < pend) {
       kahead_valid = static_cast<uint32_t>(pid_next) < static_cast<uint32_t>(a.num_pages);
       kahead_ph = static_cast<int64_t>(kahead_valid ? pid_next : 0) * a.Hkv + g;
-      load_k(a, kahead_ph, tid, kahead);
+      load_k<VT>(a, kahead_ph, tid, kahead);
     }
     if (lp + 1 < pend) load_v(a, kraw_ph, tid, vnext);
     pid_next = pid_after;
@@ -446,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
 
     // ---- tile 0: S^T, V channels 0-2 of this page unpacked meanwhile ----
     VScales vs;
-    read_vscales(sm, tid, lp & 1, vs);
+    read_vscales<VT>(sm, tid, lp & 1, vs);
     uint32_t hv[4], lv[4];
     float16_t st0{};
     s_phase(0, st0, [&](int step) {
@@ -492,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       if (step < 3)
         unpack_k(sm, kraw, tid, (step + 5) >> 2, (step + 5) & 3, nmagic);
       else if (step == 3)
-        store_vscales(sm, kraw, tid, (lp + 1) & 1);
+        store_vscales<VT>(sm, kraw, tid, (lp + 1) & 1);
     });
 
     vcur = vnext;
@@ -584,7 +598,11 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
     a.l = out_l;
   }
   timing_begin(F4KV_KERNEL_PREFILL, s);
-  hipLaunchKernelGGL(prefill_kernel, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a, pt);
+  if (c.v_scale_per_token)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a, pt);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a,
+                       pt);
   hipError_t e = hipGetLastError();
   timing_end(F4KV_KERNEL_PREFILL, s);
   if (e != hipSuccess || plan.kv_splits == 1) return e;

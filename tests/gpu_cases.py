@@ -38,7 +38,7 @@ class PagedSet:
     """Sequences of given lengths in one shared pool, written by both sides."""
 
     def __init__(self, lengths, Hkv=4, D=256, seed=0, extra_pages=3, k_scale=1.0, v_scale=1.0, outliers=False,
-                 placement=0):
+                 placement=0, v_per_token=False):
         self.lengths = [int(x) for x in lengths]
         self.Hkv, self.D = Hkv, D
         g = synth.rng(100 + seed, 0)
@@ -60,9 +60,9 @@ class PagedSet:
             slots.append(self.pt[b, t // PAGE].astype(np.int64) * PAGE + t % PAGE)
         self.slots = np.concatenate(slots).astype(np.int32) if slots else np.zeros(0, np.int32)
         self.k, self.v = k, v
-        self.oc = of4.Cache(self.num_pages, Hkv, D)
+        self.oc = of4.Cache(self.num_pages, Hkv, D, v_per_token=v_per_token)
         self.oc.write(k, v, self.slots)
-        self.gc = f4.F4Cache(self.num_pages, Hkv, D)
+        self.gc = f4.F4Cache(self.num_pages, Hkv, D, v_scale_per_token=v_per_token)
         if T:
             f4.kv_cache_write_f4(self.gc, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                                  torch.from_numpy(self.slots).cuda())

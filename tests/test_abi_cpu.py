@@ -49,11 +49,16 @@ def test_cache_bytes(lib):
     # per token and KV head: 128 bytes of nibbles + 8 fp16 scales, for K and for V
     assert parts == (16384 * 4 * 64 * 128, 16384 * 4 * 64 * 16, 16384 * 4 * 64 * 128, 16384 * 4 * 64 * 16)
     assert total == 16384 * 64 * 4 * 2 * 144
-    assert lib.f4kv_cache_bytes(1, 1, 48, None, None, None, None) == 0
+    assert lib.f4kv_cache_bytes(1, 1, 48, 0, None, None, None, None) == 0
+    assert lib.f4kv_cache_bytes(1, 1, 256, 2, None, None, None, None) == 0
+    # one V scale per token and head: 130 bytes of V per token and head
+    total, parts = f4.cache_bytes(16384, 4, 256, v_scale_per_token=True)
+    assert parts == (16384 * 4 * 64 * 128, 16384 * 4 * 64 * 16, 16384 * 4 * 64 * 128, 16384 * 4 * 64 * 2)
+    assert total == 16384 * 64 * 4 * (144 + 130)
 
 
-def _cache(ptr=16, pages=8, heads=4, dim=256, page=64):
-    return B._CacheC(ptr, ptr, ptr, ptr, pages, heads, dim, page)
+def _cache(ptr=16, pages=8, heads=4, dim=256, page=64, vtok=0):
+    return B._CacheC(ptr, ptr, ptr, ptr, pages, heads, dim, page, vtok)
 
 
 def _yarn(**kw):
@@ -96,6 +101,7 @@ def test_yarn_factor_range_edges(lib):
     ("num_pages", 0, "num_pages"),
     ("k_nib", 0, "NULL"),
     ("v_scale", 8, "aligned"),
+    ("v_scale_per_token", 2, "v_scale_per_token"),
 ])
 def test_cache_descriptor_refused(lib, field, val, needle):
     c = _cache()

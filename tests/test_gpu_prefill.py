@@ -17,7 +17,7 @@ PAGE = 64
 class Chunk:
     """A sequence whose first pos0 tokens are cached; a chunk of T new tokens follows."""
 
-    def __init__(self, pos0, T, Hkv=4, G=4, D=256, seed=0, extra_pages=2):
+    def __init__(self, pos0, T, Hkv=4, G=4, D=256, seed=0, extra_pages=2, v_per_token=False):
         g = synth.rng(600 + seed, 0)
         n = pos0 + T
         npg = (n + PAGE - 1) // PAGE
@@ -32,9 +32,9 @@ class Chunk:
         self.qbits = synth.f32_to_bf16_bits(synth.normal_f32(g, (T, self.Hq, D)))
         t = np.arange(pos0)
         old_slots = (self.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
-        self.oc = of4.Cache(self.P, Hkv, D)
+        self.oc = of4.Cache(self.P, Hkv, D, v_per_token=v_per_token)
         self.oc.write(k_old, v_old, old_slots)
-        self.gc = f4.F4Cache(self.P, Hkv, D)
+        self.gc = f4.F4Cache(self.P, Hkv, D, v_scale_per_token=v_per_token)
         if pos0:
             f4.kv_cache_write_f4(self.gc, torch.from_numpy(k_old).cuda(), torch.from_numpy(v_old).cuda(),
                                  torch.from_numpy(old_slots).cuda())
