@@ -296,6 +296,34 @@ def bench_vtok(iters=20):
             "kv_tokens_per_s": sum(lengths) / (ms / 1e3), "call_gbs": by / (ms / 1e3) / 1e9}
 
 
+def bench_gather(iters=10):
+    """gather_kv_cache_f4 of 3 x 262,144 cached tokens into contiguous bf16 K and V rows."""
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 6)
+    lengths = [262144] * 3
+    L = DecodeLayer(lengths, 4.0, gen, outliers=True)
+    total = sum(lengths)
+    cu = torch.tensor([0, 262144, 524288, 786432], dtype=torch.int32, device=dev)
+    k = torch.empty((total, HKV, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((total, HKV, D), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        f4.gather_kv_cache_f4(L.cache, L.pt, cu, total, k_out=k, v_out=v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        f4.gather_kv_cache_f4(L.cache, L.pt, cu, total, k_out=k, v_out=v)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    # read: the cells; written: two bf16 rows of D values per token and head; plus the page table
+    by = total * HKV * (BYTES_PER_TOKEN_HEAD + 2 * D * 2) + L.num_pages * 4
+    del L, k, v
+    return {"workload": "gather_kv_cache_f4, 3 x 262,144 tokens -> bf16 rows", "ms": ms,
+            "gbs": by / (ms / 1e3) / 1e9, "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "bytes": by}
+
+
 def bench_ragged(iters=20):
     dev = "cuda"
     lengths = synth.ragged_lengths(4)
@@ -484,6 +512,9 @@ def main():
         torch.cuda.empty_cache()
         extra["decode_v_per_token"] = bench_vtok()
         log("v per token:", extra["decode_v_per_token"])
+        torch.cuda.empty_cache()
+        extra["gather_bf16"] = bench_gather()
+        log("gather:", extra["gather_bf16"])
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(args.cpu_tokens)

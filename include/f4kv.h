@@ -161,7 +161,8 @@ int yarn_rope_apply(const float* cos_rows, const float* sin_rows,
  * Quantises k and v (fp32 [T][H][D], 16-byte aligned) into the cache slots
  * slot_mapping[t] = page * 64 + offset (-1 skips the token; live entries must
  * be distinct, else the result is undefined).  Per token, kv head and
- * 32-value block:
+ * 32-value block (for V with v_scale_per_token: per token and kv head, the
+ * absmax taken over the whole V row):
  *   s = fp16_nearest_even(min(absmax * 0.125, 65504)),
  *   code = clamp(nearest_even(x / s), -8, 7) with the exact quotient
  *   (s == 0: every code 0), nibble = code + 8.
@@ -241,6 +242,26 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q,
                           int32_t T, int32_t Hq, int32_t pos0, float sm_scale,
                           float* out, float* out_m, float* out_l,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * gather_kv_cache_f4 [MRS item 2: the cache's gather path gains an F4 variant]
+ * Dequantises the cached keys and values of B sequences into contiguous rows:
+ * token i of sequence b, for i < cu_seq_lens[b + 1] - cu_seq_lens[b], becomes
+ * row cu_seq_lens[b] + i of k_out and v_out, every value (nibble - 8) * scale
+ * (exact in fp32; bf16 outputs rounded to nearest-even).  A token whose page
+ * id is out of range gives a zero row; rows at or past total_tokens are not
+ * written.
+ *   page_table   int32 [B][max_pages]
+ *   cu_seq_lens  int32 [B + 1] (device): row offsets, cu_seq_lens[0] = 0,
+ *                non-decreasing, each length at most max_pages * 64, and
+ *                cu_seq_lens[B] <= total_tokens
+ *   k_out, v_out [total_tokens][H][D] of out_dtype (F4KV_BF16 or F4KV_F32),
+ *                16-byte aligned
+ * Supported: D == 256; B <= 65535.
+ */
+int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const int32_t* cu_seq_lens,
+                       int32_t B, int32_t max_pages, int32_t total_tokens, void* k_out, void* v_out,
+                       int32_t out_dtype, hipStream_t stream);
 
 /*
  * Kernel timing (a measurement aid of this library, not an operation of the

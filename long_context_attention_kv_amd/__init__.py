@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     cache_bytes,
     decode_workspace_size,
+    gather_kv_cache_f4,
     kv_cache_write_f4,
     library_path,
     load_library,
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "lse_merge",
     "paged_attn_prefill_f4_workspace_size",
     "paged_attn_prefill_f4",
+    "gather_kv_cache_f4",
     "f4kv_timing_start",
     "f4kv_timing_stop",
 )

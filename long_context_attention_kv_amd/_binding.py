@@ -52,6 +52,7 @@ _SIGS = {
     "paged_attn_prefill_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I]),
     "paged_attn_prefill_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                                         _P, _P, _P, _P, C.c_size_t, _P]),
+    "gather_kv_cache_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _I, _I, _I, _P, _P, _I, _P]),
     "f4kv_timing_start": (C.c_int, [_I, _I]),
     "f4kv_timing_stop": (C.c_int, [_I, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
@@ -306,6 +307,33 @@ def paged_attn_prefill_f4(cache: F4Cache, q, k_new, v_new, page_table, pos0: int
                                      page_table.numel(), T, Hq, int(pos0), float(sm_scale), _ptr(out), _ptr(out_m),
                                      _ptr(out_l), _ptr(workspace), ws_bytes, _stream()))
     return out, out_m, out_l
+
+
+def gather_kv_cache_f4(cache: F4Cache, page_table, cu_seq_lens, total_tokens: int, dtype=torch.bfloat16,
+                       k_out=None, v_out=None):
+    """Dequantise B sequences' cached K and V into rows [total_tokens, H, D] (bf16 or fp32);
+    sequence b's tokens go to rows cu_seq_lens[b] .. cu_seq_lens[b + 1] - 1.  Returns (k_out, v_out)."""
+    lib = load_library()
+    _need(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2:
+        raise ValueError("page_table must be [B, max_pages]")
+    B, max_pages = page_table.shape
+    _need(cu_seq_lens, torch.int32, (B + 1,), "cu_seq_lens")
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("dtype must be bfloat16 or float32")
+    shape = (int(total_tokens), cache.num_kv_heads, cache.head_dim)
+    dev = page_table.device
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=dtype, device=dev)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=dtype, device=dev)
+    _need(k_out, dtype, shape, "k_out")
+    _need(v_out, dtype, shape, "v_out")
+    c = cache._c()
+    _check("gather_kv_cache_f4",
+           lib.gather_kv_cache_f4(C.byref(c), _ptr(page_table), _ptr(cu_seq_lens), B, max_pages, int(total_tokens),
+                                  _ptr(k_out), _ptr(v_out), BF16 if dtype == torch.bfloat16 else F32, _stream()))
+    return k_out, v_out
 
 
 class KernelTimer:

@@ -250,6 +250,29 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q, const floa
                   fn);
 }
 
+int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const int32_t* cu_seq_lens, int32_t B,
+                       int32_t max_pages, int32_t total_tokens, void* k_out, void* v_out, int32_t out_dtype,
+                       hipStream_t stream) {
+  const char* fn = "gather_kv_cache_f4";
+  if (int r = check_cache(cache, fn)) return r;
+  if (out_dtype != F4KV_F32 && out_dtype != F4KV_BF16) return fail(F4KV_ERR_INVALID, "%s: bad out_dtype", fn);
+  if (B < 0 || B > 65535) return fail(F4KV_ERR_INVALID, "%s: B must be in [0, 65535] (got %d)", fn, B);
+  if (total_tokens < 0) return fail(F4KV_ERR_INVALID, "%s: total_tokens must be >= 0", fn);
+  if (B == 0 || total_tokens == 0) return ok();
+  if (max_pages <= 0 || max_pages > INT32_MAX / f4kv::kPage)
+    return fail(F4KV_ERR_INVALID, "%s: max_pages out of range (%d)", fn, max_pages);
+  if (cache->head_dim != f4kv::kHeadDim)
+    return fail(F4KV_ERR_UNSUPPORTED, "%s: head_dim %d not implemented (256 is)", fn, cache->head_dim);
+  if (!page_table || !cu_seq_lens || !k_out || !v_out) return fail(F4KV_ERR_INVALID, "%s: NULL array", fn);
+  if (!aligned(page_table, 4) || !aligned(cu_seq_lens, 4) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(F4KV_ERR_INVALID, "%s: page_table, cu_seq_lens must be 4-byte and the outputs 16-byte aligned", fn);
+  if (static_cast<int64_t>(total_tokens) * cache->num_kv_heads * cache->head_dim > (int64_t(1) << 40))
+    return fail(F4KV_ERR_INVALID, "%s: output too large", fn);
+  return launched(f4kv::launch_gather(*cache, page_table, cu_seq_lens, B, max_pages, total_tokens, k_out, v_out,
+                                      out_dtype == F4KV_BF16, stream),
+                  fn);
+}
+
 int f4kv_timing_start(int32_t kernel, int32_t max_launches) {
   const char* fn = "f4kv_timing_start";
   if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL)

@@ -64,6 +64,9 @@ hipError_t launch_rope_apply(const float* c, const float* sn, const void* x, int
 hipError_t launch_merge(const float* m, const float* l, const float* o, int32_t C, int32_t R,
                         int32_t D, float* out, float* out_m, float* out_l, hipStream_t s);
 
+hipError_t launch_gather(const f4kv_cache& c, const int32_t* pt, const int32_t* cu, int32_t B, int32_t max_pages,
+                         int32_t total, void* k_out, void* v_out, bool bf16, hipStream_t s);
+
 struct DecodePlan {
   int32_t per_head_target;   // work items per KV head that fill the GPU once
   int32_t max_items;         // bound on the work items of any context lengths

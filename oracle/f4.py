@@ -46,6 +46,21 @@ def fp16_round(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float16)
 
 
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round fp64 values to the nearest bf16 value (8 significant bits, fp32's
+    exponent range), ties to even; returned as fp64.  Finite inputs within
+    bf16's range only."""
+    a = np.asarray(a, dtype=np.float64)
+    out = np.zeros_like(a)
+    nz = a != 0.0
+    e = np.floor(np.log2(np.abs(a[nz])))
+    # a power of two just below |a| can come out one too high from log2's rounding
+    e = np.where(np.abs(a[nz]) < 2.0 ** e, e - 1, e)
+    q = 2.0 ** (np.maximum(e, -126.0) - 7.0)  # spacing of bf16 values at that binade
+    out[nz] = np.rint(a[nz] / q) * q          # exact scaling by a power of two; rint ties to even
+    return out
+
+
 def quantize_group(x: np.ndarray):
     """Quantise x[..., n] (fp32 values) with one scale per group along the last
     axis (n = 32 for a cell, head_dim for a per-token V row).  Returns (codes
@@ -170,6 +185,27 @@ class Cache:
         else:
             vd = dequantize_blocks(vc.reshape(PAGE, nb, BLOCK), vs).reshape(PAGE, self.D)
         return kd, vd
+
+    def gather(self, page_table, lengths):
+        """Dequantised K and V of each sequence's tokens, concatenated: fp64
+        [sum(lengths), H, D] each (token i of sequence b at page_table[b][i // 64],
+        slot i % 64; a page id outside the pool gives zero rows)."""
+        page_table = np.asarray(page_table)
+        total = int(sum(lengths))
+        K = np.zeros((total, self.H, self.D))
+        V = np.zeros((total, self.H, self.D))
+        row = 0
+        for b, n in enumerate(lengths):
+            for lp in range((n + PAGE - 1) // PAGE):
+                pid = int(page_table[b, lp])
+                cnt = min(PAGE, n - lp * PAGE)
+                if 0 <= pid < self.P:
+                    for h in range(self.H):
+                        kd, vd = self.page_values(pid, h)
+                        K[row:row + cnt, h] = kd[:cnt]
+                        V[row:row + cnt, h] = vd[:cnt]
+                row += cnt
+        return K, V
 
     def arrays(self):
         """The four arrays as raw bytes in C order (k_nib, k_scale bits, v_nib, v_scale bits)."""

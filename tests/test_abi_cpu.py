@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +140,20 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=16, ws_bytes=need - 1) == 3
     assert "workspace" in _err(lib)
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=None, ws_bytes=need) == 3
+
+
+def test_gather_argument_checks(lib):
+    c = _cache()
+    g = lib.gather_kv_cache_f4
+    assert g(C.byref(c), 16, 16, 0, 4, 100, 16, 16, 1, None) == 0                      # B == 0: nothing to do
+    assert g(C.byref(c), 16, 16, 2, 4, 0, 16, 16, 1, None) == 0                        # no rows
+    assert g(C.byref(c), 16, 16, 2, 4, 100, 16, 16, 5, None) == 1 and "out_dtype" in _err(lib)
+    assert g(C.byref(c), None, 16, 2, 4, 100, 16, 16, 1, None) == 1 and "NULL" in _err(lib)
+    assert g(C.byref(c), 16, 16, 2, 4, 100, 24, 16, 1, None) == 1 and "aligned" in _err(lib)
+    assert g(C.byref(c), 16, 16, 70000, 4, 100, 16, 16, 1, None) == 1
+    assert g(C.byref(c), 16, 16, 2, 0, 100, 16, 16, 1, None) == 1 and "max_pages" in _err(lib)
+    c64 = _cache(dim=64)
+    assert g(C.byref(c64), 16, 16, 2, 4, 100, 16, 16, 1, None) == 2 and "head_dim" in _err(lib)
 
 
 def test_merge_and_rope_apply_checks(lib):

@@ -282,3 +282,51 @@ def test_per_token_cache_layout_and_round_trip():
                  np.zeros((int((slots >= 0).sum()), H, D // 32), np.float16), vq[slots >= 0],
                  np.zeros((int((slots >= 0).sum()), H, D // 32), np.float16))
     assert np.array_equal(cb.v_nib, c.v_nib)
+
+
+# ---- bf16 rounding and the gather of dequantised rows -------------------------
+
+def test_bf16_round_ties_and_library_agreement():
+    one = 1.0
+    ulp = 2.0 ** -7  # bf16 keeps 8 significant bits
+    r = f4.bf16_round(np.array([one + ulp / 2, one + 3 * ulp / 2, one + ulp / 2 + 2 ** -20, -(one + ulp / 2),
+                                2.0 ** -130, 3.0 * 2 ** 100, 0.0]))
+    assert r[0] == 1.0 and r[1] == 1.0 + 2 * ulp and r[2] == 1.0 + ulp and r[3] == -1.0
+    assert r[4] == 2.0 ** -130 and r[5] == 3.0 * 2 ** 100 and r[6] == 0.0
+    # against torch's own fp32 -> bf16 conversion (a library routine)
+    import torch
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.uniform(-20, 20, 20000)).astype(np.float32)
+    x[:64] = (np.arange(64) - 32 + 0.5) * np.float32(2.0 ** -3)  # exact ties at several magnitudes
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(f4.bf16_round(x.astype(np.float64)), ref)
+
+
+@pytest.mark.parametrize("vt", [False, True])
+def test_gather_rows_are_the_written_values(vt):
+    rng = np.random.default_rng(14)
+    P, H, D = 6, 2, 64
+    lengths = [70, 0, 130]
+    c = f4.Cache(P, H, D, v_per_token=vt)
+    pt = np.full((3, 3), -1, np.int32)
+    perm = rng.permutation(P)
+    pt[0, :2] = perm[:2]
+    pt[2, :3] = perm[2:5]
+    rows_k, rows_v = [], []
+    for b, n in enumerate(lengths):
+        if n == 0:
+            continue
+        k = rng.standard_normal((n, H, D)).astype(np.float32)
+        v = rng.standard_normal((n, H, D)).astype(np.float32)
+        t = np.arange(n)
+        c.write(k, v, pt[b, t // 64].astype(np.int64) * 64 + t % 64)
+        rows_k.append(f4.dequantize_blocks(*f4.quantize_blocks(k.reshape(n, H, D // 32, 32))).reshape(n, H, D))
+        rows_v.append(f4.dequantize_blocks(*f4.quantize_group(v)) if vt else
+                      f4.dequantize_blocks(*f4.quantize_blocks(v.reshape(n, H, D // 32, 32))).reshape(n, H, D))
+    K, V = c.gather(pt, lengths)
+    assert np.array_equal(K, np.concatenate(rows_k)) and np.array_equal(V, np.concatenate(rows_v))
+    # a page id outside the pool gives zero rows
+    pt2 = pt.copy()
+    pt2[2, 1] = P + 5
+    K2, _ = c.gather(pt2, lengths)
+    assert np.all(K2[70 + 64:70 + 128] == 0) and np.array_equal(K2[:70 + 64], K[:70 + 64])
