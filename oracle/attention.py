@@ -107,6 +107,43 @@ def decode(cache, q, page_table, context_lens, sm_scale: float,
     return out, m, l
 
 
+def decode_rows(cache, q, page_table, context_lens, sm_scale: float,
+                window_tokens: int = 0, num_windows: int = 1):
+    """Decode of R query rows per sequence, as one round of speculative
+    verification takes them (ignis context-and-speculation page,
+    ``--spec-draft-tokens`` / ``--spec-draft-rows`` rows: a lane verifies up to
+    7 drafted tokens, i.e. up to 8 rows, in one round).
+
+    q: [B, R, Hq, D].  Row r of sequence b is the query at position
+    C_b - R + r: it attends to tokens [0, C_b - R + r] (its own K/V, and those
+    of the rows before it, are already in the cache), within each window as in
+    ``decode``.  A row with no token (C_b - R + r < 0) gives (-inf, 0, 0).
+    Returns out [W, B, R, Hq, D], m [W, B, R, Hq], l [W, B, R, Hq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, R, Hq, D = q.shape
+    Hkv = cache.H
+    G = Hq // Hkv
+    W = num_windows
+    out = np.zeros((W, B, R, Hq, D))
+    m = np.full((W, B, R, Hq), NEG_INF)
+    l = np.zeros((W, B, R, Hq))
+    for b in range(B):
+        C = int(context_lens[b])
+        for g in range(Hkv):
+            K, V = gather_values(cache, page_table[b], C, g)
+            for r in range(R):
+                n = max(0, C - R + r + 1)  # tokens this row sees
+                for w in range(W):
+                    lo, hi = (0, C) if window_tokens == 0 else (w * window_tokens, min(C, (w + 1) * window_tokens))
+                    lo = min(lo, n)
+                    hi = max(min(hi, n), lo)
+                    for h in range(g * G, (g + 1) * G):
+                        mm, ll, oo = partial_state(q[b, r, h], K[lo:hi], V[lo:hi], sm_scale)
+                        out[w, b, r, h], m[w, b, r, h], l[w, b, r, h] = oo, mm, ll
+    return out, m, l
+
+
 def decode_head_from_values(q_rows, K, V, sm_scale: float, window_tokens: int = 0, num_windows: int = 1):
     """Decode for one KV head given its dequantised K, V [C, D] directly.
 

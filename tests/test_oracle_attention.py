@@ -222,3 +222,48 @@ def test_decode_over_per_token_v_scales_matches_textbook_attention(C):
     np.testing.assert_allclose(out[0, 0], ref, rtol=1e-12, atol=1e-12)
     if C == 1:  # one token: the output is that token's dequantised V row
         np.testing.assert_array_equal(out[0, 0], np.repeat(Vd[:, 0], G, axis=0))
+
+
+# ---- several query rows per sequence (speculative verification rounds) -------
+
+def test_decode_rows_single_row_is_decode_and_rows_are_prefill_rows():
+    rng = np.random.default_rng(950)
+    Hkv, D, G, R = 2, 64, 2, 3
+    lengths = [130, 2, 64]
+    cache, pt, kv = _filled_cache(rng, 12, Hkv, D, lengths)
+    q = rng.standard_normal((3, R, G * Hkv, D))
+    out, m, l = att.decode_rows(cache, q, pt, lengths, 0.125)
+    # one row per sequence is plain decode
+    o1, m1, l1 = att.decode_rows(cache, q[:, -1:], pt, lengths, 0.125)
+    d, dm, dl = att.decode(cache, q[:, -1], pt, lengths, 0.125)
+    np.testing.assert_array_equal(o1[:, :, 0], d)
+    np.testing.assert_array_equal(m1[:, :, 0], dm)
+    # row r equals a decode over the first C - R + r + 1 tokens
+    for r in range(R):
+        lens_r = [max(0, n - R + r + 1) for n in lengths]
+        dr, dmr, dlr = att.decode(cache, q[:, r], pt, lens_r, 0.125)
+        np.testing.assert_allclose(out[:, :, r], dr, rtol=1e-13, atol=1e-13)
+        np.testing.assert_array_equal(m[:, :, r], dmr)
+    # the sequence of 2 tokens: its first row (position -1) sees nothing
+    assert np.isneginf(m[0, 1, 0]).all() and (l[0, 1, 0] == 0).all() and not out[0, 1, 0].any()
+    # and the R rows of a sequence are the prefill rows of a chunk at C - R
+    for b, n in enumerate(lengths):
+        if n < R:
+            continue
+        po, pm, pl = att.prefill(cache, q[b], pt[b], n - R, 0.125)
+        np.testing.assert_allclose(out[0, b], po, rtol=1e-13, atol=1e-13)
+
+
+def test_decode_rows_windows_fold_to_the_whole_context():
+    rng = np.random.default_rng(951)
+    Hkv, D, G, R = 1, 64, 4, 4
+    lengths = [300]
+    cache, pt, kv = _filled_cache(rng, 6, Hkv, D, lengths)
+    q = rng.standard_normal((1, R, G, D))
+    ow, mw, lw = att.decode_rows(cache, q, pt, lengths, 0.125, window_tokens=128, num_windows=3)
+    o, m, l = att.decode_rows(cache, q, pt, lengths, 0.125)
+    for r in range(R):
+        for h in range(G):
+            M, L, O = att.merge_states(mw[:, 0, r, h], lw[:, 0, r, h], ow[:, 0, r, h])
+            np.testing.assert_allclose(O, o[0, 0, r, h], rtol=1e-12, atol=1e-12)
+            assert abs(M - m[0, 0, r, h]) <= 1e-12 and abs(L - l[0, 0, r, h]) <= 1e-9 * L
