@@ -296,6 +296,35 @@ def bench_vtok(iters=20):
             "kv_tokens_per_s": sum(lengths) / (ms / 1e3), "call_gbs": by / (ms / 1e3) / 1e9}
 
 
+def bench_rows(R, iters=10):
+    """R query rows per sequence (a speculative verification round) at the config-1 layer shape."""
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 7)
+    lengths = [262144] * 3
+    L = DecodeLayer(lengths, 4.0, gen, outliers=True)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 17)
+    q = torch.randn((3, R, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(max(16, f4.decode_rows_workspace_size(3, R, HQ, HKV, D, 262144)), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, 3, R, HQ, D), device=dev)
+    for _ in range(2):
+        f4.paged_attn_decode_rows_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=64 * iters) as t:
+        e0.record()
+        for _ in range(iters):
+            f4.paged_attn_decode_rows_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    by = decode_algorithmic_bytes(lengths)  # the KV stream of one call, read once per pass
+    del L
+    return {"workload": f"decode of {R} query rows per lane, 3 x 262,144 tokens, one layer", "rows": R,
+            "call_ms": ms, "kernel_ms_per_call": t.total_ms / iters, "passes_per_call": t.launches // iters,
+            "row_kv_tokens_per_s": R * sum(lengths) / (ms / 1e3), "kv_stream_gbs": by / (ms / 1e3) / 1e9}
+
+
 def bench_gather(iters=10):
     """gather_kv_cache_f4 of 3 x 262,144 cached tokens into contiguous bf16 K and V rows."""
     dev = "cuda"
@@ -515,6 +544,10 @@ def main():
         torch.cuda.empty_cache()
         extra["gather_bf16"] = bench_gather()
         log("gather:", extra["gather_bf16"])
+        for R in (2, 8):
+            torch.cuda.empty_cache()
+            extra[f"decode_rows_{R}"] = bench_rows(R)
+            log(f"rows {R}:", extra[f"decode_rows_{R}"])
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(args.cpu_tokens)

@@ -205,6 +205,31 @@ int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * paged_attn_decode_rows_f4 [IGN --spec-draft-tokens / --spec-draft-rows: a
+ * verify round takes up to 8 query rows of a lane; MRS item 2; FT item 2]
+ * Decode of R query rows per sequence (1 <= R <= 8), as one round of
+ * speculative verification: row r of sequence b is the query at position
+ * context_lens[b] - R + r and attends to tokens [0, context_lens[b] - R + r]
+ * of each window, with the states and windows of paged_attn_decode_f4 (a row
+ * before position 0 gives (-inf, 0, 0)).  R == 1 is paged_attn_decode_f4.
+ *   q      bf16 [B][R][Hq][D] (already rotated), 16-byte aligned
+ *   out    fp32 [W][B][R][Hq][D];  out_m, out_l fp32 [W][B][R][Hq] or NULL
+ *   other arguments as paged_attn_decode_f4; the workspace size comes from
+ *   paged_attn_decode_rows_f4_workspace_size().
+ * The rows of a KV head's query heads are processed together, up to 8 per
+ * pass over the pages (Hq / H * R rows; more take several passes).
+ */
+size_t paged_attn_decode_rows_f4_workspace_size(int32_t B, int32_t R, int32_t Hq, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_context_len,
+                                                int32_t num_windows, int32_t window_tokens);
+int paged_attn_decode_rows_f4(const f4kv_cache* cache, const uint16_t* q,
+                              const int32_t* page_table, const int32_t* context_lens,
+                              int32_t B, int32_t R, int32_t Hq, int32_t max_pages, int32_t max_context_len,
+                              int32_t num_windows, int32_t window_tokens, float sm_scale,
+                              float* out, float* out_m, float* out_l,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * lse_merge [FT item 2: partial windows folded by log-sum-exp]
  * Folds C partial states per row:  M = max_c m_c,  w_c = l_c exp(m_c - M),
  *   L = sum w_c,  out = sum w_c o_c / L;  rows with every l_c == 0 give

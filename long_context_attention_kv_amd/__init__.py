@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     YarnParams,
     abi_version,
     cache_bytes,
+    decode_rows_workspace_size,
     decode_workspace_size,
     gather_kv_cache_f4,
     kv_cache_write_f4,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     load_library,
     lse_merge,
     paged_attn_decode_f4,
+    paged_attn_decode_rows_f4,
     paged_attn_prefill_f4,
     prefill_workspace_size,
     yarn_rope_apply,
@@ -38,6 +40,8 @@ EXPORTED_SYMBOLS = (
     "kv_cache_write_f4",
     "paged_attn_decode_f4_workspace_size",
     "paged_attn_decode_f4",
+    "paged_attn_decode_rows_f4_workspace_size",
+    "paged_attn_decode_rows_f4",
     "lse_merge",
     "paged_attn_prefill_f4_workspace_size",
     "paged_attn_prefill_f4",

@@ -48,6 +48,9 @@ _SIGS = {
     "paged_attn_decode_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_decode_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, C.c_float,
                                        _P, _P, _P, _P, C.c_size_t, _P]),
+    "paged_attn_decode_rows_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "paged_attn_decode_rows_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, C.c_float,
+                                            _P, _P, _P, _P, C.c_size_t, _P]),
     "lse_merge": (C.c_int, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "paged_attn_prefill_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I]),
     "paged_attn_prefill_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
@@ -251,6 +254,47 @@ def paged_attn_decode_f4(cache: F4Cache, q, page_table, context_lens, max_contex
                                     page_table.shape[1], int(max_context_len), W, int(window_tokens),
                                     float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _ptr(workspace), ws_bytes,
                                     _stream()))
+    return out, out_m, out_l
+
+
+def decode_rows_workspace_size(B, R, Hq, num_kv_heads, head_dim, max_context_len, num_windows=1,
+                               window_tokens=0) -> int:
+    return load_library().paged_attn_decode_rows_f4_workspace_size(B, R, Hq, num_kv_heads, head_dim, max_context_len,
+                                                                   num_windows, window_tokens)
+
+
+def paged_attn_decode_rows_f4(cache: F4Cache, q, page_table, context_lens, max_context_len: int, sm_scale: float,
+                              num_windows: int = 1, window_tokens: int = 0, out=None, out_m=None, out_l=None,
+                              workspace=None):
+    """Decode of R query rows per sequence (q [B, R, Hq, D]; row r at position context_len - R + r);
+    returns (out [W, B, R, Hq, D], m [W, B, R, Hq], l [W, B, R, Hq])."""
+    lib = load_library()
+    B, R, Hq, D = q.shape
+    _need(q, torch.bfloat16, (B, R, Hq, D), "q")
+    _need(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    _need(context_lens, torch.int32, (B,), "context_lens")
+    W = num_windows
+    dev = q.device
+    if out is None:
+        out = torch.empty((W, B, R, Hq, D), dtype=torch.float32, device=dev)
+    if out_m is None:
+        out_m = torch.empty((W, B, R, Hq), dtype=torch.float32, device=dev)
+    if out_l is None:
+        out_l = torch.empty((W, B, R, Hq), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, (W, B, R, Hq, D), "out")
+    ws_need = decode_rows_workspace_size(B, R, Hq, cache.num_kv_heads, cache.head_dim, max_context_len, W,
+                                         window_tokens)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cache._c()
+    _check("paged_attn_decode_rows_f4",
+           lib.paged_attn_decode_rows_f4(C.byref(c), _ptr(q), _ptr(page_table), _ptr(context_lens), B, R, Hq,
+                                         page_table.shape[1], int(max_context_len), W, int(window_tokens),
+                                         float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _ptr(workspace),
+                                         ws_bytes, _stream()))
     return out, out_m, out_l
 
 

@@ -143,22 +143,32 @@ int kv_cache_write_f4(const f4kv_cache* cache, const float* k, const float* v, c
 
 size_t paged_attn_decode_f4_workspace_size(int32_t B, int32_t Hq, int32_t num_kv_heads, int32_t head_dim,
                                            int32_t max_context_len, int32_t num_windows, int32_t window_tokens) {
-  if (B <= 0 || Hq <= 0 || num_kv_heads <= 0 || head_dim != f4kv::kHeadDim || max_context_len < 0 ||
-      num_windows <= 0 || window_tokens < 0)
-    return 0;
-  return f4kv::plan_decode(B, Hq, num_kv_heads, max_context_len, num_windows, window_tokens).ws_bytes;
+  return paged_attn_decode_rows_f4_workspace_size(B, 1, Hq, num_kv_heads, head_dim, max_context_len, num_windows,
+                                                  window_tokens);
 }
 
-int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,
-                         const int32_t* context_lens, int32_t B, int32_t Hq, int32_t max_pages,
-                         int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale,
-                         float* out, float* out_m, float* out_l, void* workspace, size_t ws_bytes,
-                         hipStream_t stream) {
-  const char* fn = "paged_attn_decode_f4";
+size_t paged_attn_decode_rows_f4_workspace_size(int32_t B, int32_t R, int32_t Hq, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_context_len, int32_t num_windows,
+                                                int32_t window_tokens) {
+  if (B <= 0 || R < 1 || R > 8 || Hq <= 0 || num_kv_heads <= 0 || Hq % num_kv_heads != 0 ||
+      head_dim != f4kv::kHeadDim || max_context_len < 0 || num_windows <= 0 || window_tokens < 0)
+    return 0;
+  return f4kv::plan_decode(B, R, Hq, num_kv_heads, max_context_len, num_windows, window_tokens).ws_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,
+                  const int32_t* context_lens, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
+                  int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale, float* out,
+                  float* out_m, float* out_l, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (int r = check_cache(cache, fn)) return r;
   const int32_t Hkv = cache->num_kv_heads;
   if (B < 0 || Hq <= 0 || max_pages <= 0 || max_context_len < 0)
     return fail(F4KV_ERR_INVALID, "%s: need B >= 0, Hq > 0, max_pages > 0, max_context_len >= 0", fn);
+  if (R < 1 || R > 8) return fail(F4KV_ERR_INVALID, "%s: rows per sequence must be in [1, 8] (got %d)", fn, R);
   if (Hq % Hkv != 0) return fail(F4KV_ERR_INVALID, "%s: Hq (%d) not a multiple of num_kv_heads (%d)", fn, Hq, Hkv);
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_pages) * f4kv::kPage)
     return fail(F4KV_ERR_INVALID, "%s: max_context_len exceeds max_pages * 64", fn);
@@ -174,22 +184,48 @@ int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q, const int32
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(F4KV_ERR_UNSUPPORTED, "%s: query heads per KV head must be 1, 2, 4 or 8 (got %d)", fn, G);
   if (static_cast<int64_t>(B) * Hkv > 65535) return fail(F4KV_ERR_UNSUPPORTED, "%s: B * num_kv_heads > 65535", fn);
+  if (static_cast<int64_t>(num_windows) * B * R * Hq > (int64_t(1) << 31) - 1)
+    return fail(F4KV_ERR_UNSUPPORTED, "%s: too many output rows", fn);
   if (B == 0) return ok();
   if (!q || !page_table || !context_lens || !out) return fail(F4KV_ERR_INVALID, "%s: NULL array", fn);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4) ||
       (out_m && !aligned(out_m, 4)) || (out_l && !aligned(out_l, 4)))
     return fail(F4KV_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
-  const f4kv::DecodePlan plan = f4kv::plan_decode(B, Hq, Hkv, max_context_len, num_windows, window_tokens);
+  const f4kv::DecodePlan plan = f4kv::plan_decode(B, R, Hq, Hkv, max_context_len, num_windows, window_tokens);
   if (plan.ws_bytes > 0) {
     if (!workspace || ws_bytes < plan.ws_bytes)
       return fail(F4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, plan.ws_bytes,
                   workspace ? ws_bytes : size_t(0));
     if (!aligned(workspace, 16)) return fail(F4KV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
   }
-  return launched(f4kv::launch_decode(*cache, q, page_table, context_lens, B, Hq, max_pages, max_context_len,
+  return launched(f4kv::launch_decode(*cache, q, page_table, context_lens, B, R, Hq, max_pages, max_context_len,
                                       num_windows, window_tokens, sm_scale, out, out_m, out_l, workspace, plan,
                                       stream),
                   fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,
+                         const int32_t* context_lens, int32_t B, int32_t Hq, int32_t max_pages,
+                         int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale,
+                         float* out, float* out_m, float* out_l, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  return decode_common("paged_attn_decode_f4", cache, q, page_table, context_lens, B, 1, Hq, max_pages,
+                       max_context_len, num_windows, window_tokens, sm_scale, out, out_m, out_l, workspace, ws_bytes,
+                       stream);
+}
+
+int paged_attn_decode_rows_f4(const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,
+                              const int32_t* context_lens, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
+                              int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale,
+                              float* out, float* out_m, float* out_l, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  return decode_common("paged_attn_decode_rows_f4", cache, q, page_table, context_lens, B, R, Hq, max_pages,
+                       max_context_len, num_windows, window_tokens, sm_scale, out, out_m, out_l, workspace, ws_bytes,
+                       stream);
 }
 
 int lse_merge(const float* m, const float* l, const float* o, int32_t C, int32_t R, int32_t D, float* out,

@@ -36,6 +36,7 @@
 //    corrected once per page with the page's summed weights.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
+#include <algorithm>
 #include <atomic>
 
 #include "f4kv_internal.h"
@@ -70,13 +71,17 @@ struct DecodeArgs {
   const int4* items;       // work items (window * B + sequence, first page, end page, first item of the range)
   const int32_t* n_items;  // number of valid items
   const int32_t* count;    // [W * B] items of each (window, sequence)
-  float* o;                // partial outputs [item][Hq][D]
-  float* m;                // [item][Hq], log2 units
-  float* l;                // [item][Hq]
-  float* out;              // [W * B][Hq][D]
-  float* out_m;            // [W * B][Hq] or null
-  float* out_l;            // [W * B][Hq] or null
+  float* o;                // partial outputs [item][Hr][D]
+  float* m;                // [item][Hr], log2 units
+  float* l;                // [item][Hr]
+  float* out;              // [W * B][Hr][D]
+  float* out_m;            // [W * B][Hr] or null
+  float* out_l;            // [W * B][Hr] or null
   int32_t B, Hq, Hkv, num_pages, max_pages, max_ctx;
+  // query rows: R per sequence (row r at position ctx - R + r), Hr = R * Hq
+  // output rows per range (row r, head h at r * Hq + h); this launch computes
+  // rows r0 .. r0 + G / Gq - 1 (Gq = Hq / Hkv query heads per KV head)
+  int32_t R, r0, Gq, Hr;
   int32_t window_tokens;
   float qk_scale;  // sm_scale * log2(e)
 };
@@ -94,7 +99,7 @@ struct PlanArgs {
   float* out;        // rows of empty ranges are written here
   float* out_m;
   float* out_l;
-  int32_t B, W, Hq, Hkv, window_tokens, max_ctx, per_head_target;
+  int32_t B, W, Hr, Hkv, window_tokens, max_ctx, per_head_target;  // Hr: output rows per range
 };
 
 __device__ __forceinline__ void window_pages(const PlanArgs& p, int wb, int& p0, int& p1) {
@@ -189,9 +194,9 @@ __device__ void build_work_list(const PlanArgs& p) {
     if (__syncthreads_count(wb < n && chunks == 0)) {  // identity rows of empty ranges
       for (int r = 0; r < kThreads && t0 + r < n; ++r) {
         if (s_len[r] > 0) continue;
-        const int64_t r0 = static_cast<int64_t>(t0 + r) * p.Hq;
-        for (int i = tid; i < p.Hq * kHeadDim; i += kThreads) p.out[r0 * kHeadDim + i] = 0.0f;
-        for (int i = tid; i < p.Hq; i += kThreads) {
+        const int64_t r0 = static_cast<int64_t>(t0 + r) * p.Hr;
+        for (int i = tid; i < p.Hr * kHeadDim; i += kThreads) p.out[r0 * kHeadDim + i] = 0.0f;
+        for (int i = tid; i < p.Hr; i += kThreads) {
           if (p.out_m) p.out_m[r0 + i] = -INFINITY;
           if (p.out_l) p.out_l[r0 + i] = 0.0f;
         }
@@ -302,7 +307,8 @@ __device__ __forceinline__ void lds_wave_sync() {
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* __restrict__ q,
                                                                QPrep<G>* __restrict__ out, int32_t Hq,
-                                                               int32_t Hkv, float qk_scale, PlanArgs plan) {
+                                                               int32_t Hkv, float qk_scale, PlanArgs plan,
+                                                               int32_t R, int32_t r0, int32_t Gq) {
   if (blockIdx.x == gridDim.x - 1) {
     build_work_list(plan);
     return;
@@ -312,8 +318,12 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
   const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   QPrep<G>& P = out[blockIdx.x];
-  const uint16_t* qsrc = q + (static_cast<int64_t>(b) * Hq + g * G) * kHeadDim;
-  for (int i = tid; i < G * kHeadDim; i += kThreads) qf[i / kHeadDim][i % kHeadDim] = bf16_to_f32(qsrc[i]);
+  // row h of the group: query row r0 + h / Gq (clamped: rows past R are computed, never written), head g Gq + h % Gq
+  for (int i = tid; i < G * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim, r = min(r0 + h / Gq, R - 1);
+    const int64_t row = (static_cast<int64_t>(b) * R + r) * Hq + g * Gq + h % Gq;
+    qf[h][i % kHeadDim] = bf16_to_f32(q[row * kHeadDim + i % kHeadDim]);
+  }
   __syncthreads();
   for (int h = wave; h < G; h += kWaves) {
     float mx = 0.0f;
@@ -368,13 +378,18 @@ struct __align__(16) DecodeSmem {
 };
 
 // Combines the per-wave states in LDS (max in log2 units, sum, normalised
-// output) into rows row0 .. row0 + G - 1 of dst: the output (max in natural
-// log) when final, else a partial state (max in log2 units).
+// output) into the group's rows of dst: row h of the group is output row
+// rowbase + (r0 + h / Gq) * Hq + g * Gq + h % Gq (rows past R are dropped):
+// the output (max in natural log) when final, else a partial state (max in
+// log2 units).
 template <int G>
-__device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, int64_t row0, bool final,
-                                           float* out_m, float* out_l, float* pm, float* pl) {
+__device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, int64_t rowbase, const DecodeArgs& a,
+                                           int g, bool final) {
   for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads) {
     const int h = i / kHeadDim, d = i % kHeadDim;
+    const int r = a.r0 + h / a.Gq;
+    if (r >= a.R) continue;
+    const int64_t row = rowbase + static_cast<int64_t>(r) * a.Hq + g * a.Gq + h % a.Gq;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
@@ -390,14 +405,14 @@ __device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, 
         }
       }
     }
-    dst[(row0 + h) * kHeadDim + d] = L > 0.0f ? acc / L : 0.0f;
+    dst[row * kHeadDim + d] = L > 0.0f ? acc / L : 0.0f;
     if (d == 0) {
       if (final) {
-        if (out_m) out_m[row0 + h] = L > 0.0f ? M * kLn2 : -INFINITY;
-        if (out_l) out_l[row0 + h] = L;
+        if (a.out_m) a.out_m[row] = L > 0.0f ? M * kLn2 : -INFINITY;
+        if (a.out_l) a.out_l[row] = L;
       } else {
-        pm[row0 + h] = L > 0.0f ? M : -INFINITY;
-        pl[row0 + h] = L;
+        a.m[row] = L > 0.0f ? M : -INFINITY;
+        a.l[row] = L;
       }
     }
   }
@@ -425,7 +440,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so page ids load as scalars
-  const int64_t out_row = static_cast<int64_t>(item) * a.Hq + g * G;  // first partial row of this group
 
   int ctx = a.ctx[b];
   ctx = max(0, min(ctx, a.max_ctx));
@@ -434,6 +448,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     t0 = win * a.window_tokens;
     t1 = min(ctx, t0 + a.window_tokens);
   }
+
+  // last token + 1 that each row of the group sees: row r sits at ctx - R + r
+  int lim[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    lim[h] = __builtin_amdgcn_readfirstlane(min(t1, ctx - (a.R - 1 - (a.r0 + h / a.Gq))));
 
   const QPrep<G>* QP = qprep + __builtin_amdgcn_readfirstlane(b * a.Hkv + g);
   float m_run[G], s_max[G], l_lane[G], o[G][4];
@@ -538,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int h = 0; h < G; ++h) {
       // additive mask: written as a select, the compiler turns the whole key
       // phase into a branch on the token's validity
-      s[h] = fmaf(logit[h], qp->kscale[h], tmask);
+      s[h] = fmaf(logit[h], qp->kscale[h], tok < lim[h] ? tmask : -INFINITY);
       s_max[h] = fmaxf(s_max[h], s[h]);
       raise |= s[h] > m_run[h] + kSlack;
     }
@@ -662,25 +682,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   // A range of a single item writes its output rows directly; otherwise the
   // item writes its partial state for the fold kernel.
   const bool single = nchunks == 1;
-  const int64_t final_row = static_cast<int64_t>(it.x) * a.Hq + g * G;
-  fold_waves<G>(sm, single ? a.out : a.o, single ? final_row : out_row, single, a.out_m, a.out_l, a.m, a.l);
+  fold_waves<G>(sm, single ? a.out : a.o, static_cast<int64_t>(single ? it.x : item) * a.Hr, a, g, single);
 }
 
 constexpr int kFoldWaves = 16;
 
-// Folds the partial states of each output row (window, sequence, query head)
-// whose range has two or more items: items first[wb] .. first[wb] + count[wb] - 1,
-// maxima in log2 units.  Wave w takes every 16th item with a running max
-// (lane = 4 channels); the 16 wave states meet in LDS.
+// Folds the partial states of each output row (window, sequence, query row,
+// query head) whose range has two or more items: items first[wb] .. first[wb]
+// + count[wb] - 1, maxima in log2 units.  Workgroup x folds row (x / (Rp Hq))
+// * Hr + (r0 + x % (Rp Hq) / Hq) * Hq + x % Hq: the rows r0 .. r0 + Rp - 1 of
+// this launch.  Wave w takes every 16th item with a running max (lane = 4
+// channels); the 16 wave states meet in LDS.
 __global__ __launch_bounds__(64 * kFoldWaves) void decode_fold_kernel(const float* __restrict__ po,
                                                                      const float* __restrict__ pm,
                                                                      const float* __restrict__ pl,
                                                                      const int32_t* __restrict__ first,
                                                                      const int32_t* __restrict__ count,
+                                                                     int32_t Hr, int32_t r0, int32_t Rp,
                                                                      int32_t Hq, float* out, float* out_m,
                                                                      float* out_l) {
-  const int r = blockIdx.x;  // (window * B + sequence) * Hq + query head
-  const int wb = r / Hq, hq = r % Hq;
+  const int x = blockIdx.x;
+  const int wb = x / (Rp * Hq);
+  const int rr = (r0 + (x % (Rp * Hq)) / Hq) * Hq + x % Hq;  // row within the range
+  const int64_t r = static_cast<int64_t>(wb) * Hr + rr;       // output row
   const int n = count[wb];
   if (n < 2) return;  // written by the decode kernel or the planning step
   const int c0 = first[wb];
@@ -691,7 +715,7 @@ __global__ __launch_bounds__(64 * kFoldWaves) void decode_fold_kernel(const floa
   float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int c = wave; c < n; c += kFoldWaves) {
-    const int64_t i = static_cast<int64_t>(c0 + c) * Hq + hq;
+    const int64_t i = static_cast<int64_t>(c0 + c) * Hr + rr;
     const float mi = pm[i], li = pl[i];
     const float4_t oi = reinterpret_cast<const float4_t*>(po + i * kHeadDim)[lane];
     const float Mn = li > 0.0f ? fmaxf(Mr, mi) : Mr;
@@ -736,7 +760,7 @@ hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, const PlanArgs& pla
                            hipStream_t s) {
   QPrep<G>* qp = static_cast<QPrep<G>*>(qprep);
   hipLaunchKernelGGL(decode_qprep_kernel<G>, dim3(a.B * a.Hkv + 1), dim3(kThreads), 0, s, a.q, qp, a.Hq, a.Hkv,
-                     a.qk_scale, plan);
+                     a.qk_scale, plan, a.R, a.r0, a.Gq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_begin(F4KV_KERNEL_DECODE, s);
@@ -785,36 +809,48 @@ size_t qprep_bytes(int G, int64_t items) {
   }
 }
 
+// Rows per launch: the kernel's row group is G = Gq * rows (query heads per
+// KV head times query rows), at most 8; more rows take several launches over
+// the same pages.
+int rows_per_launch(int32_t R, int32_t Gq) { return std::max(1, std::min<int32_t>(R, 8 / Gq)); }
+
+int group_size(int32_t R, int32_t Gq) {
+  const int g = rows_per_launch(R, Gq) * Gq;
+  return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8;
+}
+
 }  // namespace
 
-DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
+DecodePlan plan_decode(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
                        int32_t window_tokens) {
   (void)max_ctx;
   (void)window_tokens;
   DecodePlan p;
+  const int G = group_size(R, Hq / Hkv);
   // all chunks of all KV heads fill one resident wave of workgroups
-  const int64_t target_wgs = resident_workgroups(Hq / Hkv);
+  const int64_t target_wgs = resident_workgroups(G);
   p.per_head_target = static_cast<int32_t>(std::max<int64_t>(1, target_wgs / Hkv));
   const int64_t wb = static_cast<int64_t>(num_windows) * B;
   p.max_items = static_cast<int32_t>(wb + p.per_head_target + 1);
+  const int64_t Hr = static_cast<int64_t>(R) * Hq;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   p.part_o_offset = off;
-  off = align(off + static_cast<size_t>(p.max_items) * Hq * kHeadDim * sizeof(float));
+  off = align(off + static_cast<size_t>(p.max_items) * Hr * kHeadDim * sizeof(float));
   p.part_ml_offset = off;
-  off = align(off + static_cast<size_t>(p.max_items) * Hq * 2 * sizeof(float));
+  off = align(off + static_cast<size_t>(p.max_items) * Hr * 2 * sizeof(float));
   p.items_offset = off;
   off = align(off + static_cast<size_t>(p.max_items) * sizeof(int4));
   p.count_offset = off;  // first [W * B], count [W * B], n_items
   off = align(off + static_cast<size_t>(wb) * 2 * sizeof(int32_t) + sizeof(int32_t));
   p.qprep_offset = off;
-  off = align(off + qprep_bytes(Hq / Hkv, static_cast<int64_t>(B) * Hkv));
+  off = align(off + qprep_bytes(G, static_cast<int64_t>(B) * Hkv));
   p.ws_bytes = off;
   return p;
 }
 
 hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* pt, const int32_t* ctx,
-                         int32_t B, int32_t Hq, int32_t max_pages, int32_t max_ctx, int32_t num_windows,
+                         int32_t B, int32_t R, int32_t Hq, int32_t max_pages, int32_t max_ctx, int32_t num_windows,
                          int32_t window_tokens, float sm_scale, float* out, float* out_m, float* out_l,
                          void* ws, const DecodePlan& plan, hipStream_t s) {
   if (B == 0) return hipSuccess;
@@ -836,9 +872,12 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
   a.max_ctx = max_ctx;
   a.window_tokens = window_tokens;
   a.qk_scale = sm_scale * kLog2e;
+  a.R = R;
+  a.Gq = Hq / a.Hkv;
+  a.Hr = R * Hq;
   a.o = reinterpret_cast<float*>(base + plan.part_o_offset);
   a.m = reinterpret_cast<float*>(base + plan.part_ml_offset);
-  a.l = a.m + static_cast<size_t>(plan.max_items) * Hq;
+  a.l = a.m + static_cast<size_t>(plan.max_items) * a.Hr;
   int4* items = reinterpret_cast<int4*>(base + plan.items_offset);
   int32_t* first = reinterpret_cast<int32_t*>(base + plan.count_offset);
   int32_t* count = first + wb;
@@ -860,29 +899,36 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
   pa.out_l = out_l;
   pa.B = B;
   pa.W = num_windows;
-  pa.Hq = Hq;
+  pa.Hr = a.Hr;
   pa.Hkv = a.Hkv;
   pa.window_tokens = window_tokens;
   pa.max_ctx = max_ctx;
   pa.per_head_target = plan.per_head_target;
   void* qprep = base + plan.qprep_offset;
-  const int G = Hq / a.Hkv;
-  hipError_t e;
+  const int G = group_size(R, a.Gq);
+  const int Rp = rows_per_launch(R, a.Gq);
   const bool vt = c.v_scale_per_token != 0;
-  switch (G) {
-    case 1: e = vt ? launch_decode_g<1, true>(a, qprep, pa, plan.max_items, s)
-                   : launch_decode_g<1, false>(a, qprep, pa, plan.max_items, s); break;
-    case 2: e = vt ? launch_decode_g<2, true>(a, qprep, pa, plan.max_items, s)
-                   : launch_decode_g<2, false>(a, qprep, pa, plan.max_items, s); break;
-    case 4: e = vt ? launch_decode_g<4, true>(a, qprep, pa, plan.max_items, s)
-                   : launch_decode_g<4, false>(a, qprep, pa, plan.max_items, s); break;
-    default: e = vt ? launch_decode_g<8, true>(a, qprep, pa, plan.max_items, s)
-                    : launch_decode_g<8, false>(a, qprep, pa, plan.max_items, s); break;
+  for (int r0 = 0; r0 < R; r0 += Rp) {
+    a.r0 = r0;
+    hipError_t e;
+    switch (G) {
+      case 1: e = vt ? launch_decode_g<1, true>(a, qprep, pa, plan.max_items, s)
+                     : launch_decode_g<1, false>(a, qprep, pa, plan.max_items, s); break;
+      case 2: e = vt ? launch_decode_g<2, true>(a, qprep, pa, plan.max_items, s)
+                     : launch_decode_g<2, false>(a, qprep, pa, plan.max_items, s); break;
+      case 4: e = vt ? launch_decode_g<4, true>(a, qprep, pa, plan.max_items, s)
+                     : launch_decode_g<4, false>(a, qprep, pa, plan.max_items, s); break;
+      default: e = vt ? launch_decode_g<8, true>(a, qprep, pa, plan.max_items, s)
+                      : launch_decode_g<8, false>(a, qprep, pa, plan.max_items, s); break;
+    }
+    if (e != hipSuccess) return e;
+    const int rows = std::min(Rp, R - r0);
+    hipLaunchKernelGGL(decode_fold_kernel, dim3(static_cast<unsigned>(wb * rows * Hq)), dim3(64 * kFoldWaves), 0, s,
+                       a.o, a.m, a.l, first, count, a.Hr, r0, rows, Hq, out, out_m, out_l);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_fold_kernel, dim3(static_cast<unsigned>(wb * Hq)), dim3(64 * kFoldWaves), 0, s, a.o,
-                     a.m, a.l, first, count, Hq, out, out_m, out_l);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace f4kv

@@ -74,11 +74,12 @@ struct DecodePlan {
   size_t ws_bytes;           // workspace the call needs
 };
 
-DecodePlan plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx,
+// R query rows per sequence (row r at position ctx - R + r); R == 1 is plain decode.
+DecodePlan plan_decode(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx,
                        int32_t num_windows, int32_t window_tokens);
 
 hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
-                         const int32_t* ctx, int32_t B, int32_t Hq, int32_t max_pages,
+                         const int32_t* ctx, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
                          int32_t max_ctx, int32_t num_windows, int32_t window_tokens,
                          float sm_scale, float* out, float* out_m, float* out_l,
                          void* ws, const DecodePlan& plan, hipStream_t s);

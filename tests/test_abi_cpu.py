@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +140,20 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=16, ws_bytes=need - 1) == 3
     assert "workspace" in _err(lib)
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=None, ws_bytes=need) == 3
+
+
+def test_decode_rows_argument_checks(lib):
+    c = _cache()
+    d = lib.paged_attn_decode_rows_f4
+    args = lambda R: (C.byref(c), 16, 16, 16, 1, R, 16, 64, 4096, 1, 0, 0.0625, 16, None, None, None, 0, None)
+    assert d(*args(0)) == 1 and "rows" in _err(lib)
+    assert d(*args(9)) == 1 and "rows" in _err(lib)
+    assert d(*args(2)) == 3 and "workspace" in _err(lib)
+    # more rows need more workspace; R == 1 is plain decode's size
+    one = lib.paged_attn_decode_rows_f4_workspace_size(3, 1, 16, 4, 256, 1 << 18, 1, 0)
+    assert one == lib.paged_attn_decode_f4_workspace_size(3, 16, 4, 256, 1 << 18, 1, 0)
+    assert lib.paged_attn_decode_rows_f4_workspace_size(3, 8, 16, 4, 256, 1 << 18, 1, 0) > one
+    assert lib.paged_attn_decode_rows_f4_workspace_size(3, 9, 16, 4, 256, 1 << 18, 1, 0) == 0
 
 
 def test_gather_argument_checks(lib):

@@ -1,0 +1,67 @@
+"""paged_attn_decode_rows_f4 (R query rows per sequence, as a speculative
+verification round takes them) on the GPU vs the oracle (max |delta| <= 2e-3 x
+output RMS)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_kv_amd as f4
+import synth
+from oracle import attention as oatt
+from gpu_cases import PagedSet, assert_attention_close, assert_states_close, bf16_tensor, bf16_values
+
+pytestmark = pytest.mark.gpu
+SM = 1.0 / 16.0
+
+
+def _q(B, R, Hq, seed):
+    g = synth.rng(900 + seed, 1)
+    bits = synth.f32_to_bf16_bits(synth.normal_f32(g, (B, R, Hq, 256)))
+    return bits, bf16_values(bits)
+
+
+def _run(ps, R, Hq, seed, W=1, wt=0):
+    bits, qv = _q(len(ps.lengths), R, Hq, seed)
+    out, m, l = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), ps.gpu_lengths(),
+                                             max(ps.lengths), SM, num_windows=W, window_tokens=wt)
+    torch.cuda.synchronize()
+    ro, rm, rl = oatt.decode_rows(ps.oc, qv, ps.pt, ps.lengths, SM, window_tokens=wt, num_windows=W)
+    return (out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()), (ro, rm, rl), bits
+
+
+@pytest.mark.parametrize("R", [2, 3, 8])
+def test_rows_group_of_four(R):
+    # 4 query heads per KV head: 2 rows per pass over the pages, so 3 and 8 rows take several passes
+    ps = PagedSet([700, 130, 64 * 20 + 5], Hkv=4, seed=900 + R)
+    (o, m, l), (ro, rm, rl), _ = _run(ps, R, 16, R)
+    assert_attention_close(o, ro, f"R={R}")
+    assert_states_close(m, l, rm, rl, f"R={R}")
+
+
+@pytest.mark.parametrize("G,Hkv,R", [(1, 2, 8), (2, 2, 3), (8, 2, 2)])
+def test_rows_other_groups(G, Hkv, R):
+    ps = PagedSet([300, 1024], Hkv=Hkv, seed=910 + G, v_per_token=(G == 2))
+    (o, m, l), (ro, rm, rl), _ = _run(ps, R, G * Hkv, 10 + G)
+    assert_attention_close(o, ro, f"G={G} R={R}")
+    assert_states_close(m, l, rm, rl, f"G={G} R={R}")
+
+
+def test_rows_short_contexts_and_windows():
+    # contexts shorter than R: the leading rows see no token and are the merge identity
+    ps = PagedSet([3, 1, 1500], Hkv=4, seed=920)
+    (o, m, l), (ro, rm, rl), _ = _run(ps, 4, 16, 20, W=3, wt=640)
+    assert np.all(np.isneginf(m[:, 1, :3])) and np.all(l[:, 1, :3] == 0) and not o[:, 1, :3].any()
+    assert_attention_close(o, ro, "short contexts, windows")
+    assert_states_close(m, l, rm, rl, "short contexts, windows")
+
+
+def test_one_row_is_plain_decode_and_last_row_matches_decode():
+    ps = PagedSet([2000, 77], Hkv=4, seed=930)
+    bits, _ = _q(2, 3, 16, 30)
+    pt, lens = ps.gpu_page_table(), ps.gpu_lengths()
+    one = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 2:3].copy()), pt, lens, 2000, SM)[0]
+    dec = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits[:, 2].copy()), pt, lens, 2000, SM)[0]
+    three = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), pt, lens, 2000, SM)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(one[:, :, 0], dec)
+    assert torch.allclose(three[:, :, 2], dec, rtol=0, atol=1e-5 * float(dec.abs().max()))
