@@ -572,7 +572,7 @@ def main():
                    "ms_per_step_eager": r["ms_per_step_eager"]},
         "roofline": {"bound": "hbm", "achieved": r["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["decode_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "decode_kernel<4> (split-K attention kernel of paged_attn_decode_f4)",
+                     "kernel": "decode_kernel<4, false> (split-K attention kernel of paged_attn_decode_f4)",
                      "bytes_per_launch": r["decode_bytes_per_call"], "launch_ms_avg": r["decode_kernel_ms_avg"],
                      "whole_call_ms_avg": r["decode_call_ms_avg"], "whole_call_gbs": r["decode_call_gbs"]},
         "cpu_baseline": cpu,

@@ -1,8 +1,10 @@
 """Summaries of rocprofv3 CSV output for this library's kernels.
 
-    python -m long_context_attention_kv_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..."
+    python -m long_context_attention_kv_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..." [--timed NAME:FIRST:COUNT]
         per-kernel time table (the library's kernels first) from a
-        ``rocprofv3 --kernel-trace --stats -f csv`` run.
+        ``rocprofv3 --kernel-trace --stats -f csv`` run; --timed adds the
+        average of dispatches FIRST .. FIRST + COUNT - 1 of kernel NAME from
+        the run's kernel trace (e.g. the launches a benchmark timed).
 
     python -m long_context_attention_kv_amd.prof_summary traffic --fetch CSV --write CSV \\
             --copy-bytes N --kernel NAME --source FILE --cmd-fetch "..." --cmd-write "..."
@@ -31,7 +33,21 @@ def _short(name: str) -> str:
     return name.replace("void ", "").strip()
 
 
-def stats_table(path: str, cmd: str) -> str:
+def timed_window(trace_path: str, spec: str) -> str:
+    """Average duration of dispatches FIRST .. FIRST + COUNT - 1 (in start order)
+    of one kernel, from a kernel-trace CSV; spec = "NAME:FIRST:COUNT"."""
+    name, first, count = spec.rsplit(":", 2)
+    first, count = int(first), int(count)
+    rows = [r for r in csv.DictReader(open(trace_path)) if name in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[first:first + count]]
+    if len(d) != count:
+        raise SystemExit(f"only {len(d)} dispatches of {name!r} in that window")
+    return (f"`{name}`, dispatches {first + 1} .. {first + count} of {len(rows)} in start order (the timed launches): "
+            f"average {statistics.mean(d):.1f} us, min {min(d):.1f}, max {max(d):.1f}.")
+
+
+def stats_table(path: str, cmd: str, timed: str = "") -> str:
     rows = list(csv.DictReader(open(path)))
     lines = ["# Kernel time summary", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | share of GPU time |",
@@ -44,6 +60,9 @@ def stats_table(path: str, cmd: str) -> str:
                      f"{float(r['Percentage']):.2f}% |")
     if len(other) > 5:
         lines.append(f"| ({len(other) - 5} more kernels of the harness) | | | | | |")
+    if timed:
+        trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
+        lines += ["", timed_window(trace, timed)]
     return "\n".join(lines) + "\n"
 
 
@@ -118,6 +137,7 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--cmd", required=True)
+    s.add_argument("--timed", default="", help="NAME:FIRST:COUNT: also average these dispatches of NAME")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -127,7 +147,7 @@ def main(argv=None):
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     a = ap.parse_args(argv)
-    sys.stdout.write(stats_table(a.csv, a.cmd) if a.what == "stats" else traffic(a))
+    sys.stdout.write(stats_table(a.csv, a.cmd, a.timed) if a.what == "stats" else traffic(a))
 
 
 if __name__ == "__main__":
