@@ -21,6 +21,7 @@ import torch
 import long_context_attention_kv_amd as f4
 import synth
 from oracle import attention as oatt
+from oracle import f4 as of4
 from oracle import yarn as oyarn
 from gpu_cases import assert_attention_close, bf16_tensor, bf16_values
 
@@ -67,8 +68,9 @@ def draw_block(config, seq, head, j, n, kind, chans):
 class Layer:
     """One layer of B sequences in one pool; filled on the GPU block by block."""
 
-    def __init__(self, config, lengths, factor, outliers, with_query=True):
+    def __init__(self, config, lengths, factor, outliers, with_query=True, v_per_token=False, rows=1):
         self.config, self.lengths = config, [int(n) for n in lengths]
+        self.v_per_token, self.rows = v_per_token, rows
         self.spec = spec_for(factor)
         self.chans = outlier_channels(config, outliers)
         pages = [(n + PAGE - 1) // PAGE for n in self.lengths]
@@ -76,7 +78,7 @@ class Layer:
         self.max_pages = max(pages)
         perm = synth.page_permutation(synth.rng(config, 53), self.num_pages)
         self.pt = synth.page_table_for(self.lengths, perm, self.max_pages)
-        self.cache = f4.F4Cache(self.num_pages, HKV, D)
+        self.cache = f4.F4Cache(self.num_pages, HKV, D, v_scale_per_token=v_per_token)
         yp = gpu_params(self.spec)
         for b, n in enumerate(self.lengths):
             for j, t0 in enumerate(range(0, n, BLK)):
@@ -91,13 +93,22 @@ class Layer:
                 slots = (self.pt[b, t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
                 f4.kv_cache_write_f4(self.cache, kt, torch.from_numpy(v).cuda(), torch.from_numpy(slots).cuda())
         torch.cuda.synchronize()
-        if with_query:
+        if with_query and rows == 1:
             # one decode query per sequence, rotated at position ctx - 1
             self.qbits = np.stack([synth.f32_to_bf16_bits(synth.normal_f32(synth.rng(config, 52, b), (HQ, D)))
                                    for b in range(len(self.lengths))])
             pos = torch.tensor([n - 1 for n in self.lengths], dtype=torch.int32, device="cuda")
             c, s = f4.yarn_rope_table(yp, pos)
             self.q = f4.yarn_rope_apply(c, s, bf16_tensor(self.qbits))
+        elif with_query:
+            # R query rows per sequence, row r rotated at position ctx - R + r
+            R = rows
+            self.qbits = np.stack([synth.f32_to_bf16_bits(synth.normal_f32(synth.rng(config, 52, b), (R, HQ, D)))
+                                   for b in range(len(self.lengths))])
+            pos = torch.tensor([n - R + r for n in self.lengths for r in range(R)], dtype=torch.int32, device="cuda")
+            c, s = f4.yarn_rope_table(yp, pos)
+            flat = bf16_tensor(self.qbits.reshape(-1, HQ, D))
+            self.q = f4.yarn_rope_apply(c, s, flat).view(len(self.lengths), R, HQ, D)
 
     # ---- oracle side: its own draws, table, rotation, quantiser and attention ----
     def oracle_kv(self, b, h, t_end=None, t_begin=0):
@@ -113,13 +124,22 @@ class Layer:
             kr = oyarn.rope_apply(k[:, None, :], cs, sn, self.spec.rotary_dim)[:, 0].astype(np.float32)
             lo, hi = max(t_begin, t0) - t0, min(n, t0 + nb) - t0
             Ks.append(oatt.dequantize_rows(kr[lo:hi]))
-            Vs.append(oatt.dequantize_rows(v[lo:hi]))
+            if self.v_per_token:
+                Vs.append(of4.dequantize_blocks(*of4.quantize_group(v[lo:hi])))
+            else:
+                Vs.append(oatt.dequantize_rows(v[lo:hi]))
         return np.concatenate(Ks), np.concatenate(Vs)
 
-    def oracle_query(self, b, h):
-        """The 4 query rows of KV head h's group, rotated at ctx - 1 and stored as bf16."""
-        qv = bf16_values(self.qbits[b, h * G:(h + 1) * G])
-        cs, sn = table_f32(self.spec, np.array([self.lengths[b] - 1]))
+    def oracle_query(self, b, h, r=None):
+        """The 4 query heads of KV head h's group (of query row r), rotated at their
+        position (ctx - 1, or ctx - R + r) and stored as bf16."""
+        if r is None:
+            qv = bf16_values(self.qbits[b, h * G:(h + 1) * G])
+            pos = self.lengths[b] - 1
+        else:
+            qv = bf16_values(self.qbits[b, r, h * G:(h + 1) * G])
+            pos = self.lengths[b] - self.rows + r
+        cs, sn = table_f32(self.spec, np.array([pos]))
         qr = oyarn.rope_apply(qv[None], cs, sn, self.spec.rotary_dim)[0]
         return bf16_values(synth.f32_to_bf16_bits(qr.astype(np.float32)))
 
@@ -238,3 +258,51 @@ def test_config3_prefill_2048_at_129024():
             ro, rm, rl = oatt.decode_head_from_values(qv[i, h * G:(h + 1) * G], K[:n], V[:n], SM)
             check_group(out[i, h * G:(h + 1) * G], m[i, h * G:(h + 1) * G], l[i, h * G:(h + 1) * G],
                         (ro[0], rm[0], rl[0]), f"prefill row {i} kv head {h}")
+
+
+# ---- the next rows at the benchmark's shapes --------------------------------
+
+def test_v_per_token_decode_3x262144():
+    print("case: 3 lanes x 262,144 tokens, one V scale per token and head", flush=True)
+    layer = Layer(5, [262144] * 3, 4.0, outliers=True, v_per_token=True)
+    out, m, l = decode_call(layer)
+    for b, h in [(0, 1)]:
+        K, V = layer.oracle_kv(b, h)
+        ref = oatt.decode_head_from_values(layer.oracle_query(b, h), K, V, SM)
+        check_group(out[0, b, h * G:(h + 1) * G], m[0, b, h * G:(h + 1) * G], l[0, b, h * G:(h + 1) * G],
+                    (ref[0][0], ref[1][0], ref[2][0]), f"per-token V, lane {b} kv head {h}")
+
+
+@pytest.mark.parametrize("R", [2, 8])
+def test_rows_decode_3x262144(R):
+    print(f"case: {R} query rows per lane, 3 lanes x 262,144 tokens", flush=True)
+    n = 262144
+    layer = Layer(7, [n] * 3, 4.0, outliers=True, rows=R)
+    ws = torch.empty(max(16, f4.decode_rows_workspace_size(3, R, HQ, HKV, D, n)), dtype=torch.uint8, device="cuda")
+    out, m, l = f4.paged_attn_decode_rows_f4(layer.cache, layer.q, torch.from_numpy(layer.pt).cuda(),
+                                             torch.tensor(layer.lengths, dtype=torch.int32, device="cuda"), n, SM,
+                                             workspace=ws)
+    torch.cuda.synchronize()
+    out, m, l = out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
+    b, h = 2, 3
+    K, V = layer.oracle_kv(b, h)
+    for r in sorted({0, R // 2, R - 1}):
+        c = n - R + r + 1  # tokens row r sees
+        ref = oatt.decode_head_from_values(layer.oracle_query(b, h, r), K[:c], V[:c], SM)
+        check_group(out[0, b, r, h * G:(h + 1) * G], m[0, b, r, h * G:(h + 1) * G], l[0, b, r, h * G:(h + 1) * G],
+                    (ref[0][0], ref[1][0], ref[2][0]), f"{R} rows: row {r} lane {b} kv head {h}")
+
+
+def test_gather_3x262144_bf16():
+    print("case: gather of 3 lanes x 262,144 tokens to bf16 rows", flush=True)
+    n = 262144
+    layer = Layer(6, [n] * 3, 4.0, outliers=True, with_query=False)
+    cu = torch.tensor([0, n, 2 * n, 3 * n], dtype=torch.int32, device="cuda")
+    k, v = f4.gather_kv_cache_f4(layer.cache, torch.from_numpy(layer.pt).cuda(), cu, 3 * n)
+    torch.cuda.synchronize()
+    for b, h, t0 in [(0, 0, 0), (1, 2, 131072 + 64 * 7), (2, 3, n - 1000)]:
+        K, V = layer.oracle_kv(b, h, t_begin=t0, t_end=t0 + 1000)
+        rows = slice(b * n + t0, b * n + t0 + 1000)
+        for got, ref in ((k[rows, h], K), (v[rows, h], V)):
+            want = torch.from_numpy(of4.bf16_round(ref).astype(np.float32)).to(torch.bfloat16)
+            assert torch.equal(got.cpu().view(torch.int16), want.view(torch.int16)), (b, h, t0)
