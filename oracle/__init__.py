@@ -17,10 +17,13 @@ f4         the symmetric 4-bit block quantiser ``(nibble - 8) * scale``
 attention  paged gather, exact softmax decode attention, partial states and
            their log-sum-exp fold (FreeToken issue #568, "Proposed solution"
            item 2), and causal chunked prefill.
+fp8        the 8-bit prefill (ignis context-and-speculation page,
+           ``--model-prefill-attention`` row: Q.K^T in INT8, P.V in E4M3) as a
+           model of its rounding steps, E4M3 rounding and the INT8 quantisers.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values
 the pages print, closed forms, invariants or brute force.  The one result with
 no such pin is the end-to-end equivalence of F4 attention to unquantised
 attention: parity unpinned (the pages say it was never measured).
 """
-from . import yarn, f4, attention  # noqa: F401
+from . import yarn, f4, attention, fp8  # noqa: F401
