@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define F4KV_ABI_VERSION 2
+#define F4KV_ABI_VERSION 3
 
 enum {
   F4KV_OK = 0,
@@ -269,6 +269,34 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * paged_attn_prefill_f4_fp8 [IGN --model-prefill-attention: the prompt
+ * attention over a 4-bit-cache chunk in 8 bits, Q.K^T in INT8 and P.V in E4M3]
+ * The computation of paged_attn_prefill_f4 (same arguments, layouts, state
+ * outputs, workspace size and errors) with 8-bit products, for a query row r
+ * at position p over cache tokens [0, p]:
+ *   - q to INT8 with one power-of-two scale per row, sigma = 2^(e - 7) where
+ *     max |q| < 2^e, round half to even, clamped to [-127, 127];
+ *   - each cached key to INT8 with one power-of-two scale per token,
+ *     tau = 2^(E - 4), E = (exponent field of the token's largest fp16 block
+ *     scale) - 14, code * scale / tau rounded half up (within [-128, 112]);
+ *   - x = (Qi . Kt) sigma tau qk in log2 units, qk = fp32(sm_scale log2(e));
+ *   - per 32-token group (half a page) of a row, G = ceil(max x) and the
+ *     weights P8 = e4m3(2^(x - G)) (OCP E4M3, nearest even) carrying 2^G;
+ *   - per 32-token group and 32-channel block, values V8 = e4m3(code * scale
+ *     / 2^F) carrying 2^F, F = (exponent field of the largest V scale) - 19;
+ *   - out = sum P8 2^G V8 2^F / sum 2^x (unquantised denominator).
+ * The result is within a few percent of the exact attention (E4M3 keeps 3
+ * mantissa bits: ~4% of the output RMS on N(0,1) data); it is the faster
+ * choice where that is acceptable.
+ */
+int paged_attn_prefill_f4_fp8(const f4kv_cache* cache, const uint16_t* q,
+                              const float* k_new, const float* v_new,
+                              const int32_t* page_table, int32_t max_pages,
+                              int32_t T, int32_t Hq, int32_t pos0, float sm_scale,
+                              float* out, float* out_m, float* out_l,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * gather_kv_cache_f4 [MRS item 2: the cache's gather path gains an F4 variant]
  * Dequantises the cached keys and values of B sequences into contiguous rows:
  * token i of sequence b, for i < cu_seq_lens[b + 1] - cu_seq_lens[b], becomes
@@ -300,9 +328,10 @@ int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const
  *   kernel  F4KV_KERNEL_DECODE: the split-K attention kernel of
  *           paged_attn_decode_f4 (not its query preparation or fold);
  *           F4KV_KERNEL_PREFILL: the attention kernel of paged_attn_prefill_f4.
+ *           F4KV_KERNEL_PREFILL_FP8: that of paged_attn_prefill_f4_fp8.
  * Timing one kernel from two host threads at once is not supported.
  */
-enum { F4KV_KERNEL_DECODE = 0, F4KV_KERNEL_PREFILL = 1 };
+enum { F4KV_KERNEL_DECODE = 0, F4KV_KERNEL_PREFILL = 1, F4KV_KERNEL_PREFILL_FP8 = 2 };
 int f4kv_timing_start(int32_t kernel, int32_t max_launches);
 int f4kv_timing_stop(int32_t kernel, double* total_ms, int64_t* launches);
 

@@ -10,6 +10,7 @@ library is not built the calls raise; there is no other code path.
 from ._binding import (  # noqa: F401
     KERNEL_DECODE,
     KERNEL_PREFILL,
+    KERNEL_PREFILL_FP8,
     F4KVError,
     F4Cache,
     KernelTimer,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     paged_attn_decode_f4,
     paged_attn_decode_rows_f4,
     paged_attn_prefill_f4,
+    paged_attn_prefill_f4_fp8,
     prefill_workspace_size,
     yarn_rope_apply,
     yarn_rope_table,
@@ -45,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "lse_merge",
     "paged_attn_prefill_f4_workspace_size",
     "paged_attn_prefill_f4",
+    "paged_attn_prefill_f4_fp8",
     "gather_kv_cache_f4",
     "f4kv_timing_start",
     "f4kv_timing_stop",

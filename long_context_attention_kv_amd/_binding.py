@@ -55,12 +55,14 @@ _SIGS = {
     "paged_attn_prefill_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I]),
     "paged_attn_prefill_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                                         _P, _P, _P, _P, C.c_size_t, _P]),
+    "paged_attn_prefill_f4_fp8": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
+                                            _P, _P, _P, _P, C.c_size_t, _P]),
     "gather_kv_cache_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _I, _I, _I, _P, _P, _I, _P]),
     "f4kv_timing_start": (C.c_int, [_I, _I]),
     "f4kv_timing_stop": (C.c_int, [_I, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
 
-KERNEL_DECODE, KERNEL_PREFILL = 0, 1
+KERNEL_DECODE, KERNEL_PREFILL, KERNEL_PREFILL_FP8 = 0, 1, 2
 
 
 def library_path() -> str:
@@ -327,6 +329,18 @@ def prefill_workspace_size(T, Hq, num_kv_heads, head_dim, pos0) -> int:
 def paged_attn_prefill_f4(cache: F4Cache, q, k_new, v_new, page_table, pos0: int, sm_scale: float, out=None,
                           out_m=None, out_l=None, workspace=None):
     """Write the chunk's K/V (if given) and attend causally; returns (out [T, Hq, D], m [T, Hq], l [T, Hq])."""
+    return _prefill("paged_attn_prefill_f4", cache, q, k_new, v_new, page_table, pos0, sm_scale, out, out_m, out_l,
+                    workspace)
+
+
+def paged_attn_prefill_f4_fp8(cache: F4Cache, q, k_new, v_new, page_table, pos0: int, sm_scale: float, out=None,
+                              out_m=None, out_l=None, workspace=None):
+    """paged_attn_prefill_f4 with 8-bit products (Q.K^T in INT8, P.V in E4M3); same arguments and results."""
+    return _prefill("paged_attn_prefill_f4_fp8", cache, q, k_new, v_new, page_table, pos0, sm_scale, out, out_m,
+                    out_l, workspace)
+
+
+def _prefill(name, cache: F4Cache, q, k_new, v_new, page_table, pos0, sm_scale, out, out_m, out_l, workspace):
     lib = load_library()
     T, Hq, D = q.shape
     _need(q, torch.bfloat16, (T, Hq, D), "q")
@@ -346,10 +360,9 @@ def paged_attn_prefill_f4(cache: F4Cache, q, k_new, v_new, page_table, pos0: int
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     c = cache._c()
-    _check("paged_attn_prefill_f4",
-           lib.paged_attn_prefill_f4(C.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(page_table),
-                                     page_table.numel(), T, Hq, int(pos0), float(sm_scale), _ptr(out), _ptr(out_m),
-                                     _ptr(out_l), _ptr(workspace), ws_bytes, _stream()))
+    _check(name, getattr(lib, name)(C.byref(c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(page_table),
+                                    page_table.numel(), T, Hq, int(pos0), float(sm_scale), _ptr(out), _ptr(out_m),
+                                    _ptr(out_l), _ptr(workspace), ws_bytes, _stream()))
     return out, out_m, out_l
 
 

@@ -23,7 +23,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # Per-file flags.  The prefill kernel rescales its MFMA accumulators with VALU
 # multiplies; MFMA in the VGPR form keeps them in VGPRs instead of copying them
 # between AGPRs and VGPRs every iteration.
-FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "prefill_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

@@ -247,11 +247,14 @@ size_t paged_attn_prefill_f4_workspace_size(int32_t T, int32_t Hq, int32_t num_k
   return f4kv::plan_prefill(T, Hq, num_kv_heads, pos0).ws_bytes;
 }
 
-int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q, const float* k_new, const float* v_new,
-                          const int32_t* page_table, int32_t max_pages, int32_t T, int32_t Hq, int32_t pos0,
-                          float sm_scale, float* out, float* out_m, float* out_l, void* workspace,
-                          size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "paged_attn_prefill_f4";
+}  // extern "C"
+
+namespace {
+// Both prefill entry points: validation, the in-call cache write, the launch.
+int prefill_common(const char* fn, bool fp8, const f4kv_cache* cache, const uint16_t* q, const float* k_new,
+                   const float* v_new, const int32_t* page_table, int32_t max_pages, int32_t T, int32_t Hq,
+                   int32_t pos0, float sm_scale, float* out, float* out_m, float* out_l, void* workspace,
+                   size_t ws_bytes, hipStream_t stream) {
   if (int r = check_cache(cache, fn)) return r;
   const int32_t Hkv = cache->num_kv_heads;
   if (T < 0 || Hq <= 0 || pos0 < 0 || max_pages <= 0)
@@ -281,9 +284,32 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q, const floa
     hipError_t e = f4kv::launch_kv_write_paged(*cache, k_new, v_new, page_table, pos0, T, stream);
     if (e != hipSuccess) return launched(e, fn);
   }
+  if (fp8)
+    return launched(f4kv::launch_prefill_fp8(*cache, q, page_table, max_pages, T, Hq, pos0, sm_scale, out, out_m,
+                                             out_l, workspace, plan, stream),
+                    fn);
   return launched(f4kv::launch_prefill(*cache, q, page_table, max_pages, T, Hq, pos0, sm_scale, out, out_m, out_l,
                                        workspace, plan, stream),
                   fn);
+}
+}  // namespace
+
+extern "C" {
+
+int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q, const float* k_new, const float* v_new,
+                          const int32_t* page_table, int32_t max_pages, int32_t T, int32_t Hq, int32_t pos0,
+                          float sm_scale, float* out, float* out_m, float* out_l, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  return prefill_common("paged_attn_prefill_f4", false, cache, q, k_new, v_new, page_table, max_pages, T, Hq, pos0,
+                        sm_scale, out, out_m, out_l, workspace, ws_bytes, stream);
+}
+
+int paged_attn_prefill_f4_fp8(const f4kv_cache* cache, const uint16_t* q, const float* k_new, const float* v_new,
+                              const int32_t* page_table, int32_t max_pages, int32_t T, int32_t Hq, int32_t pos0,
+                              float sm_scale, float* out, float* out_m, float* out_l, void* workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+  return prefill_common("paged_attn_prefill_f4_fp8", true, cache, q, k_new, v_new, page_table, max_pages, T, Hq,
+                        pos0, sm_scale, out, out_m, out_l, workspace, ws_bytes, stream);
 }
 
 int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const int32_t* cu_seq_lens, int32_t B,
@@ -311,7 +337,7 @@ int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const
 
 int f4kv_timing_start(int32_t kernel, int32_t max_launches) {
   const char* fn = "f4kv_timing_start";
-  if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL)
+  if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL && kernel != F4KV_KERNEL_PREFILL_FP8)
     return fail(F4KV_ERR_INVALID, "%s: unknown kernel %d", fn, kernel);
   if (max_launches <= 0 || max_launches > (1 << 20))
     return fail(F4KV_ERR_INVALID, "%s: max_launches must be in [1, 2^20], got %d", fn, max_launches);
@@ -322,7 +348,7 @@ int f4kv_timing_start(int32_t kernel, int32_t max_launches) {
 
 int f4kv_timing_stop(int32_t kernel, double* total_ms, int64_t* launches) {
   const char* fn = "f4kv_timing_stop";
-  if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL)
+  if (kernel != F4KV_KERNEL_DECODE && kernel != F4KV_KERNEL_PREFILL && kernel != F4KV_KERNEL_PREFILL_FP8)
     return fail(F4KV_ERR_INVALID, "%s: unknown kernel %d", fn, kernel);
   hipError_t e = f4kv::timing_stop(kernel, total_ms, launches);
   if (e != hipSuccess) return fail(F4KV_ERR_LAUNCH, "%s: reading the events failed: %s", fn, hipGetErrorString(e));

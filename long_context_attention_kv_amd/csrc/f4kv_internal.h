@@ -97,4 +97,10 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
                           float sm_scale, float* out, float* out_m, float* out_l,
                           void* ws, const PrefillPlan& plan, hipStream_t s);
 
+// The same chunk with 8-bit products (Q.K^T in INT8, P.V in E4M3); same plan.
+hipError_t launch_prefill_fp8(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
+                              int32_t max_pages, int32_t T, int32_t Hq, int32_t pos0,
+                              float sm_scale, float* out, float* out_m, float* out_l,
+                              void* ws, const PrefillPlan& plan, hipStream_t s);
+
 }  // namespace f4kv

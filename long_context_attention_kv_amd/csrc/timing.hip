@@ -17,7 +17,7 @@ struct Timer {
   bool open = false;  // a begin without its end yet
 };
 
-Timer g_timers[2];
+Timer g_timers[3];
 
 void destroy_events(Timer& t) {
   for (hipEvent_t e : t.start) (void)hipEventDestroy(e);

@@ -129,11 +129,13 @@ def logit_scale_log2(sm_scale: float) -> float:
 # ---- the model ----------------------------------------------------------------
 
 def group_weights(x: np.ndarray):
-    """Step 5 for one group's scores x (log2 units, at least one finite):
-    (P8, G) with G = ceil(max x) and P8 = e4m3(2^(x - G)): the largest weight
-    before rounding lies in (1/2, 1]."""
-    G = math.ceil(float(np.max(x)))
-    return e4m3_round(np.exp2(np.asarray(x, dtype=np.float64) - G)), G
+    """Step 5 for groups of scores x [..., 32] (log2 units, -inf for keys not
+    seen, at least one finite per group): (P8 [..., 32], G [...]) with
+    G = ceil(max x) and P8 = e4m3(2^(x - G)): the largest weight before
+    rounding lies in (1/2, 1]."""
+    x = np.asarray(x, dtype=np.float64)
+    G = np.ceil(x.max(axis=-1))
+    return e4m3_round(np.exp2(x - G[..., None])), G
 
 
 def _page_half_values(cache, page: int, head: int, half: int):
@@ -198,10 +200,11 @@ def prefill(cache, q, page_row, pos0: int, sm_scale: float, rows=None):
                 S = Kt[:n] @ Qi[i, h].astype(np.int64)            # exact integers
                 x = S.astype(np.float64) * sigma[i, h] * tau[:n] * qk
                 M = x.max()
-                w = np.zeros(n)
-                for t0 in range(0, n, GROUP):
-                    p8, G = group_weights(x[t0:t0 + GROUP])
-                    w[t0:t0 + GROUP] = p8 * 2.0 ** (G - M)
+                ng = (n + GROUP - 1) // GROUP
+                xg = np.full(ng * GROUP, -np.inf)
+                xg[:n] = x                                  # groups of 32 keys, the last one padded
+                p8, G = group_weights(xg.reshape(ng, GROUP))
+                w = (p8 * np.exp2(G - M)[:, None]).reshape(-1)[:n]
                 den = np.exp2(x - M).sum()
                 out[i, h] = (w @ Vd[:n]) / den
                 m[i, h] = M * math.log(2.0)

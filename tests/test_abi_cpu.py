@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -179,19 +179,22 @@ def test_merge_and_rope_apply_checks(lib):
     assert lib.yarn_rope_apply(16, 16, 16, 0, 16, 1, 1, 1, 256, 256, None) == 1   # in place, dtypes differ
 
 
-def test_prefill_argument_checks(lib):
+@pytest.mark.parametrize("name", ["paged_attn_prefill_f4", "paged_attn_prefill_f4_fp8"])
+def test_prefill_argument_checks(lib, name):
     c = _cache()
-    f = lambda **kw: lib.paged_attn_prefill_f4(
+    f = lambda **kw: getattr(lib, name)(
         C.byref(c), 16, kw.get("k", 16), kw.get("v", 16), 16, kw.get("mp", 64), kw.get("T", 64), kw.get("Hq", 16),
-        kw.get("pos0", 0), 0.0625, 16, None, None, None, 0, None)
-    assert f(pos0=64 * 64) == 1 and "max_pages" in _err(lib)
+        kw.get("pos0", 0), kw.get("sm", 0.0625), 16, None, None, None, 0, None)
+    assert f(pos0=64 * 64) == 1 and "max_pages" in _err(lib) and name + ":" in _err(lib)
     assert f(k=None) == 1 and "together" in _err(lib)
+    assert f(sm=float("nan")) == 1 and "sm_scale" in _err(lib)
     assert f(Hq=8) == 2
     assert f(T=0) == 0
 
 
 def test_timing_argument_checks(lib):
     assert lib.f4kv_timing_start(7, 16) == 1 and "unknown kernel" in _err(lib)
+    assert lib.f4kv_timing_start(3, 16) == 1 and "unknown kernel" in _err(lib)
     assert lib.f4kv_timing_start(0, 0) == 1 and "max_launches" in _err(lib)
     assert lib.f4kv_timing_start(1, (1 << 20) + 1) == 1
     ms, n = C.c_double(-1.0), C.c_int64(-1)

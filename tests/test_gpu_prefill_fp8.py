@@ -1,0 +1,93 @@
+"""paged_attn_prefill_f4_fp8 on the GPU vs the oracle's 8-bit prefill model
+(max |delta| <= 2e-3 x output RMS), and vs the exact attention within the
+model's error budget."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_kv_amd as f4
+from oracle import attention as oatt
+from oracle import fp8 as ofp8
+from gpu_cases import assert_attention_close, assert_states_close, bf16_tensor, bf16_values, cache_arrays_equal
+from test_gpu_prefill import Chunk, PAGE, SM
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8(ch: Chunk, write=True, qbits=None):
+    kn = torch.from_numpy(ch.k_new).cuda() if write else None
+    vn = torch.from_numpy(ch.v_new).cuda() if write else None
+    qb = ch.qbits if qbits is None else qbits
+    out = f4.paged_attn_prefill_f4_fp8(ch.gc, bf16_tensor(qb), kn, vn, torch.from_numpy(ch.pt).cuda(), ch.pos0, SM)
+    torch.cuda.synchronize()
+    return [x.cpu().numpy() for x in out]
+
+
+def oracle_fp8(ch: Chunk, qbits=None, rows=None):
+    t = np.arange(ch.pos0, ch.pos0 + ch.T)
+    slots = (ch.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+    ch.oc.write(ch.k_new, ch.v_new, slots)
+    qb = ch.qbits if qbits is None else qbits
+    return ofp8.prefill(ch.oc, bf16_values(qb), ch.pt, ch.pos0, SM, rows=rows)
+
+
+@pytest.mark.parametrize("pos0,T", [(0, 1), (0, 64), (100, 37), (64, 130), (1000, 200), (4000, 33)])
+def test_prefill_fp8_small(pos0, T):
+    print(f"prefill_fp8 pos0={pos0} T={T}", flush=True)
+    ch = Chunk(pos0, T, seed=800 + pos0 + T)
+    o, m, l = run_fp8(ch)
+    ro, rm, rl = oracle_fp8(ch)
+    assert cache_arrays_equal(ch.gc, ch.oc) == []
+    assert_attention_close(o, ro, f"prefill_fp8 pos0={pos0} T={T}")
+    assert_states_close(m, l, rm, rl, f"prefill_fp8 pos0={pos0} T={T}")
+
+
+@pytest.mark.parametrize("pos0,T", [(37, 100), (1000, 64)])
+def test_prefill_fp8_v_per_token(pos0, T):
+    print(f"prefill_fp8 v_per_token pos0={pos0} T={T}", flush=True)
+    ch = Chunk(pos0, T, seed=840 + pos0 + T, v_per_token=True)
+    o, m, l = run_fp8(ch)
+    ro, rm, rl = oracle_fp8(ch)
+    assert_attention_close(o, ro, f"prefill_fp8 v_per_token pos0={pos0} T={T}")
+    assert_states_close(m, l, rm, rl, f"prefill_fp8 v_per_token pos0={pos0} T={T}")
+
+
+def test_prefill_fp8_query_scales():
+    """Rows of very different magnitudes, and an all-zero row (uniform weights)."""
+    print("prefill_fp8 query scales", flush=True)
+    ch = Chunk(300, 40, seed=861)
+    q = bf16_values(ch.qbits).astype(np.float32)
+    q[:, 0] *= 1e-3
+    q[:, 1] *= 50.0
+    q[5] = 0.0
+    from synth import f32_to_bf16_bits
+    qbits = f32_to_bf16_bits(q)
+    o, m, l = run_fp8(ch, qbits=qbits)
+    ro, rm, rl = oracle_fp8(ch, qbits=qbits)
+    assert_attention_close(o, ro, "prefill_fp8 query scales")
+    assert_states_close(m, l, rm, rl, "prefill_fp8 query scales")
+
+
+def test_prefill_fp8_kv_already_written():
+    print("prefill_fp8 cache pre-written", flush=True)
+    ch = Chunk(300, 70, seed=862)
+    t = np.arange(300, 370)
+    slots = (ch.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+    f4.kv_cache_write_f4(ch.gc, torch.from_numpy(ch.k_new).cuda(), torch.from_numpy(ch.v_new).cuda(),
+                         torch.from_numpy(slots).cuda())
+    o, m, l = run_fp8(ch, write=False)
+    ro, rm, rl = oracle_fp8(ch)
+    assert_attention_close(o, ro, "prefill_fp8, cache pre-written")
+
+
+def test_prefill_fp8_within_budget_of_exact():
+    """The 8-bit result against the exact attention: the model's error budget
+    (E4M3 weights and values: ~4% of the output RMS on N(0,1) data)."""
+    print("prefill_fp8 vs exact", flush=True)
+    ch = Chunk(2000, 96, seed=863)
+    o, m, l = run_fp8(ch)
+    ro, rm, rl = ch.run_oracle()
+    rms = np.sqrt(np.mean(ro ** 2))
+    err = o - ro
+    assert np.sqrt(np.mean(err ** 2)) <= 0.10 * rms
+    assert np.abs(err).max() <= 0.6 * rms

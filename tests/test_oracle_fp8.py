@@ -89,12 +89,14 @@ def test_group_weights_put_the_largest_in_the_top_binade():
     for _ in range(200):
         x = g.normal(0, 5, 32) + g.uniform(-100, 100)
         p8, G = fp8.group_weights(x)
-        assert G == math.ceil(x.max())
+        assert G == math.ceil(x.max()) and p8.shape == (32,)
         assert 0.5 <= p8.max() <= 1.0                 # 2^(x - G) in (1/2, 1], then rounded
         np.testing.assert_array_equal(p8, [nearest_code_value(v) for v in np.exp2(x - G)])
-    # an integer maximum gives weight exactly 1; a score 10 below it rounds to 0 (below half of 2^-9)
-    p8, G = fp8.group_weights(np.array([3.0, 2.0, -7.0]))
-    assert G == 3 and list(p8) == [1.0, 0.5, 0.0]
+    # an integer maximum gives weight exactly 1; a score 10 below it rounds to 0 (below half of 2^-9);
+    # groups are independent and unseen keys (-inf) weigh 0
+    p8, G = fp8.group_weights(np.array([[3.0, 2.0, -7.0], [-0.5, -np.inf, -1.5]]))
+    assert list(G) == [3, 0] and p8.tolist() == [[1.0, 0.5, 0.0], [fp8.e4m3_round(2 ** -0.5), 0.0,
+                                                                     fp8.e4m3_round(2 ** -1.5)]]
 
 
 def fp16_exponent_rule(smax):
