@@ -33,6 +33,7 @@ import synth  # noqa: E402
 METRIC = "decode KV-tokens/s + achieved HBM GB/s (% of peak) for F4 paged attention"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense E4M3 (and INT8, in TOP/s)
 PAGE = 64
 HQ, HKV, D = 16, 4, 256
 SM = 1.0 / 16.0
@@ -383,8 +384,10 @@ def prefill_flops(T, pos0):
     return 4 * D * HQ * sum(pos0 + i + 1 for i in range(T))
 
 
-def bench_prefill(iters=5, T=2048, window=131072):
+def bench_prefill(iters=5, T=2048, window=131072, fp8=False):
+    """The prefill chunk; fp8 selects the 8-bit products (INT8 scores, E4M3 weighted sum)."""
     dev = "cuda"
+    call = f4.paged_attn_prefill_f4_fp8 if fp8 else f4.paged_attn_prefill_f4
     pos0 = window - T
     gen = torch.Generator().manual_seed(synth.BASE_SEED + 3)
     # one sequence's window of 2,048 pages placed by a random permutation of the pool;
@@ -410,22 +413,27 @@ def bench_prefill(iters=5, T=2048, window=131072):
     ws = torch.empty(max(16, f4.prefill_workspace_size(T, HQ, HKV, D, pos0)), dtype=torch.uint8, device=dev)
     out = torch.empty((T, HQ, D), device=dev)
     for _ in range(2):
-        f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
+        call(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with f4.KernelTimer(f4.KERNEL_PREFILL, max_launches=iters) as timer:
+    with f4.KernelTimer(f4.KERNEL_PREFILL_FP8 if fp8 else f4.KERNEL_PREFILL, max_launches=iters) as timer:
         e0.record()
         for _ in range(iters):
-            f4.paged_attn_prefill_f4(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
+            call(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
         e1.record()
         torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     fl = prefill_flops(T, pos0)
     tf = fl / (ms / 1e3) / 1e12
     tk = fl / (timer.avg_ms / 1e3) / 1e12
-    return {"workload": "2,048 queries at 129,024..131,071 over a 131,072-token causal window (write included)",
-            "ms": ms, "tflops": tf, "mfma_frac": tf / MFMA_F16_PEAK_TFLOPS, "flops": fl,
-            "kernel_ms": timer.avg_ms, "kernel_tflops": tk, "kernel_mfma_frac": tk / MFMA_F16_PEAK_TFLOPS}
+    peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_F16_PEAK_TFLOPS
+    r = {"workload": "2,048 queries at 129,024..131,071 over a 131,072-token causal window (write included)",
+         "ms": ms, "tflops": tf, "mfma_frac": tf / peak, "flops": fl,
+         "kernel_ms": timer.avg_ms, "kernel_tflops": tk, "kernel_mfma_frac": tk / peak}
+    if fp8:
+        r["precision"] = "Q.K^T INT8, P.V E4M3 (fractions of the 5.0 PFLOP/s dense FP8 peak)"
+        r["kernel_frac_of_fp16_peak"] = tk / MFMA_F16_PEAK_TFLOPS
+    return r
 
 
 def cpu_baseline(sample_tokens=458752):
@@ -538,6 +546,8 @@ def main():
         torch.cuda.empty_cache()
         extra["prefill"] = bench_prefill()
         log("prefill:", extra["prefill"])
+        extra["prefill_fp8"] = bench_prefill(fp8=True)
+        log("prefill fp8:", extra["prefill_fp8"])
         torch.cuda.empty_cache()
         extra["decode_v_per_token"] = bench_vtok()
         log("v per token:", extra["decode_v_per_token"])

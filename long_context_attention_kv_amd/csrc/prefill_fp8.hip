@@ -79,6 +79,7 @@ struct __align__(16) Fp8Smem {
   float tau[kPage];                 // the INT8 key scale of each token
   uint16_t vsc[2][8][kPage];        // V scales [page parity][block][token] (one scale per token: row 0)
   uint32_t vmax[2][2][8];           // largest V scale bits [page parity][token group][block]
+  i32x4 qs[kWaves][8][64];          // INT8 query operands [wave][score step][lane]
 };
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
@@ -229,7 +230,7 @@ __device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, in
 }
 
 template <bool VT>
-__global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, const int32_t* __restrict__ pt) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Fp8Args a, const int32_t* __restrict__ pt) {
   __shared__ Fp8Smem sm;
   const int qt = blockIdx.x;     // query tile
   const int g = blockIdx.y;      // KV head
@@ -250,8 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
   const int pbeg = __builtin_amdgcn_readfirstlane(split * per);
   const int pend = __builtin_amdgcn_readfirstlane(min(npages, pbeg + per));
 
-  // ---- query row to INT8: B operands of the 8 score steps (channels 32 s + 16 half .. + 15) ----
-  i32x4 qop[8];
+  // ---- query row to INT8: B operands of the 8 score steps (channels 32 s + 16 half .. + 15), kept in LDS ----
   float row_scale;  // sigma * qk
   {
     const uint16_t* qrow = a.q + (static_cast<int64_t>(qvalid ? qi : 0) * a.Hq + hq) * kHeadDim;
@@ -287,12 +287,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
         b[i] = static_cast<int>(r) & 0xFF;
       }
       // each group of 8 channels in the order 0, 1, 4, 5, 2, 3, 6, 7
+      i32x4 op;
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         const int* c = b + 8 * v;
-        qop[s][2 * v] = c[0] | (c[1] << 8) | (c[4] << 16) | (c[5] << 24);
-        qop[s][2 * v + 1] = c[2] | (c[3] << 8) | (c[6] << 16) | (c[7] << 24);
+        op[2 * v] = c[0] | (c[1] << 8) | (c[4] << 16) | (c[5] << 24);
+        op[2 * v + 1] = c[2] | (c[3] << 8) | (c[6] << 16) | (c[7] << 24);
       }
+      sm.qs[wave][s][lane] = op;
     }
   }
 
@@ -311,33 +313,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
   if (tid < 32) reinterpret_cast<uint32_t*>(sm.vmax)[tid] = 0u;
   __syncthreads();
 
-  // cells in flight at the top of iteration lp: vcur = V of page lp, kraw = K
-  // of page lp + 1; requested during lp: vnext = V of lp + 1, kahead = K of lp + 2
-  KRaw kraw{}, kahead{};
+  // cells in flight: vcur = V of page lp; requested at the top of iteration
+  // lp: K and V of page lp + 1 (the keys are converted in this iteration's
+  // second half, the values in the next iteration)
+  KRaw kraw{};
   VRaw vcur{}, vnext{};
-  bool cur_valid = false, kraw_valid = false, kahead_valid = false;
-  int64_t kraw_ph = 0, kahead_ph = 0;
+  bool cur_valid = false, next_valid = false;
   if (pbeg < pend) {
-    KRaw k0;
     const int64_t ph0 = page_handle(pbeg, cur_valid);
-    load_k<VT>(a, ph0, tid, k0);
+    load_k<VT>(a, ph0, tid, kraw);
     load_v(a, ph0, tid, vcur);
-    if (pbeg + 1 < pend) {
-      kraw_ph = page_handle(pbeg + 1, kraw_valid);
-      load_k<VT>(a, kraw_ph, tid, kraw);
-    }
-    unpack_k(sm, k0, tid, 0);
-    unpack_k(sm, k0, tid, 1);
-    stage_vscales<VT>(sm, k0, tid, pbeg & 1);
+    unpack_k(sm, kraw, tid, 0);
+    unpack_k(sm, kraw, tid, 1);
+    stage_vscales<VT>(sm, kraw, tid, pbeg & 1);
   }
 
   for (int lp = pbeg; lp < pend; ++lp) {
     const int par = lp & 1;
-    if (lp + 2 < pend) {
-      kahead_ph = page_handle(lp + 2, kahead_valid);
-      load_k<VT>(a, kahead_ph, tid, kahead);
+    if (lp + 1 < pend) {
+      const int64_t ph1 = page_handle(lp + 1, next_valid);
+      load_k<VT>(a, ph1, tid, kraw);
+      load_v(a, ph1, tid, vnext);
     }
-    if (lp + 1 < pend) load_v(a, kraw_ph, tid, vnext);
     __syncthreads();  // keys and V scales of this page are in LDS; every wave is done with the previous values
 
     // ---- values of this page to E4M3 (read in the PV step below) ----
@@ -345,24 +342,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     unpack_v<VT>(sm, vcur, tid, 0, par);
     unpack_v<VT>(sm, vcur, tid, 1, par);
 
-    // ---- S^T = K Q^T per 32-token tile, exact in INT32 ----
+    // ---- S^T = K Q^T for both 32-token tiles, exact in INT32 ----
+    i32x16 st[2] = {i32x16{}, i32x16{}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const i32x4 qop = sm.qs[wave][s][lane];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const i32x4 kop = *reinterpret_cast<const i32x4*>(&sm.kt[32 * tt + col][32 * s + 16 * half]);
+        st[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop, st[tt], 0, 0, 0);
+      }
+    }
     float x[2][16];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      i32x16 st = i32x16{};
-      const uint8_t* krow = &sm.kt[32 * tt + col][16 * half];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const i32x4 kop = *reinterpret_cast<const i32x4*>(krow + 32 * s);
-        st = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[s], st, 0, 0, 0);
-      }
       // rows 8 q + 4 half + i of the tile: token scales from LDS
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4_t tau4 = *reinterpret_cast<const float4_t*>(&sm.tau[32 * tt + 8 * q4 + 4 * half]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          x[tt][4 * q4 + i] = static_cast<float>(st[4 * q4 + i]) * (tau4[i] * row_scale);
+          x[tt][4 * q4 + i] = static_cast<float>(st[tt][4 * q4 + i]) * (tau4[i] * row_scale);
       }
     }
 
@@ -447,10 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     }
 
     vcur = vnext;
-    cur_valid = kraw_valid;
-    kraw = kahead;
-    kraw_valid = kahead_valid;
-    kraw_ph = kahead_ph;
+    cur_valid = next_valid;
   }
 
   // ---- epilogue ----
