@@ -138,16 +138,17 @@ def group_weights(x: np.ndarray):
     return e4m3_round(np.exp2(x - G[..., None])), G
 
 
-def _page_half_values(cache, page: int, head: int, half: int):
-    """V8 [32, D] and the factor 2^F [D] of one page half (step 6)."""
-    _, _, vc, vs = cache.page_codes(page, head)
+def _page_half_values(vc, vs, half: int):
+    """V8 [32, D] and the factor 2^F [D] of one page half (step 6), from the
+    page's value codes vc [64, D] and scales vs ([64, D/32], or [64])."""
+    D = vc.shape[1]
     rows = slice(GROUP * half, GROUP * (half + 1))
     vc = vc[rows].astype(np.float64)
     vs = np.asarray(vs[rows], dtype=np.float64)
     if vs.ndim == 1:  # one V scale per token
         F = scale_exponent(vs.max()) - 5
         vals = vc * vs[:, None] * 2.0 ** (-F)
-        f = np.full(cache.D, 2.0 ** F)
+        f = np.full(D, 2.0 ** F)
     else:
         F = scale_exponent(vs.max(axis=0)) - 5       # per block
         sd = np.repeat(vs, BLOCK, axis=1)
@@ -184,12 +185,12 @@ def prefill(cache, q, page_row, pos0: int, sm_scale: float, rows=None):
         Vf = np.zeros((n_pages * PAGE, D))
         for lp in range(n_pages):
             pg = int(page_row[lp])
-            kc, ks, _, _ = cache.page_codes(pg, g)
+            kc, ks, vc, vs = cache.page_codes(pg, g)
             kt, ta = requantize_keys(kc, ks)
             Kt[lp * PAGE:(lp + 1) * PAGE] = kt
             tau[lp * PAGE:(lp + 1) * PAGE] = ta
             for half in range(2):
-                v8, f = _page_half_values(cache, pg, g, half)
+                v8, f = _page_half_values(vc, vs, half)
                 sl = slice(lp * PAGE + GROUP * half, lp * PAGE + GROUP * (half + 1))
                 V8[sl] = v8
                 Vf[sl] = f[None, :]

@@ -22,6 +22,7 @@ import long_context_attention_kv_amd as f4
 import synth
 from oracle import attention as oatt
 from oracle import f4 as of4
+from oracle import fp8 as ofp8
 from oracle import yarn as oyarn
 from gpu_cases import assert_attention_close, bf16_tensor, bf16_values
 
@@ -207,13 +208,15 @@ def test_config4_ragged_8():
                     (ref[0][0], ref[1][0], ref[2][0]), f"sequence {b} (len {lengths[b]}) kv head {h}")
 
 
-def test_config3_prefill_2048_at_129024():
-    print("case: prefill of 2,048 queries at 129,024 over a 131,072-token window", flush=True)
+def prefill_setup():
+    """The prefill workload on the GPU: a 131,072-token window of one sequence
+    (2,048 pages placed by a permutation of the pool), the first 129,024 tokens
+    rotated and written block by block; the chunk of 2,048 queries, keys and
+    values drawn for the call itself."""
     T, window = 2048, 131072
     pos0 = window - T
     spec = spec_for(4.0)
     none = np.zeros(0, np.int64)
-    # one sequence whose window of 2,048 pages is placed by a permutation of the pool
     n_pages = window // PAGE
     pt = synth.page_permutation(synth.rng(3, 54), n_pages).astype(np.int32)
     cache = f4.F4Cache(n_pages, HKV, D)
@@ -232,32 +235,72 @@ def test_config3_prefill_2048_at_129024():
     kn = synth.normal_f32(g, (T, HKV, D))
     vn = synth.normal_f32(g, (T, HKV, D))
     qbits = synth.f32_to_bf16_bits(synth.normal_f32(g, (T, HQ, D)))
+    return T, pos0, spec, pt, cache, kn, vn, qbits
+
+
+def prefill_oracle_values(spec, pos0, kn, vn, h):
+    """The oracle's fp32 keys (rotated with its own fp32-stored table) and values
+    of KV head h, prefix and chunk, in token order."""
+    none = np.zeros(0, np.int64)
+    Ks, Vs = [], []
+    for j, t0 in enumerate(range(0, pos0, BLK)):
+        nb = min(BLK, pos0 - t0)
+        k = draw_block(3, 0, h, j, nb, 0, none).astype(np.float64)
+        cs, sn = table_f32(spec, np.arange(t0, t0 + nb))
+        Ks.append(oyarn.rope_apply(k[:, None, :], cs, sn, 256)[:, 0].astype(np.float32))
+        Vs.append(draw_block(3, 0, h, j, nb, 1, none))
+    Ks.append(kn[:, h])
+    Vs.append(vn[:, h])
+    return np.concatenate(Ks), np.concatenate(Vs)
+
+
+PREFILL_ROWS = [0, 1, 63, 64, 1000, 2046, 2047]
+
+
+def prefill_call(fn, T, pos0, pt, cache, kn, vn, qbits):
     ws = torch.empty(max(16, f4.prefill_workspace_size(T, HQ, HKV, D, pos0)), dtype=torch.uint8, device="cuda")
-    out, m, l = f4.paged_attn_prefill_f4(cache, bf16_tensor(qbits), torch.from_numpy(kn).cuda(),
-                                         torch.from_numpy(vn).cuda(), torch.from_numpy(pt).cuda(), pos0, SM,
-                                         workspace=ws)
+    out, m, l = fn(cache, bf16_tensor(qbits), torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
+                   torch.from_numpy(pt).cuda(), pos0, SM, workspace=ws)
     torch.cuda.synchronize()
     out, m, l = out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
     assert np.isfinite(out).all()
+    return out, m, l
+
+
+def test_config3_prefill_2048_at_129024():
+    print("case: prefill of 2,048 queries at 129,024 over a 131,072-token window", flush=True)
+    T, pos0, spec, pt, cache, kn, vn, qbits = prefill_setup()
+    out, m, l = prefill_call(f4.paged_attn_prefill_f4, T, pos0, pt, cache, kn, vn, qbits)
     qv = bf16_values(qbits)
-    rows = [0, 1, 63, 64, 1000, 2046, 2047]
     for h in (0, 3):
-        # oracle keys: rotated prefix + the chunk's raw keys, both quantised by the oracle
-        Ks, Vs = [], []
-        for j, t0 in enumerate(range(0, pos0, BLK)):
-            nb = min(BLK, pos0 - t0)
-            k = draw_block(3, 0, h, j, nb, 0, none).astype(np.float64)
-            cs, sn = table_f32(spec, np.arange(t0, t0 + nb))
-            Ks.append(oatt.dequantize_rows(oyarn.rope_apply(k[:, None, :], cs, sn, 256)[:, 0].astype(np.float32)))
-            Vs.append(oatt.dequantize_rows(draw_block(3, 0, h, j, nb, 1, none)))
-        Ks.append(oatt.dequantize_rows(kn[:, h]))
-        Vs.append(oatt.dequantize_rows(vn[:, h]))
-        K, V = np.concatenate(Ks), np.concatenate(Vs)
-        for i in rows:
+        K, V = prefill_oracle_values(spec, pos0, kn, vn, h)
+        K, V = oatt.dequantize_rows(K), oatt.dequantize_rows(V)
+        for i in PREFILL_ROWS:
             n = pos0 + i + 1
             ro, rm, rl = oatt.decode_head_from_values(qv[i, h * G:(h + 1) * G], K[:n], V[:n], SM)
             check_group(out[i, h * G:(h + 1) * G], m[i, h * G:(h + 1) * G], l[i, h * G:(h + 1) * G],
                         (ro[0], rm[0], rl[0]), f"prefill row {i} kv head {h}")
+
+
+def test_config3_prefill_fp8_2048_at_129024():
+    """The 8-bit prefill at the same shape, against the oracle's 8-bit model on
+    sampled rows; the model needs the cache's codes and scales, so the oracle
+    writes its own one-head cache of the sampled KV head."""
+    print("case: 8-bit prefill of 2,048 queries at 129,024 over a 131,072-token window", flush=True)
+    T, pos0, spec, pt, cache, kn, vn, qbits = prefill_setup()
+    out, m, l = prefill_call(f4.paged_attn_prefill_f4_fp8, T, pos0, pt, cache, kn, vn, qbits)
+    qv = bf16_values(qbits)
+    n = pos0 + T
+    t = np.arange(n)
+    slots = (pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+    for h in (0, 3):
+        K, V = prefill_oracle_values(spec, pos0, kn, vn, h)
+        oc = of4.Cache(len(pt), 1, D)
+        oc.write(K[:, None, :], V[:, None, :], slots)
+        ro, rm, rl = ofp8.prefill(oc, qv[:, h * G:(h + 1) * G], pt, pos0, SM, rows=PREFILL_ROWS)
+        for i in PREFILL_ROWS:
+            check_group(out[i, h * G:(h + 1) * G], m[i, h * G:(h + 1) * G], l[i, h * G:(h + 1) * G],
+                        (ro[i], rm[i], rl[i]), f"8-bit prefill row {i} kv head {h}")
 
 
 # ---- the next rows at the benchmark's shapes --------------------------------
