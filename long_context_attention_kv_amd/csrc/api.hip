@@ -4,6 +4,8 @@
 #include <cstdio>
 #include <string>
 
+#include <algorithm>
+
 #include "f4kv_internal.h"
 
 namespace {
@@ -244,7 +246,9 @@ int lse_merge(const float* m, const float* l, const float* o, int32_t C, int32_t
 size_t paged_attn_prefill_f4_workspace_size(int32_t T, int32_t Hq, int32_t num_kv_heads, int32_t head_dim,
                                             int32_t pos0) {
   if (T <= 0 || Hq <= 0 || num_kv_heads <= 0 || head_dim != f4kv::kHeadDim || pos0 < 0) return 0;
-  return f4kv::plan_prefill(T, Hq, num_kv_heads, pos0).ws_bytes;
+  // one size for both prefill entry points
+  return std::max(f4kv::plan_prefill_f16(T, Hq, num_kv_heads, pos0).ws_bytes,
+                  f4kv::plan_prefill_fp8(T, Hq, num_kv_heads, pos0).ws_bytes);
 }
 
 }  // extern "C"
@@ -273,7 +277,8 @@ int prefill_common(const char* fn, bool fp8, const f4kv_cache* cache, const uint
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || (k_new && !aligned(k_new, 16)) ||
       (v_new && !aligned(v_new, 16)))
     return fail(F4KV_ERR_INVALID, "%s: q, out, k_new, v_new must be 16-byte aligned", fn);
-  const f4kv::PrefillPlan plan = f4kv::plan_prefill(T, Hq, Hkv, pos0);
+  const f4kv::PrefillPlan plan =
+      fp8 ? f4kv::plan_prefill_fp8(T, Hq, Hkv, pos0) : f4kv::plan_prefill_f16(T, Hq, Hkv, pos0);
   if (plan.ws_bytes > 0) {
     if (!workspace || ws_bytes < plan.ws_bytes)
       return fail(F4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, plan.ws_bytes,

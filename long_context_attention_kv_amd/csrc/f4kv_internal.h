@@ -90,7 +90,18 @@ struct PrefillPlan {
   size_t ws_bytes;
 };
 
-PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0);
+// tile_positions query positions per workgroup; the key range is split until
+// the grid has about target_wgs workgroups (at most 16 splits, each >= 16 pages).
+PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0, int32_t tile_positions,
+                         int32_t target_wgs);
+// The plans of the two prefill kernels (fp16: 32 positions, two workgroup
+// rounds; 8-bit: 64 positions, one round).
+inline PrefillPlan plan_prefill_f16(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0) {
+  return plan_prefill(T, Hq, Hkv, pos0, 32, 512);
+}
+inline PrefillPlan plan_prefill_fp8(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0) {
+  return plan_prefill(T, Hq, Hkv, pos0, 64, 256);
+}
 
 hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
                           int32_t max_pages, int32_t T, int32_t Hq, int32_t pos0,

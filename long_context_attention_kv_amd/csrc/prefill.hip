@@ -549,13 +549,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
 
 }  // namespace
 
-PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0) {
+PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0, int32_t tile_positions,
+                         int32_t target_wgs) {
   PrefillPlan p;
-  p.q_tiles = (T + kQPos - 1) / kQPos;
+  p.q_tiles = (T + tile_positions - 1) / tile_positions;
   const int64_t total_pages = (static_cast<int64_t>(pos0) + T + kPage - 1) / kPage;
-  // enough workgroups to cover the chip twice over when the key range is long
+  // split the key range until the grid reaches the target when the range is long
   const int64_t wgs = static_cast<int64_t>(p.q_tiles) * Hkv;
-  int64_t splits = (512 + wgs - 1) / std::max<int64_t>(wgs, 1);
+  int64_t splits = (target_wgs + wgs - 1) / std::max<int64_t>(wgs, 1);
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, total_pages / 16));
   p.kv_splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, 16)));
   const int64_t R = static_cast<int64_t>(T) * Hq;

@@ -18,9 +18,12 @@
 //    exponent field of the largest V scale there) - 19, V8 = e4m3(c s 2^-F);
 //  * out = sum P8 2^G V8 2^F / sum 2^x (the unquantised weights below).
 //
-// Shape of the work: as in the fp16 prefill, a workgroup of 4 waves owns 32
-// query positions of one KV head (128 rows, 32 per wave, one lane per row) and
-// a range of key pages.  Per page of 64 keys:
+// Shape of the work: a workgroup of 8 waves owns 64 query positions of one KV
+// head (256 rows once the 4 query heads of the group are stacked, 32 per wave,
+// one lane per row; 8 positions per wave as in the fp16 prefill) and a range
+// of key pages.  With 8 waves sharing a page's conversion each thread converts
+// one 16-byte unit of keys and one of values per page; two waves per SIMD
+// hide each other's latencies.  Per page of 64 keys:
 //  1. the workgroup requantises the page's keys into LDS as INT8 [token]
 //     [channel] (packed 16-bit integer arithmetic: c M + round, shifted) and
 //     its values as E4M3 V^T [channel][token];
@@ -49,9 +52,9 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQPos = 32;               // query positions per workgroup (8 per wave)
+constexpr int kQPos = 64;               // query positions per workgroup (8 per wave)
 constexpr int kKRow = kHeadDim + 16;    // bytes per INT8 key row in LDS
 constexpr int kVRow = kPage + 8;        // bytes per E4M3 value row in LDS
 constexpr float kLog2e = 1.4426950408889634f;
@@ -86,38 +89,35 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Raw cells of one page for this thread.  Keys: units (block 2 w + u, token
-// t) for u = 0, 1 (w = wave, t = lane) and the token's eight K scales; one
-// dword of the V scale tile (token tid / 4, blocks 2 (tid % 4), + 1; with one
-// V scale per token, tokens 2 (tid % 32), + 1).  Values: units (token group
-// 2 w + u of 8 tokens, channel quad t).
+// Raw cells of one page for this thread.  Keys: the unit (block w, token t)
+// (w = wave, t = lane) and the token's eight K scales; threads below 256 also
+// hold one dword of the V scale tile (token tid / 4, blocks 2 (tid % 4), + 1;
+// with one V scale per token, threads below 32 hold tokens 2 tid, + 1).
+// Values: the unit (token group w of 8 tokens, channel quad t).
 struct KRaw {
-  uint4 k[2];
+  uint4 k;
   uint4 ks;      // the eight K block scales of token t
   uint32_t vsd;  // two V scales
 };
 struct VRaw {
-  uint4 v[2];
+  uint4 v;
 };
 
 template <bool VT>
 __device__ __forceinline__ void load_k(const Fp8Args& a, int64_t ph, int tid, KRaw& r) {
   const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
   const int w = tid >> 6, t = tid & 63;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) r.k[u] = kt[(2 * w + u) * 64 + t];
+  r.k = kt[w * 64 + t];
   r.ks = reinterpret_cast<const uint4*>(a.k_scale + ph * (kPage * 8))[t];
   if (VT)
     r.vsd = reinterpret_cast<const uint32_t*>(a.v_scale + ph * kPage)[tid & 31];
   else
-    r.vsd = reinterpret_cast<const uint32_t*>(a.v_scale + ph * (kPage * 8))[tid];
+    r.vsd = reinterpret_cast<const uint32_t*>(a.v_scale + ph * (kPage * 8))[tid & 255];
 }
 
 __device__ __forceinline__ void load_v(const Fp8Args& a, int64_t ph, int tid, VRaw& r) {
   const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
-  const int w = tid >> 6, t = tid & 63;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) r.v[u] = vt[(2 * w + u) * 64 + t];
+  r.v = vt[tid];
 }
 
 // The V scales of the page to LDS ([block][token]) and their largest value per
@@ -131,7 +131,7 @@ __device__ __forceinline__ void stage_vscales(Fp8Smem& sm, const KRaw& r, int ti
       const uint32_t mx = max(r.vsd & 0xFFFFu, r.vsd >> 16);
       atomicMax(&sm.vmax[parity][tid >> 4][0], mx);
     }
-  } else {
+  } else if (tid < 256) {
     const int t = tid >> 2, b = 2 * (tid & 3);
     sm.vsc[parity][b][t] = static_cast<uint16_t>(r.vsd);
     sm.vsc[parity][b + 1][t] = static_cast<uint16_t>(r.vsd >> 16);
@@ -140,15 +140,15 @@ __device__ __forceinline__ void stage_vscales(Fp8Smem& sm, const KRaw& r, int ti
   }
 }
 
-// Keys of unit u to INT8.  With the block scale s = M 2^(max(e5, 1) - 25) (M
+// Keys of this thread's unit to INT8.  With the block scale s = M 2^(max(e5, 1) - 25) (M
 // its significand, e5 its exponent field) and tau = 2^(e5max - 18), c s / tau
 // = c M / 2^k for k = e5max + 7 - max(e5, 1) >= 6; rounded half up that is
 // (n M - 8 M + 2^(k-1)) >> k on 16-bit lanes (|c M| <= 16376; k is clamped at
 // 15, where the result is 0 either way).  Nibble pairs (j, j + 4) of a dword
 // come out of one AND; the bytes are stored as channels 0, 1, 4, 5, 2, 3, 6, 7
 // of each group of 8, and the query operands use the same order.
-__device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, int u) {
-  const int c = 2 * (tid >> 6) + u, t = tid & 63;
+__device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid) {
+  const int c = tid >> 6, t = tid & 63;
   const uint32_t b01 = word(r.ks, 0), b23 = word(r.ks, 1), b45 = word(r.ks, 2), b67 = word(r.ks, 3);
   // largest of the eight scales (non-negative fp16 bits compare as integers)
   const uint32_t m1 = max(max(b01 & 0xFFFFu, b01 >> 16), max(b23 & 0xFFFFu, b23 >> 16));
@@ -165,7 +165,7 @@ __device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, in
   uint32_t out[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t w = word(r.k[u], d);
+    const uint32_t w = word(r.k, d);
     uint32_t p[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -182,13 +182,13 @@ __device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, in
   if (tid < 64) sm.tau[t] = __builtin_amdgcn_ldexpf(1.0f, e5max - 18);
 }
 
-// Values of unit u (tokens 8 (2 w + u) .., channel quad j = lane) to E4M3.  The
+// Values of this thread's unit (tokens 8 w .., channel quad j = lane) to E4M3.  The
 // 8 tokens of the unit fall in one 32-token group g and one 8-token column a
 // of it; within a group the MFMA takes tokens 8 a + 4 h + i from lane half h,
 // byte 4 a + i, so each channel gets two 4-byte pieces (h = 0, 1).
 template <bool VT>
-__device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, int u, int parity) {
-  const int c8 = 2 * (tid >> 6) + u, j = tid & 63;
+__device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, int parity) {
+  const int c8 = tid >> 6, j = tid & 63;
   const int g = c8 >> 2, acol = c8 & 3, blk = j >> 3;
   const uint32_t mx = sm.vmax[parity][g][VT ? 0 : blk];
   const float inv = __builtin_amdgcn_ldexpf(1.0f, 19 - static_cast<int>(mx >> 10));  // 2^-F
@@ -204,7 +204,7 @@ __device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, in
   float x[8][4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t w = word(r.v[u], k);
+    const uint32_t w = word(r.v, k);
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
@@ -230,7 +230,7 @@ __device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, in
 }
 
 template <bool VT>
-__global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Fp8Args a, const int32_t* __restrict__ pt) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, const int32_t* __restrict__ pt) {
   __shared__ Fp8Smem sm;
   const int qt = blockIdx.x;     // query tile
   const int g = blockIdx.y;      // KV head
@@ -323,8 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Fp8Args a, con
     const int64_t ph0 = page_handle(pbeg, cur_valid);
     load_k<VT>(a, ph0, tid, kraw);
     load_v(a, ph0, tid, vcur);
-    unpack_k(sm, kraw, tid, 0);
-    unpack_k(sm, kraw, tid, 1);
+    unpack_k(sm, kraw, tid);
     stage_vscales<VT>(sm, kraw, tid, pbeg & 1);
   }
 
@@ -339,8 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Fp8Args a, con
 
     // ---- values of this page to E4M3 (read in the PV step below) ----
     if (tid < 16) sm.vmax[par ^ 1][tid >> 3][tid & 7] = 0u;  // the next page's maxima start from 0
-    unpack_v<VT>(sm, vcur, tid, 0, par);
-    unpack_v<VT>(sm, vcur, tid, 1, par);
+    unpack_v<VT>(sm, vcur, tid, par);
 
     // ---- S^T = K Q^T for both 32-token tiles, exact in INT32 ----
     i32x16 st[2] = {i32x16{}, i32x16{}};
@@ -424,8 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Fp8Args a, con
 
     // ---- keys of the next page to INT8 and its V scales, while the matrix cores work on P.V ----
     if (lp + 1 < pend) {
-      unpack_k(sm, kraw, tid, 0);
-      unpack_k(sm, kraw, tid, 1);
+      unpack_k(sm, kraw, tid);
       stage_vscales<VT>(sm, kraw, tid, par ^ 1);
     }
 
