@@ -147,7 +147,9 @@ __device__ __forceinline__ void stage_vscales(Fp8Smem& sm, const KRaw& r, int ti
 // 15, where the result is 0 either way).  Nibble pairs (j, j + 4) of a dword
 // come out of one AND; the bytes are stored as channels 0, 1, 4, 5, 2, 3, 6, 7
 // of each group of 8, and the query operands use the same order.
-__device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid) {
+// tau goes to LDS with the sign of the logit scale, so that the scores up to
+// the positive factor |sigma qk| order like the scores themselves.
+__device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, float tau_sign) {
   const int c = tid >> 6, t = tid & 63;
   const uint32_t b01 = word(r.ks, 0), b23 = word(r.ks, 1), b45 = word(r.ks, 2), b67 = word(r.ks, 3);
   // largest of the eight scales (non-negative fp16 bits compare as integers)
@@ -179,7 +181,7 @@ __device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid) {
   uint4* dst = reinterpret_cast<uint4*>(&sm.kt[t][32 * c]);
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-  if (tid < 64) sm.tau[t] = __builtin_amdgcn_ldexpf(1.0f, e5max - 18);
+  if (tid < 64) sm.tau[t] = __builtin_amdgcn_ldexpf(tau_sign, e5max - 18);
 }
 
 // Values of this thread's unit (tokens 8 w .., channel quad j = lane) to E4M3.  The
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
   const int pend = __builtin_amdgcn_readfirstlane(min(npages, pbeg + per));
 
   // ---- query row to INT8: B operands of the 8 score steps (channels 32 s + 16 half .. + 15), kept in LDS ----
-  float row_scale;  // sigma * qk
+  float row_scale;  // |sigma qk|
   {
     const uint16_t* qrow = a.q + (static_cast<int64_t>(qvalid ? qi : 0) * a.Hq + hq) * kHeadDim;
     float qv[8][16];
@@ -277,7 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     int e = 7;  // an all-zero row: sigma = 1
     if (mx > 0.0f) frexpf(mx, &e);  // mx < 2^e
     const float inv_sigma = __builtin_amdgcn_ldexpf(1.0f, 7 - e);
-    row_scale = __builtin_amdgcn_ldexpf(a.qk_scale, e - 7);
+    // (a zero logit scale: tau is 0 below, every score 0)
+    row_scale = a.qk_scale == 0.0f ? 1.0f : __builtin_amdgcn_ldexpf(fabsf(a.qk_scale), e - 7);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       int b[16];
@@ -298,6 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     }
   }
 
+  const float tau_sign = a.qk_scale > 0.0f ? 1.0f : (a.qk_scale < 0.0f ? -1.0f : 0.0f);
   f32x16 acc[8];  // O^T: 8 tiles of 32 value rows (rows 32 ct .. of the LDS order)
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc[d] = f32x16{};
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     const int64_t ph0 = page_handle(pbeg, cur_valid);
     load_k<VT>(a, ph0, tid, kraw);
     load_v(a, ph0, tid, vcur);
-    unpack_k(sm, kraw, tid);
+    unpack_k(sm, kraw, tid, tau_sign);
     stage_vscales<VT>(sm, kraw, tid, pbeg & 1);
   }
 
@@ -354,32 +358,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     float x[2][16];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      // rows 8 q + 4 half + i of the tile: token scales from LDS
+      // rows 8 q + 4 half + i of the tile: x = S tau with the token scales from LDS; the
+      // scores in log2 units are x row_scale (row_scale > 0, the sign is in tau)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4_t tau4 = *reinterpret_cast<const float4_t*>(&sm.tau[32 * tt + 8 * q4 + 4 * half]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          x[tt][4 * q4 + i] = static_cast<float>(st[tt][4 * q4 + i]) * (tau4[i] * row_scale);
+          x[tt][4 * q4 + i] = static_cast<float>(st[tt][4 * q4 + i]) * tau4[i];  // exact: tau is a power of two
       }
     }
 
     // ---- softmax: mask, group maxima, lazy raise of the running max ----
+    // (the mask only on pages that reach past the tile's first position: a
+    // branch of its own, which keeps its compares off the other pages)
     const bool need_mask = !cur_valid || lp * kPage + 63 > qpos_first;
     float gmax[2];
+    if (need_mask) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float mx = -INFINITY;
+      for (int tt = 0; tt < 2; ++tt) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if (need_mask) {
+        for (int e = 0; e < 16; ++e) {
           const int tok = lp * kPage + 32 * tt + 8 * (e >> 2) + 4 * half + (e & 3);
           if (!(cur_valid && qvalid && tok <= qpos)) x[tt][e] = -INFINITY;
+          mx = fmaxf(mx, x[tt][e]);
         }
-        mx = fmaxf(mx, x[tt][e]);
+        gmax[tt] = mx;
       }
-      gmax[tt] = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float mx = x[tt][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[tt][e]);
+        gmax[tt] = mx;
+      }
     }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) gmax[tt] = fmaxf(gmax[tt], __shfl_xor(gmax[tt], 32, 64)) * row_scale;
     s_max = fmaxf(s_max, fmaxf(gmax[0], gmax[1]));
     const float G0 = ceilf(gmax[0]), G1 = ceilf(gmax[1]);  // -inf stays -inf
     const float pmax = fmaxf(G0, G1);
@@ -404,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
       float e[16], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(x[tt][i] - off);  // 0 for masked keys
+        e[i] = __builtin_amdgcn_exp2f(fmaf(x[tt][i], row_scale, -off));  // 0 for masked keys
         psum += e[i];
       }
 #pragma unroll
@@ -422,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
 
     // ---- keys of the next page to INT8 and its V scales, while the matrix cores work on P.V ----
     if (lp + 1 < pend) {
-      unpack_k(sm, kraw, tid);
+      unpack_k(sm, kraw, tid, tau_sign);
       stage_vscales<VT>(sm, kraw, tid, par ^ 1);
     }
 

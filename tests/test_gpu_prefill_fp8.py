@@ -14,21 +14,21 @@ from test_gpu_prefill import Chunk, PAGE, SM
 pytestmark = pytest.mark.gpu
 
 
-def run_fp8(ch: Chunk, write=True, qbits=None):
+def run_fp8(ch: Chunk, write=True, qbits=None, sm=SM):
     kn = torch.from_numpy(ch.k_new).cuda() if write else None
     vn = torch.from_numpy(ch.v_new).cuda() if write else None
     qb = ch.qbits if qbits is None else qbits
-    out = f4.paged_attn_prefill_f4_fp8(ch.gc, bf16_tensor(qb), kn, vn, torch.from_numpy(ch.pt).cuda(), ch.pos0, SM)
+    out = f4.paged_attn_prefill_f4_fp8(ch.gc, bf16_tensor(qb), kn, vn, torch.from_numpy(ch.pt).cuda(), ch.pos0, sm)
     torch.cuda.synchronize()
     return [x.cpu().numpy() for x in out]
 
 
-def oracle_fp8(ch: Chunk, qbits=None, rows=None):
+def oracle_fp8(ch: Chunk, qbits=None, rows=None, sm=SM):
     t = np.arange(ch.pos0, ch.pos0 + ch.T)
     slots = (ch.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
     ch.oc.write(ch.k_new, ch.v_new, slots)
     qb = ch.qbits if qbits is None else qbits
-    return ofp8.prefill(ch.oc, bf16_values(qb), ch.pt, ch.pos0, SM, rows=rows)
+    return ofp8.prefill(ch.oc, bf16_values(qb), ch.pt, ch.pos0, sm, rows=rows)
 
 
 @pytest.mark.parametrize("pos0,T", [(0, 1), (0, 64), (100, 37), (64, 130), (1000, 200), (4000, 33)])
@@ -66,6 +66,17 @@ def test_prefill_fp8_query_scales():
     ro, rm, rl = oracle_fp8(ch, qbits=qbits)
     assert_attention_close(o, ro, "prefill_fp8 query scales")
     assert_states_close(m, l, rm, rl, "prefill_fp8 query scales")
+
+
+@pytest.mark.parametrize("sm", [0.0, -1.0 / 16.0, 0.25])
+def test_prefill_fp8_logit_scale_signs(sm):
+    """A zero logit scale (uniform weights), a negative one and a large one."""
+    print(f"prefill_fp8 sm_scale={sm}", flush=True)
+    ch = Chunk(200, 50, seed=870)
+    o, m, l = run_fp8(ch, sm=sm)
+    ro, rm, rl = oracle_fp8(ch, sm=sm)
+    assert_attention_close(o, ro, f"prefill_fp8 sm_scale={sm}")
+    assert_states_close(m, l, rm, rl, f"prefill_fp8 sm_scale={sm}")
 
 
 def test_prefill_fp8_kv_already_written():
