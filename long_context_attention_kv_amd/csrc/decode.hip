@@ -33,7 +33,7 @@
 //    mixed-precision FMA (fp32 weight times fp16 nibble operand): an fp16
 //    weight (11 bits) would leave ~2e-3 of the output RMS on channels whose
 //    values are many times the others' (outlier channels).  The "- 8" is
-//    corrected once per page with the page's summed weights.
+//    corrected once, at the end, with the summed weights of the lane's block.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
 #include <algorithm>
@@ -457,11 +457,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 
   const QPrep<G>* QP = qprep + __builtin_amdgcn_readfirstlane(b * a.Hkv + g);
   float m_run[G], s_max[G], l_lane[G], o[G][4];
+  float wpart[G];  // this lane's share (8 tokens of each page) of the summed weights of block cj
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     s_max[h] = -INFINITY;
     l_lane[h] = 0.0f;
+    wpart[h] = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
   }
@@ -569,6 +571,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
         // mn == -inf only while no valid token has been seen: nothing to rescale
         const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - mn);
         l_lane[h] *= alpha;
+        wpart[h] *= alpha;
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[h][d] *= alpha;
         m_run[h] = mn;
@@ -632,18 +635,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
         }
       }
     }
-    // "- 8" correction: the page's summed weights of block cj
+    // "- 8" correction, part 1: this lane's 8 tokens of the page's weights of
+    // block cj (the 8 lanes of the block cover its 64 tokens); the sum over the
+    // lanes and the correction itself wait for the epilogue
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float4_t x = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8]);
       const float4_t y = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8 + 4]);
-      const float ws = sum8(((x.x + x.y) + (x.z + x.w)) + ((y.x + y.y) + (y.z + y.w)));
-      const float c1 = ws * 4.76837158203125e-07f;  // 8 * 2^-24
-      o[h][0] -= c1;
-      o[h][1] -= 16.0f * c1;
-      o[h][2] -= c1;
-      o[h][3] -= 16.0f * c1;
+      wpart[h] += ((x.x + x.y) + (x.z + x.w)) + ((y.x + y.y) + (y.z + y.w));
     }
+  }
+
+  // "- 8" correction, part 2: the summed weights of block cj over every page of
+  // the wave, times 8 (in the units of the nibble operands, 2^-24 and 16 x 2^-24)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float c1 = sum8(wpart[h]) * 4.76837158203125e-07f;  // 8 * 2^-24
+    o[h][0] -= c1;
+    o[h][1] -= 16.0f * c1;
+    o[h][2] -= c1;
+    o[h][3] -= 16.0f * c1;
   }
 
   // ---- epilogue: restore the exact maximum, fold the 4 waves ---------------
