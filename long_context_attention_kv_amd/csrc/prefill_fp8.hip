@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
 
-  // this lane's query row: position qt*32 + wave*8 + col/4, head g*4 + col%4
+  // this lane's query row: position qt * 64 + wave * 8 + col / 4, head g * 4 + col % 4
   const int qi = qt * kQPos + wave * 8 + col / 4;
   const bool qvalid = qi < a.T;
   const int qpos = a.pos0 + qi;
