@@ -6,7 +6,6 @@ import pytest
 import torch
 
 import long_context_attention_kv_amd as f4
-from oracle import attention as oatt
 from oracle import fp8 as ofp8
 from gpu_cases import assert_attention_close, assert_states_close, bf16_tensor, bf16_values, cache_arrays_equal
 from test_gpu_prefill import Chunk, PAGE, SM

@@ -7,7 +7,6 @@ import torch
 
 import long_context_attention_kv_amd as f4
 import synth
-from oracle import attention as oatt
 from oracle import f4 as of4
 from gpu_cases import (PagedSet, assert_attention_close, assert_states_close, bf16_tensor, cache_arrays_equal,
                        oracle_decode, random_q)
