@@ -253,17 +253,19 @@ def bench_1m(iters=10):
         once()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        once()
-    e1.record()
-    torch.cuda.synchronize()
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=iters) as timer:
+        e0.record()
+        for _ in range(iters):
+            once()
+        e1.record()
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     by = decode_algorithmic_bytes([ctx], windows=W)
     del L
     return {"workload": "1 x 1,048,576 tokens, 16 windows of 65,536 + lse_merge", "ms": ms,
             "kv_tokens_per_s": ctx / (ms / 1e3), "gbs": by / (ms / 1e3) / 1e9,
-            "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms": timer.avg_ms, "kernel_hbm_frac": by / (timer.avg_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_vtok(iters=20):
