@@ -101,3 +101,19 @@ def test_prefill_fp8_within_budget_of_exact():
     err = o - ro
     assert np.sqrt(np.mean(err ** 2)) <= 0.10 * rms
     assert np.abs(err).max() <= 0.6 * rms
+
+
+@pytest.mark.parametrize("Hkv", [1, 2])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_other_kv_head_counts(Hkv, fp8):
+    """Both prefills with 1 and 2 KV heads (4 and 8 query heads)."""
+    print(f"prefill ({'8-bit' if fp8 else 'fp16'}) Hkv={Hkv}", flush=True)
+    ch = Chunk(150, 90, Hkv=Hkv, seed=890 + Hkv)
+    if fp8:
+        o, m, l = run_fp8(ch)
+        ro, rm, rl = oracle_fp8(ch)
+    else:
+        o, m, l = ch.run_gpu()
+        ro, rm, rl = ch.run_oracle()
+    assert_attention_close(o, ro, f"prefill Hkv={Hkv}")
+    assert_states_close(m, l, rm, rl, f"prefill Hkv={Hkv}")
