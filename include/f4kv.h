@@ -310,7 +310,7 @@ int paged_attn_prefill_f4_fp8(const f4kv_cache* cache, const uint16_t* q,
  *                cu_seq_lens[B] <= total_tokens
  *   k_out, v_out [total_tokens][H][D] of out_dtype (F4KV_BF16 or F4KV_F32),
  *                16-byte aligned
- * Supported: D == 256; B <= 65535.
+ * Supported: D == 256; B <= 65535; max_pages * H < 2^31.
  */
 int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const int32_t* cu_seq_lens,
                        int32_t B, int32_t max_pages, int32_t total_tokens, void* k_out, void* v_out,

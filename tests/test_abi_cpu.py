@@ -166,6 +166,8 @@ def test_gather_argument_checks(lib):
     assert g(C.byref(c), 16, 16, 2, 4, 100, 24, 16, 1, None) == 1 and "aligned" in _err(lib)
     assert g(C.byref(c), 16, 16, 70000, 4, 100, 16, 16, 1, None) == 1
     assert g(C.byref(c), 16, 16, 2, 0, 100, 16, 16, 1, None) == 1 and "max_pages" in _err(lib)
+    wide = _cache(heads=128)                                                             # grid of max_pages * H
+    assert g(C.byref(wide), 16, 16, 2, 1 << 24, 100, 16, 16, 1, None) == 1 and "num_kv_heads" in _err(lib)
     c64 = _cache(dim=64)
     assert g(C.byref(c64), 16, 16, 2, 4, 100, 16, 16, 1, None) == 2 and "head_dim" in _err(lib)
 
