@@ -257,7 +257,11 @@ int lse_merge(const float* m, const float* l, const float* o, int32_t C, int32_t
  *   workspace    at least paged_attn_prefill_f4_workspace_size() bytes
  * Supported: D == 256, Hq / H == 4.  The products run in fp16 on MFMA with
  * fp32 accumulation, so cache values must lie within fp16 range (|x| < 65504,
- * which holds whenever the written keys/values did).
+ * which holds whenever the written keys/values did).  Each query row enters
+ * fp16 scaled by a power of two (its largest |q| into [2^10, 2^11)), exact for
+ * rows whose largest |q| lies in [2^-54, 2^75); elements below 2^-27 of their
+ * row's largest round to fp16's subnormal step.  Any finite sm_scale,
+ * including 0 and negative values.
  */
 size_t paged_attn_prefill_f4_workspace_size(int32_t T, int32_t Hq, int32_t num_kv_heads,
                                             int32_t head_dim, int32_t pos0);

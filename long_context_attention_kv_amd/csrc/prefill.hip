@@ -247,21 +247,53 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   const int pend = __builtin_amdgcn_readfirstlane(min(npages, pbeg + per));
 
   // Q^T operands: lane holds q[row][channels of LDS positions 16 s + 8 half + 0..7]
-  // for s = 0..15, i.e. channels 8 (2 s + half) + {0, 4, 1, 5, 2, 6, 3, 7}
+  // for s = 0..15, i.e. channels 8 (2 s + half) + {0, 4, 1, 5, 2, 6, 3, 7}.
+  // The wave's query rows are scaled by one power of two 2^qe that brings
+  // their largest |q| into [2^10, 2^11) (qe clamped to [-64, 64]), so fp16
+  // holds every bf16 query of that range exactly (elements below 2^-27 of the
+  // wave's largest round to fp16's subnormal step), and by the sign of the
+  // logit scale, so that the scores' maximum is the maximum of the scaled
+  // logits.  The wave's logit scale qk = |sm_scale log2(e)| 2^-qe undoes both;
+  // a zero logit scale gives zero operands and qk = 1 (every score 0).
+  const float qsign = a.qk_scale > 0.0f ? 1.0f : (a.qk_scale < 0.0f ? -1.0f : 0.0f);
   half8_t qf[kCT][16];
-#pragma unroll
-  for (int c = 0; c < kCT; ++c) {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(qvalid[c] ? qi[c] : 0) * a.Hq + hq) * kHeadDim;
+  float qk;
+  {
+    static_assert(kCT == 1, "one query row per lane");
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(qvalid[0] ? qi[0] : 0) * a.Hq + hq) * kHeadDim;
+    uint4 raw[16];
+    float qmax = 0.0f;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * half);
+      raw[s] = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * half);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = word(raw, j);
+        const uint32_t w = word(raw[s], j);
+        qmax = fmaxf(qmax, fmaxf(fabsf(bf16_to_f32(static_cast<uint16_t>(w))),
+                                 fabsf(bf16_to_f32(static_cast<uint16_t>(w >> 16)))));
+      }
+    }
+    for (int sh = 32; sh >= 1; sh >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, sh, 64));
+    int qe = 0;
+    if (qmax > 0.0f) {
+      int ex;
+      frexpf(qmax, &ex);  // qmax in [2^(ex-1), 2^ex)
+      qe = min(64, max(-64, 11 - ex));
+    }
+    qe = __builtin_amdgcn_readfirstlane(qe);
+    qk = qsign == 0.0f ? 1.0f : ldexpf(fabsf(a.qk_scale), -qe);
+    // wave-uniform: kept in a scalar register, as the plain argument would be
+    qk = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, qk)));
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = word(raw[s], j);
+        const float x0 = qsign * ldexpf(bf16_to_f32(static_cast<uint16_t>(w)), qe);
+        const float x1 = qsign * ldexpf(bf16_to_f32(static_cast<uint16_t>(w >> 16)), qe);
         // channels 2j, 2j + 1 of the group go to positions 2j and 2j - 7 (+8 for the odd half)
-        qf[c][s][(2 * j) < 4 ? 4 * j : 4 * j - 7] = static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w)));
-        qf[c][s][(2 * j + 1) < 4 ? 4 * j + 2 : 4 * j - 5] =
-            static_cast<_Float16>(bf16_to_f32(static_cast<uint16_t>(w >> 16)));
+        qf[0][s][(2 * j) < 4 ? 4 * j : 4 * j - 7] = static_cast<_Float16>(x0);
+        qf[0][s][(2 * j + 1) < 4 ? 4 * j + 2 : 4 * j - 5] = static_cast<_Float16>(x1);
       }
     }
   }
@@ -394,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.qk_scale;  // log2 units
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qk;  // log2 units
     s_max[0] = fmaxf(s_max[0], mx);
     const bool raise = mx > m_run[0] + kSlack;
     if (__ballot(raise)) {
@@ -425,8 +457,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   auto p_half = [&](const float16_t& st, float off, int h, float* e, float& psum, half8_t* pb, half8_t* pl) {
     const int j = h >> 1;
     if ((h & 1) == 0) {
-      e[0] = __builtin_amdgcn_exp2f(fmaf(st[2 * j], a.qk_scale, off));
-      e[1] = __builtin_amdgcn_exp2f(fmaf(st[2 * j + 1], a.qk_scale, off));
+      e[0] = __builtin_amdgcn_exp2f(fmaf(st[2 * j], qk, off));
+      e[1] = __builtin_amdgcn_exp2f(fmaf(st[2 * j + 1], qk, off));
     } else {
       psum += e[0] + e[1];
       const auto hh = __builtin_amdgcn_cvt_pkrtz(e[0], e[1]);

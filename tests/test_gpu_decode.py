@@ -13,14 +13,14 @@ pytestmark = pytest.mark.gpu
 SM = 1.0 / 16.0
 
 
-def _run(ps: PagedSet, Hq, seed=0, W=1, wt=0, q_scale=1.0, max_ctx=None):
+def _run(ps: PagedSet, Hq, seed=0, W=1, wt=0, q_scale=1.0, max_ctx=None, sm=SM):
     B = len(ps.lengths)
     bits, qv = random_q(B, Hq, ps.D, seed, q_scale)
     max_ctx = max(ps.lengths) if max_ctx is None else max_ctx
     out, m, l = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), ps.gpu_lengths(), max_ctx,
-                                        SM, num_windows=W, window_tokens=wt)
+                                        sm, num_windows=W, window_tokens=wt)
     torch.cuda.synchronize()
-    ro, rm, rl = oracle_decode(ps, qv, SM, num_windows=W, window_tokens=wt)
+    ro, rm, rl = oracle_decode(ps, qv, sm, num_windows=W, window_tokens=wt)
     return (out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()), (ro, rm, rl)
 
 
@@ -68,6 +68,25 @@ def test_large_and_small_query_scale():
         (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=9, q_scale=sc)
         assert_attention_close(o, ro, f"q scale {sc}")
         assert_states_close(m, l, rm, rl, f"q scale {sc}")
+
+
+@pytest.mark.parametrize("sm", [0.0, -1.0 / 16.0, 0.25])
+def test_logit_scale_signs(sm):
+    """A zero logit scale (uniform weights), a negative one and a large one."""
+    ps = PagedSet([700, 90], Hkv=4, seed=12)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=12, sm=sm)
+    assert_attention_close(o, ro, f"sm_scale {sm}")
+    assert_states_close(m, l, rm, rl, f"sm_scale {sm}")
+
+
+@pytest.mark.parametrize("log2_scale", [20, -30])
+def test_query_far_outside_fp16_range(log2_scale):
+    """bf16 queries beyond fp16's largest value (x 2^20) or below its smallest
+    normal (x 2^-30); the logit scale compensates, so the weights stay the same."""
+    ps = PagedSet([500], Hkv=4, seed=13)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=13, q_scale=2.0 ** log2_scale, sm=SM * 2.0 ** -log2_scale)
+    assert_attention_close(o, ro, f"q x 2^{log2_scale}")
+    assert_states_close(m, l, rm, rl, f"q x 2^{log2_scale}")
 
 
 def test_outliers_and_scaled_values():

@@ -39,19 +39,21 @@ class Chunk:
             f4.kv_cache_write_f4(self.gc, torch.from_numpy(k_old).cuda(), torch.from_numpy(v_old).cuda(),
                                  torch.from_numpy(old_slots).cuda())
 
-    def run_gpu(self, write=True):
+    def run_gpu(self, write=True, qbits=None, sm=SM):
         kn = torch.from_numpy(self.k_new).cuda() if write else None
         vn = torch.from_numpy(self.v_new).cuda() if write else None
-        out = f4.paged_attn_prefill_f4(self.gc, bf16_tensor(self.qbits), kn, vn, torch.from_numpy(self.pt).cuda(),
-                                       self.pos0, SM)
+        qb = self.qbits if qbits is None else qbits
+        out = f4.paged_attn_prefill_f4(self.gc, bf16_tensor(qb), kn, vn, torch.from_numpy(self.pt).cuda(),
+                                       self.pos0, sm)
         torch.cuda.synchronize()
         return [x.cpu().numpy() for x in out]
 
-    def run_oracle(self, rows=None):
+    def run_oracle(self, rows=None, qbits=None, sm=SM):
         t = np.arange(self.pos0, self.pos0 + self.T)
         slots = (self.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
         self.oc.write(self.k_new, self.v_new, slots)
-        return oatt.prefill(self.oc, bf16_values(self.qbits), self.pt, self.pos0, SM, rows=rows)
+        qb = self.qbits if qbits is None else qbits
+        return oatt.prefill(self.oc, bf16_values(qb), self.pt, self.pos0, sm, rows=rows)
 
 
 @pytest.mark.parametrize("pos0,T", [(0, 1), (0, 64), (100, 37), (64, 130), (1000, 200), (4000, 33)])
@@ -82,3 +84,44 @@ def test_prefill_last_row_matches_decode():
     q_last = bf16_tensor(ch.qbits[-1:])
     d, dm, dl = f4.paged_attn_decode_f4(ch.gc, q_last, torch.from_numpy(ch.pt[None]).cuda(), lens, 2096, SM)
     assert_attention_close(o[-1], d.cpu().numpy()[0, 0], "prefill last row vs decode")
+
+
+@pytest.mark.parametrize("sm", [0.0, -1.0 / 16.0, 0.25])
+def test_prefill_logit_scale_signs(sm):
+    """A zero logit scale (uniform weights over each row's causal range), a
+    negative one and a large one."""
+    print(f"prefill sm_scale={sm}", flush=True)
+    ch = Chunk(200, 50, seed=70)
+    o, m, l = ch.run_gpu(sm=sm)
+    ro, rm, rl = ch.run_oracle(sm=sm)
+    assert_attention_close(o, ro, f"prefill sm_scale={sm}")
+    assert_states_close(m, l, rm, rl, f"prefill sm_scale={sm}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("log2_scale", [20, -30])
+def test_prefill_query_far_outside_fp16_range(log2_scale, fp8):
+    """bf16 queries beyond fp16's largest value (x 2^20) or below its smallest
+    normal (x 2^-30), the logit scale compensating, and one all-zero row."""
+    from oracle import fp8 as ofp8
+    print(f"prefill ({'8-bit' if fp8 else 'fp16'}) q x 2^{log2_scale}", flush=True)
+    ch = Chunk(150, 40, seed=71)
+    q = bf16_values(ch.qbits) * 2.0 ** log2_scale  # exact: a power of two within bf16's range
+    q[3] = 0.0
+    qbits = synth.f32_to_bf16_bits(q.astype(np.float32))
+    sm = SM * 2.0 ** -log2_scale
+    if fp8:
+        kn, vn = torch.from_numpy(ch.k_new).cuda(), torch.from_numpy(ch.v_new).cuda()
+        out = f4.paged_attn_prefill_f4_fp8(ch.gc, bf16_tensor(qbits), kn, vn, torch.from_numpy(ch.pt).cuda(),
+                                           ch.pos0, sm)
+        torch.cuda.synchronize()
+        o, m, l = [x.cpu().numpy() for x in out]
+        t = np.arange(ch.pos0, ch.pos0 + ch.T)
+        slots = (ch.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
+        ch.oc.write(ch.k_new, ch.v_new, slots)
+        ro, rm, rl = ofp8.prefill(ch.oc, bf16_values(qbits), ch.pt, ch.pos0, sm)
+    else:
+        o, m, l = ch.run_gpu(qbits=qbits, sm=sm)
+        ro, rm, rl = ch.run_oracle(qbits=qbits, sm=sm)
+    assert_attention_close(o, ro, f"prefill q x 2^{log2_scale}")
+    assert_states_close(m, l, rm, rl, f"prefill q x 2^{log2_scale}")
