@@ -313,7 +313,9 @@ def bench_rows(R, iters=10):
         f4.paged_attn_decode_rows_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=64 * iters) as t:
+    # five or more rows (of 4 query heads per KV head) run on the prefill kernel
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=64 * iters) as t, \
+            f4.KernelTimer(f4.KERNEL_PREFILL, max_launches=64 * iters) as tp:
         e0.record()
         for _ in range(iters):
             f4.paged_attn_decode_rows_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
@@ -323,7 +325,9 @@ def bench_rows(R, iters=10):
     by = decode_algorithmic_bytes(lengths)  # the KV stream of one call, read once per pass
     del L
     return {"workload": f"decode of {R} query rows per lane, 3 x 262,144 tokens, one layer", "rows": R,
-            "call_ms": ms, "kernel_ms_per_call": t.total_ms / iters, "passes_per_call": t.launches // iters,
+            "kernel": "prefill_kernel (one pass, matrix cores)" if tp.launches else "decode_kernel",
+            "call_ms": ms, "kernel_ms_per_call": (t.total_ms + tp.total_ms) / iters,
+            "passes_per_call": (t.launches + tp.launches) // iters,
             "row_kv_tokens_per_s": R * sum(lengths) / (ms / 1e3), "kv_stream_gbs": by / (ms / 1e3) / 1e9}
 
 
@@ -555,7 +559,7 @@ def main():
         torch.cuda.empty_cache()
         extra["gather_bf16"] = bench_gather()
         log("gather:", extra["gather_bf16"])
-        for R in (2, 8):
+        for R in (2, 5, 8):
             torch.cuda.empty_cache()
             extra[f"decode_rows_{R}"] = bench_rows(R)
             log(f"rows {R}:", extra[f"decode_rows_{R}"])

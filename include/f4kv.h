@@ -217,7 +217,11 @@ int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q,
  *   other arguments as paged_attn_decode_f4; the workspace size comes from
  *   paged_attn_decode_rows_f4_workspace_size().
  * The rows of a KV head's query heads are processed together, up to 8 per
- * pass over the pages (Hq / H * R rows; more take several passes).
+ * pass over the pages (Hq / H * R rows; more take several passes).  With
+ * Hq / H == 4, R >= 5 and one window over the whole context (num_windows == 1,
+ * window_tokens == 0), a verification round is a short causal prefill: the
+ * rows then run on the prefill kernel (fp16 matrix cores with exact splits,
+ * one pass over the pages for all R rows), within the same tolerance.
  */
 size_t paged_attn_decode_rows_f4_workspace_size(int32_t B, int32_t R, int32_t Hq, int32_t num_kv_heads,
                                                 int32_t head_dim, int32_t max_context_len,

@@ -155,6 +155,9 @@ size_t paged_attn_decode_rows_f4_workspace_size(int32_t B, int32_t R, int32_t Hq
   if (B <= 0 || R < 1 || R > 8 || Hq <= 0 || num_kv_heads <= 0 || Hq % num_kv_heads != 0 ||
       head_dim != f4kv::kHeadDim || max_context_len < 0 || num_windows <= 0 || window_tokens < 0)
     return 0;
+  if (const int32_t sp = f4kv::rows_prefill_splits(B, R, Hq, num_kv_heads, max_context_len, num_windows,
+                                                   window_tokens))
+    return f4kv::rows_prefill_ws_bytes(B, R, Hq, sp);
   return f4kv::plan_decode(B, R, Hq, num_kv_heads, max_context_len, num_windows, window_tokens).ws_bytes;
 }
 
@@ -193,6 +196,18 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4) ||
       (out_m && !aligned(out_m, 4)) || (out_l && !aligned(out_l, 4)))
     return fail(F4KV_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (const int32_t sp = f4kv::rows_prefill_splits(B, R, Hq, Hkv, max_context_len, num_windows, window_tokens)) {
+    const size_t need = f4kv::rows_prefill_ws_bytes(B, R, Hq, sp);
+    if (need > 0) {
+      if (!workspace || ws_bytes < need)
+        return fail(F4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need,
+                    workspace ? ws_bytes : size_t(0));
+      if (!aligned(workspace, 16)) return fail(F4KV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    }
+    return launched(f4kv::launch_prefill_rows(*cache, q, page_table, context_lens, B, R, Hq, max_pages,
+                                              max_context_len, sm_scale, out, out_m, out_l, workspace, sp, stream),
+                    fn);
+  }
   const f4kv::DecodePlan plan = f4kv::plan_decode(B, R, Hq, Hkv, max_context_len, num_windows, window_tokens);
   if (plan.ws_bytes > 0) {
     if (!workspace || ws_bytes < plan.ws_bytes)

@@ -84,6 +84,17 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
                          float sm_scale, float* out, float* out_m, float* out_l,
                          void* ws, const DecodePlan& plan, hipStream_t s);
 
+// Query rows of B sequences (row r at position ctx[b] - R + r) through the
+// prefill kernel: 4 query heads per KV head, head_dim 256, R <= 8.
+// rows_prefill_splits gives the key splits of such a launch, or 0 when the
+// call stays on the decode kernel; rows_prefill_ws_bytes its workspace.
+int32_t rows_prefill_splits(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
+                            int32_t window_tokens);
+size_t rows_prefill_ws_bytes(int32_t B, int32_t R, int32_t Hq, int32_t splits);
+hipError_t launch_prefill_rows(const f4kv_cache& c, const uint16_t* q, const int32_t* pt, const int32_t* ctx,
+                               int32_t B, int32_t R, int32_t Hq, int32_t max_pages, int32_t max_ctx, float sm_scale,
+                               float* out, float* out_m, float* out_l, void* ws, int32_t kv_splits, hipStream_t s);
+
 struct PrefillPlan {
   int32_t q_tiles;      // query tiles of 32 positions
   int32_t kv_splits;    // workgroups along the key range per query tile

@@ -68,6 +68,13 @@ struct PrefillArgs {
   int32_t T, Hq, Hkv, num_pages, max_pages, pos0;
   int32_t kv_splits;
   float qk_scale;  // sm_scale * log2(e)
+  // Several sequences in one launch (query rows of a verification round):
+  // grid x = sequence * q_tiles + tile; with ctx set, sequence b's T rows sit
+  // at positions ctx[b] - T .. ctx[b] - 1 (ctx clamped to [0, max_ctx]; rows
+  // at negative positions attend to nothing), its page-table row starts at
+  // b * pt_stride and its queries and outputs follow those of sequence b - 1.
+  const int32_t* ctx;
+  int32_t max_ctx, q_tiles, pt_stride, B;
 };
 
 struct __align__(16) PrefillSmem {
@@ -220,27 +227,33 @@ __device__ __forceinline__ void v_piece(PrefillSmem& sm, const VRaw& r, const VS
 template <bool VT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ pt) {
   __shared__ PrefillSmem sm;
-  const int qt = blockIdx.x;     // query tile
+  const int seq = blockIdx.x / a.q_tiles;          // sequence
+  const int qt = blockIdx.x - seq * a.q_tiles;     // query tile
   const int g = blockIdx.y;      // KV head
   const int split = blockIdx.z;  // key-range split
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
+  int pos0 = a.pos0;
+  if (a.ctx) pos0 = min(max(a.ctx[seq], 0), a.max_ctx) - a.T;
+  pos0 = __builtin_amdgcn_readfirstlane(pos0);
+  pt += static_cast<int64_t>(seq) * a.pt_stride;
 
   // column tile c of this wave: positions (wave*kCT + c)*8 + col/4, head col % 4
   int qi[kCT], qpos[kCT];
-  bool qvalid[kCT];
+  bool qexists[kCT], qvalid[kCT];
   const int hq = g * kG + (col & 3);
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
     qi[c] = qt * kQPos + (wave * kCT + c) * 8 + col / 4;
-    qvalid[c] = qi[c] < a.T;
-    qpos[c] = a.pos0 + qi[c];
+    qpos[c] = pos0 + qi[c];
+    qexists[c] = qi[c] < a.T;
+    qvalid[c] = qexists[c] && qpos[c] >= 0;  // a row at a negative position attends to nothing
   }
-  const int qpos_first = a.pos0 + qt * kQPos;  // no key below it needs a mask
+  const int qpos_first = pos0 + qt * kQPos;  // no key below it needs a mask
 
   // key pages this workgroup covers: up to the tile's last position, split evenly
-  const int tile_last = min(a.T, (qt + 1) * kQPos) - 1;
-  const int npages = (a.pos0 + tile_last) / kPage + 1;
+  const int tile_last = pos0 + min(a.T, (qt + 1) * kQPos) - 1;
+  const int npages = tile_last < 0 ? 0 : tile_last / kPage + 1;
   const int per = (npages + a.kv_splits - 1) / a.kv_splits;
   // uniform: the division runs on the vector unit, keep the range in scalar registers
   const int pbeg = __builtin_amdgcn_readfirstlane(split * per);
@@ -260,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   float qk;
   {
     static_assert(kCT == 1, "one query row per lane");
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(qvalid[0] ? qi[0] : 0) * a.Hq + hq) * kHeadDim;
+    const uint16_t* qrow =
+        a.q + ((static_cast<int64_t>(seq) * a.T + (qexists[0] ? qi[0] : 0)) * a.Hq + hq) * kHeadDim;
     uint4 raw[16];
     float qmax = 0.0f;
 #pragma unroll
@@ -550,15 +564,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
 
 
   // ---- epilogue: this lane's two query rows ----
-  const int R = a.T * a.Hq;
+  const int64_t R = static_cast<int64_t>(a.B) * a.T * a.Hq;
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
     // restore the exact maximum: the normalised output is unchanged, the sum scales
     const float f = s_max[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[c] - s_max[c]);
     const float Lr = l_lane[c] + __shfl_xor(l_lane[c], 32, 64);  // in units of exp2(m_run)
     const float L = Lr * f;
-    if (!qvalid[c]) continue;
-    const int64_t row = static_cast<int64_t>(split) * R + static_cast<int64_t>(qi[c]) * a.Hq + hq;
+    if (!qexists[c]) continue;
+    const int64_t row = split * R + (static_cast<int64_t>(seq) * a.T + qi[c]) * a.Hq + hq;
     const float inv = Lr > 0.0f ? 1.0f / (Lr * 2048.0f) : 0.0f;  // P was carried times 2^11
     float* dst = a.o + row * kHeadDim;
 #pragma unroll
@@ -586,11 +600,15 @@ PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0, int32
   PrefillPlan p;
   p.q_tiles = (T + tile_positions - 1) / tile_positions;
   const int64_t total_pages = (static_cast<int64_t>(pos0) + T + kPage - 1) / kPage;
-  // split the key range until the grid reaches the target when the range is long
+  // split the key range until the grid reaches the target when the range is
+  // long (a short chunk over a long window gets as many splits as it needs to
+  // fill the device), keeping at least 16 pages per split
+  // (rounded down: a grid just past a whole number of rounds would add a
+  // round of a few workgroups that takes as long as a full one)
   const int64_t wgs = static_cast<int64_t>(p.q_tiles) * Hkv;
-  int64_t splits = (target_wgs + wgs - 1) / std::max<int64_t>(wgs, 1);
+  int64_t splits = target_wgs / std::max<int64_t>(wgs, 1);
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, total_pages / 16));
-  p.kv_splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, 16)));
+  p.kv_splits = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, 1024)));
   const int64_t R = static_cast<int64_t>(T) * Hq;
   p.ws_bytes = p.kv_splits > 1 ? static_cast<size_t>(p.kv_splits) * R * (kHeadDim + 2) * sizeof(float) : 0;
   return p;
@@ -615,6 +633,11 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
   a.pos0 = pos0;
   a.kv_splits = plan.kv_splits;
   a.qk_scale = sm_scale * kLog2e;
+  a.ctx = nullptr;
+  a.max_ctx = 0;
+  a.q_tiles = plan.q_tiles;
+  a.pt_stride = 0;
+  a.B = 1;
   const int64_t R = static_cast<int64_t>(T) * Hq;
   float* pm = nullptr;
   float* pl = nullptr;
@@ -640,6 +663,80 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
   timing_end(F4KV_KERNEL_PREFILL, s);
   if (e != hipSuccess || plan.kv_splits == 1) return e;
   return launch_merge(pm, pl, a.o, plan.kv_splits, static_cast<int32_t>(R), kHeadDim, out, out_m, out_l, s);
+}
+
+// Five or more rows of a group of 4 query heads (20 or more rows per KV head,
+// three or more passes of the decode kernel over the pages) go through this
+// kernel, whose workgroup reads each page once for up to 32 rows with
+// matrix-core products: a verification round is a short causal prefill over
+// the cache.  Whole-context calls only.
+int32_t rows_prefill_splits(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
+                            int32_t window_tokens) {
+  if (R < 5 || R > 8 || Hq != 4 * Hkv || num_windows != 1 || window_tokens != 0 || B <= 0) return 0;
+  const int64_t wgs = static_cast<int64_t>(B) * Hkv;
+  const int64_t total_pages = (static_cast<int64_t>(max_ctx) + kPage - 1) / kPage;
+  int64_t splits = 512 / wgs;  // at most two rounds of one workgroup per CU, as the prefill plans
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, total_pages / 16));
+  return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(splits, 1024)));
+}
+
+size_t rows_prefill_ws_bytes(int32_t B, int32_t R, int32_t Hq, int32_t splits) {
+  const int64_t rows = static_cast<int64_t>(B) * R * Hq;
+  return splits > 1 ? static_cast<size_t>(splits) * rows * (kHeadDim + 2) * sizeof(float) : 0;
+}
+
+// R <= 8 query rows of each of B sequences, row r at position ctx[b] - R + r,
+// causal over the cache: one query tile per sequence (only the first wave's
+// rows exist), the key range split kv_splits ways and folded by the merge.
+hipError_t launch_prefill_rows(const f4kv_cache& c, const uint16_t* q, const int32_t* pt, const int32_t* ctx,
+                               int32_t B, int32_t R, int32_t Hq, int32_t max_pages, int32_t max_ctx, float sm_scale,
+                               float* out, float* out_m, float* out_l, void* ws, int32_t kv_splits, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  PrefillArgs a;
+  a.k_nib = c.k_nib;
+  a.k_scale = c.k_scale;
+  a.v_nib = c.v_nib;
+  a.v_scale = c.v_scale;
+  a.q = q;
+  a.pt = pt;
+  a.T = R;
+  a.Hq = Hq;
+  a.Hkv = c.num_kv_heads;
+  a.num_pages = c.num_pages;
+  a.max_pages = max_pages;
+  a.pos0 = 0;
+  a.kv_splits = kv_splits;
+  a.qk_scale = sm_scale * kLog2e;
+  a.ctx = ctx;
+  a.max_ctx = max_ctx;
+  a.q_tiles = 1;
+  a.pt_stride = max_pages;
+  a.B = B;
+  const int64_t rows = static_cast<int64_t>(B) * R * Hq;
+  float* pm = nullptr;
+  float* pl = nullptr;
+  if (kv_splits > 1) {
+    float* base = static_cast<float*>(ws);
+    a.o = base;
+    pm = base + static_cast<size_t>(kv_splits) * rows * kHeadDim;
+    pl = pm + static_cast<size_t>(kv_splits) * rows;
+    a.m = pm;
+    a.l = pl;
+  } else {
+    a.o = out;
+    a.m = out_m;
+    a.l = out_l;
+  }
+  const dim3 grid(B, a.Hkv, kv_splits);
+  timing_begin(F4KV_KERNEL_PREFILL, s);
+  if (c.v_scale_per_token)
+    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kThreads), 0, s, a, pt);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kThreads), 0, s, a, pt);
+  hipError_t e = hipGetLastError();
+  timing_end(F4KV_KERNEL_PREFILL, s);
+  if (e != hipSuccess || kv_splits == 1) return e;
+  return launch_merge(pm, pl, a.o, kv_splits, static_cast<int32_t>(rows), kHeadDim, out, out_m, out_l, s);
 }
 
 }  // namespace f4kv

@@ -29,9 +29,10 @@ def _run(ps, R, Hq, seed, W=1, wt=0):
     return (out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()), (ro, rm, rl), bits
 
 
-@pytest.mark.parametrize("R", [2, 3, 8])
+@pytest.mark.parametrize("R", [2, 3, 5, 8])
 def test_rows_group_of_four(R):
-    # 4 query heads per KV head: 2 rows per pass over the pages, so 3 and 8 rows take several passes
+    # 4 query heads per KV head: 2 rows per pass over the pages, so 3 rows take two passes; 5 and more
+    # rows of a whole-context call go through the prefill kernel
     ps = PagedSet([700, 130, 64 * 20 + 5], Hkv=4, seed=900 + R)
     (o, m, l), (ro, rm, rl), _ = _run(ps, R, 16, R)
     assert_attention_close(o, ro, f"R={R}")
@@ -65,3 +66,36 @@ def test_one_row_is_plain_decode_and_last_row_matches_decode():
     torch.cuda.synchronize()
     assert torch.equal(one[:, :, 0], dec)
     assert torch.allclose(three[:, :, 2], dec, rtol=0, atol=1e-5 * float(dec.abs().max()))
+
+
+@pytest.mark.parametrize("v_per_token", [False, True])
+def test_rows_through_the_prefill_kernel_short_contexts(v_per_token):
+    """Rows of whole-context calls with R >= 5 (group of 4) run on the prefill
+    kernel: contexts shorter than R leave the leading rows empty (the merge
+    identity), an empty context all of them."""
+    print(f"rows via prefill, short contexts, v_per_token={v_per_token}", flush=True)
+    ps = PagedSet([3, 1, 1500, 64, 0], Hkv=4, seed=940, v_per_token=v_per_token)
+    (o, m, l), (ro, rm, rl), _ = _run(ps, 8, 16, 40)
+    assert np.all(np.isneginf(m[0, 0, :5])) and np.all(l[0, 0, :5] == 0) and not o[0, 0, :5].any()
+    assert np.all(np.isneginf(m[0, 4])) and np.all(l[0, 4] == 0) and not o[0, 4].any()
+    assert_attention_close(o, ro, "rows via prefill, short contexts")
+    assert_states_close(m, l, rm, rl, "rows via prefill, short contexts")
+
+
+def test_rows_through_the_prefill_kernel_agree_with_the_decode_kernel():
+    """The same 6 rows through the prefill kernel (whole context) and through the
+    decode kernel (one window that covers the context)."""
+    print("rows via prefill vs decode kernel", flush=True)
+    ps = PagedSet([2000, 300, 4097], Hkv=4, seed=950)
+    bits, qv = _q(3, 6, 16, 50)
+    pt, lens = ps.gpu_page_table(), ps.gpu_lengths()
+    a = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), pt, lens, 4097, SM)
+    b = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), pt, lens, 4097, SM, num_windows=1,
+                                     window_tokens=64 * 65)
+    torch.cuda.synchronize()
+    a = [x.cpu().numpy() for x in a]
+    b = [x.cpu().numpy() for x in b]
+    assert_attention_close(a[0], b[0], "prefill kernel vs decode kernel")
+    assert_states_close(a[1], a[2], b[1], b[2], "prefill kernel vs decode kernel")
+    ro, rm, rl = oatt.decode_rows(ps.oc, qv, ps.pt, ps.lengths, SM)
+    assert_attention_close(a[0], ro, "prefill kernel vs oracle")
