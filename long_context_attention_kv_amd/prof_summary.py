@@ -1,10 +1,12 @@
 """Summaries of rocprofv3 CSV output for this library's kernels.
 
-    python -m long_context_attention_kv_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..." [--timed NAME:FIRST:COUNT]
+    python -m long_context_attention_kv_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..." \\
+            [--timed NAME:FIRST:COUNT] [--shapes NAME;NAME]
         per-kernel time table (the library's kernels first) from a
         ``rocprofv3 --kernel-trace --stats -f csv`` run; --timed adds the
         average of dispatches FIRST .. FIRST + COUNT - 1 of kernel NAME from
-        the run's kernel trace (e.g. the launches a benchmark timed).
+        the run's kernel trace (e.g. the launches a benchmark timed); --shapes
+        splits the named kernels' dispatches by launch grid.
 
     python -m long_context_attention_kv_amd.prof_summary traffic --fetch CSV --write CSV \\
             --copy-bytes N --kernel NAME --source FILE --cmd-fetch "..." --cmd-write "..."
@@ -47,7 +49,30 @@ def timed_window(trace_path: str, spec: str) -> str:
             f"average {statistics.mean(d):.1f} us, min {min(d):.1f}, max {max(d):.1f}.")
 
 
-def stats_table(path: str, cmd: str, timed: str = "") -> str:
+def launch_shapes(trace_path: str, names) -> str:
+    """Per-grid rows of the named kernels (one kernel serving two entry points,
+    say), from a kernel-trace CSV."""
+    groups = {}
+    for r in csv.DictReader(open(trace_path)):
+        if "f4kv::" not in r["Kernel_Name"] or _short(r["Kernel_Name"]) not in names:
+            continue
+        grid = tuple(int(r[f"Grid_Size_{a}"]) // max(1, int(r[f"Workgroup_Size_{a}"])) for a in "XYZ")
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault(_short(r["Kernel_Name"]), {}).setdefault(grid, []).append(d)
+    lines = []
+    for name, by_grid in sorted(groups.items()):
+        for grid, d in sorted(by_grid.items(), key=lambda kv: -statistics.mean(kv[1])):
+            lines.append(f"| `{name}` | {grid[0]} x {grid[1]} x {grid[2]} | {len(d)} | {statistics.mean(d):.1f} | "
+                         f"{min(d):.1f} | {max(d):.1f} |")
+    if not lines:
+        return ""
+    return "\n".join(["", "Launch grids (workgroups x, y, z) of " + ", ".join(f"`{n}`" for n in names)
+                      + ", from the kernel trace:", "",
+                      "| kernel | grid | calls | avg us | min us | max us |", "|---|---|---:|---:|---:|---:|"]
+                     + lines)
+
+
+def stats_table(path: str, cmd: str, timed: str = "", shapes=()) -> str:
     rows = list(csv.DictReader(open(path)))
     lines = ["# Kernel time summary", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | share of GPU time |",
@@ -60,8 +85,10 @@ def stats_table(path: str, cmd: str, timed: str = "") -> str:
                      f"{float(r['Percentage']):.2f}% |")
     if len(other) > 5:
         lines.append(f"| ({len(other) - 5} more kernels of the harness) | | | | | |")
+    trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
+    if shapes:
+        lines.append(launch_shapes(trace, shapes))
     if timed:
-        trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
         lines += ["", timed_window(trace, timed)]
     return "\n".join(lines) + "\n"
 
@@ -138,6 +165,7 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("--cmd", required=True)
     s.add_argument("--timed", default="", help="NAME:FIRST:COUNT: also average these dispatches of NAME")
+    s.add_argument("--shapes", default="", help="NAME[;NAME]: also list these kernels' dispatches per launch grid")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -147,7 +175,10 @@ def main(argv=None):
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     a = ap.parse_args(argv)
-    sys.stdout.write(stats_table(a.csv, a.cmd, a.timed) if a.what == "stats" else traffic(a))
+    if a.what == "stats":
+        sys.stdout.write(stats_table(a.csv, a.cmd, a.timed, [n for n in a.shapes.split(";") if n]))
+    else:
+        sys.stdout.write(traffic(a))
 
 
 if __name__ == "__main__":

@@ -92,3 +92,26 @@ def test_committed_traffic_figure_belongs_to_the_current_decode_source():
     assert t is not None, "profiles/decode_kernel_traffic.md was taken from another decode.hip"
     # within 1% of the algorithmic bytes of one launch (no wasted re-reads)
     assert abs(t - 906_092_928) / 906_092_928 < 0.01
+
+
+def test_launch_shapes_split_one_kernel_by_grid(tmp_path):
+    trace = tmp_path / "t_kernel_trace.csv"
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"] + [f"{k}_Size_{a}" for k in ("Workgroup", "Grid")
+                                                                  for a in "XYZ"]
+    pre = "void f4kv::(anonymous namespace)::prefill_kernel<false>(f4kv::PrefillArgs, int const*)"
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        # grid sizes in work-items along x (256 per workgroup), workgroups along y and z
+        for start, dur, gx, gz in [(0, 9000, 64 * 256, 2), (10, 1000, 3 * 256, 42), (20, 3000, 3 * 256, 42),
+                                   (30, 11000, 64 * 256, 2)]:
+            w.writerow({"Kernel_Name": pre, "Start_Timestamp": start, "End_Timestamp": start + dur,
+                        "Workgroup_Size_X": 256, "Workgroup_Size_Y": 1, "Workgroup_Size_Z": 1,
+                        "Grid_Size_X": gx, "Grid_Size_Y": 4, "Grid_Size_Z": gz})
+        w.writerow({"Kernel_Name": DECODE, "Start_Timestamp": 0, "End_Timestamp": 5, "Workgroup_Size_X": 256,
+                    "Workgroup_Size_Y": 1, "Workgroup_Size_Z": 1, "Grid_Size_X": 256, "Grid_Size_Y": 4,
+                    "Grid_Size_Z": 1})
+    out = ps.launch_shapes(str(trace), ["prefill_kernel<false>"])
+    assert "| `prefill_kernel<false>` | 64 x 4 x 2 | 2 | 10.0 | 9.0 | 11.0 |" in out
+    assert "| `prefill_kernel<false>` | 3 x 4 x 42 | 2 | 2.0 | 1.0 | 3.0 |" in out
+    assert "decode_kernel" not in out.split("from the kernel trace:")[1]
