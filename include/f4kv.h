@@ -334,8 +334,11 @@ int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const
  * events, returns the summed kernel time and the number of timed launches, and
  * ends the timing.  Launches beyond max_launches are not timed.
  *   kernel  F4KV_KERNEL_DECODE: the split-K attention kernel of
- *           paged_attn_decode_f4 (not its query preparation or fold);
- *           F4KV_KERNEL_PREFILL: the attention kernel of paged_attn_prefill_f4.
+ *           paged_attn_decode_f4 and paged_attn_decode_rows_f4 (not its query
+ *           preparation or fold);
+ *           F4KV_KERNEL_PREFILL: the attention kernel of paged_attn_prefill_f4,
+ *           which also runs the verification rounds of paged_attn_decode_rows_f4
+ *           that go to it (R >= 5, see there).
  *           F4KV_KERNEL_PREFILL_FP8: that of paged_attn_prefill_f4_fp8.
  * Timing one kernel from two host threads at once is not supported.
  */
