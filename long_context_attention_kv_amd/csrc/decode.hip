@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
       if (mx > 0.0f) {
         int ex;
         frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
-        e = 11 - ex;      // scaled max in [2^10, 2^11)
+        e = 11 - ex;      // scaled max in [2^10, 2^11); up to 144 for the smallest bf16 subnormals
       }
       qexp[h] = e;
       P.kscale[h] = ldexpf(qk_scale, 24 - e);
@@ -347,9 +347,11 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
     const int c = r / 16, k = (r / 4) % 4, p = r % 4;
     // pair p of dword k holds channels (base + p, base + p + 4); odd p are the x16 slots
     const int base = 32 * c + 8 * k + p;
-    const float sc = ldexpf((p & 1) ? 0.0625f : 1.0f, qexp[h]);
-    const _Float16 lo = static_cast<_Float16>(qf[h][base] * sc);
-    const _Float16 hi = static_cast<_Float16>(qf[h][base + 4] * sc);
+    // the exponent goes to the values themselves (a factor 2^e alone would
+    // overflow for rows of tiny queries, whose e exceeds 127)
+    const int ex = qexp[h] - ((p & 1) ? 4 : 0);
+    const _Float16 lo = static_cast<_Float16>(ldexpf(qf[h][base], ex));
+    const _Float16 hi = static_cast<_Float16>(ldexpf(qf[h][base + 4], ex));
     P.pair[h][c][k][p] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
@@ -359,8 +361,8 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
     for (int d = 0; d < kBlock; ++d) {
       const float v = qf[h][32 * c + d];
       // the value each channel contributes through its fp16 operand
-      const float rep = (d & 1) ? 16.0f * static_cast<float>(static_cast<_Float16>(v * ldexpf(0.0625f, qexp[h])))
-                                : static_cast<float>(static_cast<_Float16>(v * ldexpf(1.0f, qexp[h])));
+      const float rep = (d & 1) ? 16.0f * static_cast<float>(static_cast<_Float16>(ldexpf(v, qexp[h] - 4)))
+                                : static_cast<float>(static_cast<_Float16>(ldexpf(v, qexp[h])));
       sum += rep;
     }
     P.qinit[h][c] = -8.0f * ldexpf(sum, -24);

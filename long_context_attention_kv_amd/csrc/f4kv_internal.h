@@ -102,7 +102,7 @@ struct PrefillPlan {
 };
 
 // tile_positions query positions per workgroup; the key range is split until
-// the grid has about target_wgs workgroups (at most 16 splits, each >= 16 pages).
+// the grid has about target_wgs workgroups (at most 1024 splits, each >= 16 pages).
 PrefillPlan plan_prefill(int32_t T, int32_t Hq, int32_t Hkv, int32_t pos0, int32_t tile_positions,
                          int32_t target_wgs);
 // The plans of the two prefill kernels (fp16: 32 positions, two workgroup

@@ -54,7 +54,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
   } else {
     const int64_t pos = a.pos0 + t;
     const int32_t pg = a.page_table[pos / kPage];
-    slot = pg < 0 ? -1 : pg * kPage + static_cast<int32_t>(pos % kPage);
+    // out-of-range page ids (negative or >= num_pages) write nothing; the
+    // compare comes before the multiply, which would overflow for ids >= 2^25
+    if (static_cast<uint32_t>(pg) >= static_cast<uint32_t>(a.num_pages)) return;
+    slot = pg * kPage + static_cast<int32_t>(pos % kPage);
   }
   if (slot < 0 || slot >= static_cast<int64_t>(a.num_pages) * kPage) return;
   const int page = slot / kPage;

@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 CSV output for this library's kernels.
 
-    python -m long_context_attention_kv_amd.prof_summary stats KERNEL_STATS_CSV --cmd "..." \\
+    python prof_summary.py stats KERNEL_STATS_CSV --cmd "..." \\
             [--timed NAME:FIRST:COUNT] [--shapes NAME;NAME]
         per-kernel time table (the library's kernels first) from a
         ``rocprofv3 --kernel-trace --stats -f csv`` run; --timed adds the
@@ -8,7 +8,7 @@
         the run's kernel trace (e.g. the launches a benchmark timed); --shapes
         splits the named kernels' dispatches by launch grid.
 
-    python -m long_context_attention_kv_amd.prof_summary traffic --fetch CSV --write CSV \\
+    python prof_summary.py traffic --fetch CSV --write CSV \\
             --copy-bytes N --kernel NAME --source FILE --cmd-fetch "..." --cmd-write "..."
         HBM bytes per launch of one kernel from a ``--pmc FETCH_SIZE`` run and a
         ``--pmc WRITE_SIZE`` run (counter values in KiB per dispatch).  Each

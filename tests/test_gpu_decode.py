@@ -79,14 +79,24 @@ def test_logit_scale_signs(sm):
     assert_states_close(m, l, rm, rl, f"sm_scale {sm}")
 
 
-@pytest.mark.parametrize("log2_scale", [20, -30])
+@pytest.mark.parametrize("log2_scale", [20, -30, -125])
 def test_query_far_outside_fp16_range(log2_scale):
-    """bf16 queries beyond fp16's largest value (x 2^20) or below its smallest
-    normal (x 2^-30); the logit scale compensates, so the weights stay the same."""
+    """bf16 queries beyond fp16's largest value (x 2^20), below its smallest
+    normal (x 2^-30) or at the bottom of bf16's own range (x 2^-125, partly
+    subnormal); the logit scale compensates, so the weights stay the same."""
     ps = PagedSet([500], Hkv=4, seed=13)
     (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=13, q_scale=2.0 ** log2_scale, sm=SM * 2.0 ** -log2_scale)
     assert_attention_close(o, ro, f"q x 2^{log2_scale}")
     assert_states_close(m, l, rm, rl, f"q x 2^{log2_scale}")
+
+
+def test_tiny_query_gives_uniform_weights():
+    """A query of bf16 values near 2^-125 with the plain logit scale: every
+    logit is ~0, so the weights are uniform (the output is the mean value)."""
+    ps = PagedSet([900, 130], Hkv=4, seed=14)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=14, q_scale=2.0 ** -125)
+    assert_attention_close(o, ro, "tiny query")
+    assert_states_close(m, l, rm, rl, "tiny query")
 
 
 def test_outliers_and_scaled_values():

@@ -6,9 +6,9 @@ the query, F4 writes, then the decode (or prefill) call.  The fp64 oracle
 cannot redo a whole 262,144-token layer of 3 lanes in seconds, so it recomputes
 a sample: chosen (sequence, KV head) pairs -- all 4 query heads of the group,
 every channel -- from the same seeded draws, with its own table, rotation,
-quantiser and attention.  Where even a sample is too long for the oracle
-(1,048,576 tokens), it checks sampled windows, and the fold of all windows is
-checked against the unwindowed call (log-sum-exp identity) on the GPU.
+quantiser and attention.  At 1,048,576 tokens it recomputes one KV head over
+all 16 windows and folds them with its own merge: the final answer of the
+call is checked against it.
 
 Draws: K and V of sequence b, KV head h are N(0,1) fp32 in blocks of 65,536
 tokens, each block from its own seeded stream, so the oracle regenerates only
@@ -181,15 +181,35 @@ def test_config2_1048576_in_16_windows():
     W, wt, n = 16, 65536, 1048576
     layer = Layer(2, [n], 4.0, outliers=False)
     out, m, l = decode_call(layer, W=W, wt=wt)
-    for w, h in [(3, 1), (15, 3)]:  # window 15 ends at position 1,048,575
-        K, V = layer.oracle_kv(0, h, t_begin=w * wt, t_end=(w + 1) * wt)
-        ref = oatt.decode_head_from_values(layer.oracle_query(0, h), K, V, SM)
-        check_group(out[w, 0, h * G:(h + 1) * G], m[w, 0, h * G:(h + 1) * G], l[w, 0, h * G:(h + 1) * G],
-                    (ref[0][0], ref[1][0], ref[2][0]), f"window {w} kv head {h}")
-    # the 16 windows folded by lse_merge give the unwindowed answer
+    # the 16 windows folded by lse_merge: the call's final answer
     fo, fm, fl = f4.lse_merge(torch.from_numpy(m).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(out).cuda())
-    wo, wm, wl = decode_call(layer)
     fo, fm, fl = fo.cpu().numpy(), fm.cpu().numpy(), fl.cpu().numpy()
+    # oracle: KV head 3, all 4 of its query heads, every window over the whole
+    # 1,048,576 tokens (its own draws, table, rotation, quantiser and
+    # attention), folded by its own log-sum-exp merge
+    h = 3
+    q = layer.oracle_query(0, h)
+
+    def window_state(w):
+        K, V = layer.oracle_kv(0, h, t_begin=w * wt, t_end=(w + 1) * wt)
+        return oatt.decode_head_from_values(q, K, V, SM)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        states = list(ex.map(window_state, range(W)))
+    for w in range(W):
+        ro, rm, rl = states[w]
+        check_group(out[w, 0, h * G:(h + 1) * G], m[w, 0, h * G:(h + 1) * G], l[w, 0, h * G:(h + 1) * G],
+                    (ro[0], rm[0], rl[0]), f"window {w} kv head {h}")
+    for i in range(G):
+        M, L, O = oatt.merge_states([st[1][0, i] for st in states], [st[2][0, i] for st in states],
+                                    [st[0][0, i] for st in states])
+        what = f"fold of 16 windows, query head {h * G + i}"
+        assert_attention_close(fo[0, h * G + i], O, what)
+        assert abs(fm[0, h * G + i] - M) <= 1e-3 * max(1.0, abs(M)), f"{what}: m"
+        assert abs(fl[0, h * G + i] - L) <= 2e-3 * L, f"{what}: l"
+    # and the fold equals the unwindowed call (log-sum-exp identity) for every head
+    wo, wm, wl = decode_call(layer)
     assert_attention_close(fo, wo[0], "fold of 16 windows vs whole context")
     assert np.all(np.abs(fm - wm[0]) <= 1e-5 * np.maximum(1.0, np.abs(wm[0])))
     assert np.all(np.abs(fl - wl[0]) <= 1e-4 * wl[0])

@@ -79,3 +79,36 @@ def test_prefill_drops_out_of_range_pages(fp8):
             ro, rm, rl = oatt.decode_head_from_values(qv[i, 4 * g:4 * g + 4], K[:n][keep[:n]], V[:n][keep[:n]], SM)
             assert_attention_close(o[i, 4 * g:4 * g + 4], ro[0], f"prefill row {i} kv head {g}")
             assert_states_close(m[i, 4 * g:4 * g + 4], l[i, 4 * g:4 * g + 4], rm[0], rl[0], f"prefill row {i} g={g}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_write_skips_huge_page_ids(fp8):
+    """The chunk's own pages carry ids 2^26 and 2^26 + 1: the in-call write must
+    leave every cell of the pool unchanged (an id times 64 overflows int32 and
+    would wrap onto a live page), and the attention drops those pages."""
+    print(f"prefill ({'8-bit' if fp8 else 'fp16'}) writing through page ids 2^26, 2^26 + 1", flush=True)
+    ch = Chunk(128, 128, seed=881)
+    pt_gpu = ch.pt.copy()
+    pt_gpu[2] = 1 << 26
+    pt_gpu[3] = (1 << 26) + 1
+    before = [t.clone() for t in (ch.gc.k_nib, ch.gc.k_scale, ch.gc.v_nib, ch.gc.v_scale)]
+    fn = f4.paged_attn_prefill_f4_fp8 if fp8 else f4.paged_attn_prefill_f4
+    o, m, l = fn(ch.gc, bf16_tensor(ch.qbits), torch.from_numpy(ch.k_new).cuda(), torch.from_numpy(ch.v_new).cuda(),
+                 torch.from_numpy(pt_gpu).cuda(), ch.pos0, SM)
+    torch.cuda.synchronize()
+    after = (ch.gc.k_nib, ch.gc.k_scale, ch.gc.v_nib, ch.gc.v_scale)
+    for name, a, b in zip(("k_nib", "k_scale", "v_nib", "v_scale"), before, after):
+        assert torch.equal(a, b), f"{name} changed"
+    # every row sees the 128 cached tokens only
+    o = o.cpu().numpy()
+    qv = bf16_values(ch.qbits)
+    for i in range(0, ch.T, 9):
+        if fp8:
+            # the 8-bit model of a query at position 127: the same 128 keys, the same groups
+            ro, _, _ = ofp8.prefill(ch.oc, qv[i:i + 1], ch.pt[:2], ch.pos0 - 1, SM)
+            assert_attention_close(o[i], ro[0], f"8-bit prefill row {i}")
+            continue
+        for g in range(4):
+            K, V = oatt.gather_values(ch.oc, ch.pt, ch.pos0, g)
+            ro, _, _ = oatt.decode_head_from_values(qv[i, 4 * g:4 * g + 4], K, V, SM)
+            assert_attention_close(o[i, 4 * g:4 * g + 4], ro[0], f"prefill row {i} kv head {g}")

@@ -9,7 +9,7 @@ from types import SimpleNamespace
 
 import pytest
 
-from long_context_attention_kv_amd import prof_summary as ps
+import prof_summary as ps
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DECODE = "void f4kv::(anonymous namespace)::decode_kernel<4, false>(f4kv::DecodeArgs, f4kv::QPrep<4> const*)"
