@@ -50,6 +50,7 @@ constexpr int kWRow = 68;  // fp32 weights per (head, block) row: 64 tokens + 16
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the running max by
+constexpr float kInvU16 = 1.0f / 65535.0f;
 
 // Query operands of one (sequence, KV head), prepared once per call and read by
 // the decode kernel with scalar loads (the same for every lane).
@@ -260,6 +261,27 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+// Max over each group of 8 consecutive lanes, returned in all 8.
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  return x;
+}
+
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+// Two values in [0, 1] to unsigned 16-bit fixed point, nearest (v_cvt_pknorm_u16_f32):
+// lo = nearest(a 65535), hi = nearest(b 65535).
+__device__ __forceinline__ uint32_t pknorm_u16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_u16(a, b));
+}
+
+// a.lo b.lo + a.hi b.hi + c on unsigned 16-bit pairs, 32-bit accumulate (v_dot2_u32_u16).
+__device__ __forceinline__ uint32_t udot2(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -421,6 +443,13 @@ __device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, 
 }
 
 static_assert((kWRow * 4) % 16 == 0, "weight rows must be 16-byte aligned");
+
+// The 16-bit weights of (wave, head, block): 64 tokens in the first half of
+// that fp32 weight row.
+template <int G>
+__device__ __forceinline__ uint16_t* urow(DecodeSmem<G>& sm, int wave, int h, int c) {
+  return reinterpret_cast<uint16_t*>(&sm.u.w[wave][h][c][0]);
+}
 
 // VT: V scales are one per token and head (v_scale [P][H][64]) instead of one
 // per 32 values; the weight of a token is then the same for all blocks, so a
@@ -601,51 +630,85 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       }
     }
     lds_wave_sync();
-    const int wrow = VT ? 0 : cj;  // weight row of this lane's value block
+    const int wrow = VT ? 0 : cj;  // fp32 weight row of this lane's value block
 
-    // values: lane = channels 4*lane .. 4*lane+3 (block cj); this wave's VALU
-    // stream goes first while it holds its operands
+    // Weights to 16-bit fixed point.  The 8 lanes of block cj share the row of
+    // the block's 64 weights per head; lane sub converts tokens 8 sub .. 8 sub
+    // + 7.  The row's largest weight w_max = f 2^e (f in [1/2, 1)) sets the
+    // unit 2^e / 65535, so u = nearest(w 2^-e 65535) keeps 16 bits for the
+    // page's dominant tokens and an absolute error of at most 2^(e-17) for the
+    // rest; the sums of u n over the page are exact in 32-bit integers.  The
+    // 16-bit rows overwrite the first half of the fp32 rows once every lane of
+    // the wave has read its part (LDS serves one wave's instructions in order).
+    float4_t wx[G], wy[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      wx[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8]);
+      wy[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8 + 4]);
+    }
+    lds_wave_sync();
+    float funit[G];  // value of one unit of u in the units of the value products (n 2^-24)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float4_t x = wx[h], y = wy[h];
+      const float mx = max8(fmaxf(fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)), fmaxf(fmaxf(y.x, y.y), fmaxf(y.z, y.w))));
+      const int e = __builtin_amdgcn_frexp_expf(mx);  // 0 when the row is all zero
+      uint4 u;
+      u.x = pknorm_u16(__builtin_amdgcn_ldexpf(x.x, -e), __builtin_amdgcn_ldexpf(x.y, -e));
+      u.y = pknorm_u16(__builtin_amdgcn_ldexpf(x.z, -e), __builtin_amdgcn_ldexpf(x.w, -e));
+      u.z = pknorm_u16(__builtin_amdgcn_ldexpf(y.x, -e), __builtin_amdgcn_ldexpf(y.y, -e));
+      u.w = pknorm_u16(__builtin_amdgcn_ldexpf(y.z, -e), __builtin_amdgcn_ldexpf(y.w, -e));
+      *reinterpret_cast<uint4*>(&urow(sm, wave, h, cj)[sub * 8]) = u;
+      // "- 8" correction, part 1: this lane's 8 tokens of the block's
+      // (rounded) weights; the sum over the lanes waits for the epilogue
+      const uint32_t usum = udot2(u.x, 0x00010001u, udot2(u.y, 0x00010001u,
+                                  udot2(u.z, 0x00010001u, udot2(u.w, 0x00010001u, 0u))));
+      wpart[h] = fmaf(static_cast<float>(usum), __builtin_amdgcn_ldexpf(kInvU16, e), wpart[h]);
+      funit[h] = __builtin_amdgcn_ldexpf(kInvU16, e - 24);
+    }
+    lds_wave_sync();
+
+    // values: lane = channels 4*lane .. 4*lane+3 (block cj); per token pair
+    // one 16-bit dot product (two tokens' weights x their nibbles, 32-bit
+    // integer accumulate); this wave's VALU stream goes first while it holds
+    // its operands
     __builtin_amdgcn_s_setprio(2);
+    uint32_t oi[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oi[h][d] = 0u;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if ((ct & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two token groups' weights in flight
       pin(vq[ct]);
-      float4_t wa[G], wb[G];  // weights of tokens 8ct..8ct+3 and 8ct+4..8ct+7
+      uint4 uw[G];  // 16-bit weight pairs of tokens 8ct .. 8ct+7
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        wa[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][ct * 8]);
-        wb[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][ct * 8 + 4]);
-      }
+      for (int h = 0; h < G; ++h) uw[h] = *reinterpret_cast<const uint4*>(&urow(sm, wave, h, cj)[ct * 8]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t wd = word(vq[ct], k);
-        // fp16 pairs (token 8ct+2k, token 8ct+2k+1) of channels 0..3
-        const half2_t v0 = __builtin_bit_cast(half2_t, wd & 0x000F000Fu);
-        const half2_t v1 = __builtin_bit_cast(half2_t, wd & 0x00F000F0u);
+        // 16-bit pairs (token 8ct+2k, token 8ct+2k+1) of channels 0..3 (x16 for 1 and 3)
+        const uint32_t v0 = wd & 0x000F000Fu;
+        const uint32_t v1 = wd & 0x00F000F0u;
         const uint32_t w8 = wd >> 8;
-        const half2_t v2 = __builtin_bit_cast(half2_t, w8 & 0x000F000Fu);
-        const half2_t v3 = __builtin_bit_cast(half2_t, w8 & 0x00F000F0u);
+        const uint32_t v2 = w8 & 0x000F000Fu;
+        const uint32_t v3 = w8 & 0x00F000F0u;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float w0 = k < 2 ? wa[h][2 * k] : wb[h][2 * k - 4];
-          const float w1 = k < 2 ? wa[h][2 * k + 1] : wb[h][2 * k - 3];
-          // fp32 weight x fp16 nibble operand, fp32 accumulate (v_fma_mix_f32)
-          o[h][0] = fmaf(w1, static_cast<float>(v0.y), fmaf(w0, static_cast<float>(v0.x), o[h][0]));
-          o[h][1] = fmaf(w1, static_cast<float>(v1.y), fmaf(w0, static_cast<float>(v1.x), o[h][1]));
-          o[h][2] = fmaf(w1, static_cast<float>(v2.y), fmaf(w0, static_cast<float>(v2.x), o[h][2]));
-          o[h][3] = fmaf(w1, static_cast<float>(v3.y), fmaf(w0, static_cast<float>(v3.x), o[h][3]));
+          const uint32_t up = word(uw[h], k);
+          oi[h][0] = udot2(up, v0, oi[h][0]);
+          oi[h][1] = udot2(up, v1, oi[h][1]);
+          oi[h][2] = udot2(up, v2, oi[h][2]);
+          oi[h][3] = udot2(up, v3, oi[h][3]);
         }
       }
     }
-    // "- 8" correction, part 1: this lane's 8 tokens of the page's weights of
-    // block cj (the 8 lanes of the block cover its 64 tokens); the sum over the
-    // lanes and the correction itself wait for the epilogue
+    // the page's integer sums (< 64 x 65535 x 240 < 2^32) into the fp32 accumulators
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float4_t x = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8]);
-      const float4_t y = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8 + 4]);
-      wpart[h] += ((x.x + x.y) + (x.z + x.w)) + ((y.x + y.y) + (y.z + y.w));
-    }
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[h][d] = fmaf(static_cast<float>(oi[h][d]), funit[h], o[h][d]);
   }
 
   // "- 8" correction, part 2: the summed weights of block cj over every page of

@@ -38,7 +38,7 @@ class PagedSet:
     """Sequences of given lengths in one shared pool, written by both sides."""
 
     def __init__(self, lengths, Hkv=4, D=256, seed=0, extra_pages=3, k_scale=1.0, v_scale=1.0, outliers=False,
-                 placement=0, v_per_token=False):
+                 placement=0, v_per_token=False, k_edit=None):
         self.lengths = [int(x) for x in lengths]
         self.Hkv, self.D = Hkv, D
         g = synth.rng(100 + seed, 0)
@@ -54,6 +54,8 @@ class PagedSet:
             cols = synth.outlier_columns(g, Hkv, D)
             synth.apply_outliers(k, cols)
             synth.apply_outliers(v, cols)
+        if k_edit is not None:  # e.g. plant dominant keys (attention sinks)
+            k_edit(k)
         slots = []
         for b, n in enumerate(self.lengths):
             t = np.arange(n)

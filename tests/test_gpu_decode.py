@@ -99,6 +99,35 @@ def test_tiny_query_gives_uniform_weights():
     assert_states_close(m, l, rm, rl, "tiny query")
 
 
+@pytest.mark.parametrize("sinks,mag", [([1234], 12.0), ([5], 30.0), ([77, 3000], 20.0), ([64, 65, 4000], 9.0)])
+def test_dominant_tokens(sinks, mag):
+    """Keys planted along the query of the group's first head (attention
+    sinks), over N(0,1) keys and values with outlier channels and values x100:
+    a few tokens carry most of the weight, so the output is close to their
+    values and every rounding of those weights shows."""
+    print(f"decode with dominant tokens {sinks}, logit {mag}", flush=True)
+    lengths = [5000, 4100]
+    bits, qv = random_q(2, 16, 256, seed=15)
+
+    def plant(k):
+        start = 0
+        for b, n in enumerate(lengths):
+            for g in range(4):
+                d = qv[b, 4 * g] / np.linalg.norm(qv[b, 4 * g])
+                for t in sinks:
+                    # logit sm * q . k = mag for the group's first head
+                    k[start + t, g] = (d * mag * 16.0 / np.linalg.norm(qv[b, 4 * g])).astype(np.float32)
+            start += n
+
+    ps = PagedSet(lengths, Hkv=4, seed=15, outliers=True, v_scale=100.0, k_edit=plant)
+    out, m, l = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), ps.gpu_lengths(), 5000, SM)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle_decode(ps, qv, SM)
+    o, m, l = out.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
+    assert_attention_close(o, ro, f"sinks {sinks}")
+    assert_states_close(m, l, rm, rl, f"sinks {sinks}")
+
+
 def test_outliers_and_scaled_values():
     ps = PagedSet([2000], Hkv=4, seed=10, outliers=True, v_scale=100.0)
     (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=10)
