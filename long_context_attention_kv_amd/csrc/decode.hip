@@ -261,12 +261,22 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
-// Max over each group of 8 consecutive lanes, returned in all 8.
-__device__ __forceinline__ float max8(float x) {
-  x = fmaxf(x, dpp<kDppQuadXor1>(x));
-  x = fmaxf(x, dpp<kDppQuadXor2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  return x;
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Max of non-negative fp32 values over each group of 8 consecutive lanes,
+// returned in all 8.  Non-negative floats order as their bit patterns, so the
+// max runs on integers (no NaN quieting around each step).
+__device__ __forceinline__ float max8_nonneg(float4_t x, float4_t y) {
+  const uint32_t a = max(max(__float_as_uint(x.x), __float_as_uint(x.y)), max(__float_as_uint(x.z), __float_as_uint(x.w)));
+  const uint32_t b = max(max(__float_as_uint(y.x), __float_as_uint(y.y)), max(__float_as_uint(y.z), __float_as_uint(y.w)));
+  uint32_t m = max(a, b);
+  m = max(m, dpp_u<kDppQuadXor1>(m));
+  m = max(m, dpp_u<kDppQuadXor2>(m));
+  m = max(m, dpp_u<kDppHalfMirror>(m));
+  return __uint_as_float(m);
 }
 
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
@@ -651,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float4_t x = wx[h], y = wy[h];
-      const float mx = max8(fmaxf(fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)), fmaxf(fmaxf(y.x, y.y), fmaxf(y.z, y.w))));
+      const float mx = max8_nonneg(x, y);
       const int e = __builtin_amdgcn_frexp_expf(mx);  // 0 when the row is all zero
       uint4 u;
       u.x = pknorm_u16(__builtin_amdgcn_ldexpf(x.x, -e), __builtin_amdgcn_ldexpf(x.y, -e));
