@@ -205,6 +205,26 @@ int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * paged_attn_decode_f4_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The same computation, arguments and outputs as
+ * paged_attn_decode_f4, without the workspace: its partial states, work list
+ * and query operands live in a fixed 8 MiB device array of the library (one
+ * per GPU, held until the process ends; its address is looked up on the first
+ * call on each device).  The call allocates and frees nothing.  Calls whose
+ * workspace (paged_attn_decode_f4_workspace_size) exceeds 8 MiB are refused
+ * with F4KV_ERR_UNSUPPORTED before any launch.  Nothing in the array carries
+ * from one call to the next (every call writes what it reads), but all calls
+ * on one GPU share it: calls that can overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+int paged_attn_decode_f4_noalloc(const f4kv_cache* cache, const uint16_t* q,
+                                 const int32_t* page_table, const int32_t* context_lens,
+                                 int32_t B, int32_t Hq, int32_t max_pages, int32_t max_context_len,
+                                 int32_t num_windows, int32_t window_tokens, float sm_scale,
+                                 float* out, float* out_m, float* out_l, hipStream_t stream);
+
+/*
  * paged_attn_decode_rows_f4 [IGN --spec-draft-tokens / --spec-draft-rows: a
  * verify round takes up to 8 query rows of a lane; MRS item 2; FT item 2]
  * Decode of R query rows per sequence (1 <= R <= 8), as one round of

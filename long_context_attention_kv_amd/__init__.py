@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     load_library,
     lse_merge,
     paged_attn_decode_f4,
+    paged_attn_decode_f4_noalloc,
     paged_attn_decode_rows_f4,
     paged_attn_prefill_f4,
     paged_attn_prefill_f4_fp8,
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "kv_cache_write_f4",
     "paged_attn_decode_f4_workspace_size",
     "paged_attn_decode_f4",
+    "paged_attn_decode_f4_noalloc",
     "paged_attn_decode_rows_f4_workspace_size",
     "paged_attn_decode_rows_f4",
     "lse_merge",

@@ -48,6 +48,8 @@ _SIGS = {
     "paged_attn_decode_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_decode_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, C.c_float,
                                        _P, _P, _P, _P, C.c_size_t, _P]),
+    "paged_attn_decode_f4_noalloc": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, C.c_float,
+                                               _P, _P, _P, _P]),
     "paged_attn_decode_rows_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_decode_rows_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, C.c_float,
                                             _P, _P, _P, _P, C.c_size_t, _P]),
@@ -256,6 +258,37 @@ def paged_attn_decode_f4(cache: F4Cache, q, page_table, context_lens, max_contex
                                     page_table.shape[1], int(max_context_len), W, int(window_tokens),
                                     float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _ptr(workspace), ws_bytes,
                                     _stream()))
+    return out, out_m, out_l
+
+
+def paged_attn_decode_f4_noalloc(cache: F4Cache, q, page_table, context_lens, max_context_len: int,
+                                 sm_scale: float, num_windows: int = 1, window_tokens: int = 0, out=None, out_m=None,
+                                 out_l=None):
+    """paged_attn_decode_f4 on the library's fixed device-side scratch (the C call
+    allocates nothing; pass out, out_m, out_l to allocate nothing here either)."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(q, torch.bfloat16, (B, Hq, D), "q")
+    _need(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    _need(context_lens, torch.int32, (B,), "context_lens")
+    W = num_windows
+    dev = q.device
+    if out is None:
+        out = torch.empty((W, B, Hq, D), dtype=torch.float32, device=dev)
+    if out_m is None:
+        out_m = torch.empty((W, B, Hq), dtype=torch.float32, device=dev)
+    if out_l is None:
+        out_l = torch.empty((W, B, Hq), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, (W, B, Hq, D), "out")
+    _need(out_m, torch.float32, (W, B, Hq), "out_m")
+    _need(out_l, torch.float32, (W, B, Hq), "out_l")
+    c = cache._c()
+    _check("paged_attn_decode_f4_noalloc",
+           lib.paged_attn_decode_f4_noalloc(C.byref(c), _ptr(q), _ptr(page_table), _ptr(context_lens), B, Hq,
+                                            page_table.shape[1], int(max_context_len), W, int(window_tokens),
+                                            float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _stream()))
     return out, out_m, out_l
 
 

@@ -165,10 +165,13 @@ size_t paged_attn_decode_rows_f4_workspace_size(int32_t B, int32_t R, int32_t Hq
 
 namespace {
 
+// fixed_scratch: the workspace is the library's own device-side scratch array
+// (workspace / ws_bytes are ignored); the call allocates nothing.
 int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,
                   const int32_t* context_lens, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
                   int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale, float* out,
-                  float* out_m, float* out_l, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                  float* out_m, float* out_l, void* workspace, size_t ws_bytes, hipStream_t stream,
+                  bool fixed_scratch = false) {
   if (int r = check_cache(cache, fn)) return r;
   const int32_t Hkv = cache->num_kv_heads;
   if (B < 0 || Hq <= 0 || max_pages <= 0 || max_context_len < 0)
@@ -209,6 +212,17 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
                     fn);
   }
   const f4kv::DecodePlan plan = f4kv::plan_decode(B, R, Hq, Hkv, max_context_len, num_windows, window_tokens);
+  if (fixed_scratch) {
+    if (plan.ws_bytes > f4kv::decode_scratch_bytes())
+      return fail(F4KV_ERR_UNSUPPORTED,
+                  "%s: this call needs %zu bytes of workspace, more than the fixed scratch of %zu bytes "
+                  "(use paged_attn_decode_f4 with a workspace)",
+                  fn, plan.ws_bytes, f4kv::decode_scratch_bytes());
+    hipError_t e = f4kv::decode_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(F4KV_ERR_LAUNCH, "%s: device address of the scratch array: %s", fn, hipGetErrorString(e));
+    ws_bytes = f4kv::decode_scratch_bytes();
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || ws_bytes < plan.ws_bytes)
       return fail(F4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, plan.ws_bytes,
@@ -233,6 +247,15 @@ int paged_attn_decode_f4(const f4kv_cache* cache, const uint16_t* q, const int32
   return decode_common("paged_attn_decode_f4", cache, q, page_table, context_lens, B, 1, Hq, max_pages,
                        max_context_len, num_windows, window_tokens, sm_scale, out, out_m, out_l, workspace, ws_bytes,
                        stream);
+}
+
+int paged_attn_decode_f4_noalloc(const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,
+                                 const int32_t* context_lens, int32_t B, int32_t Hq, int32_t max_pages,
+                                 int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale,
+                                 float* out, float* out_m, float* out_l, hipStream_t stream) {
+  return decode_common("paged_attn_decode_f4_noalloc", cache, q, page_table, context_lens, B, 1, Hq, max_pages,
+                       max_context_len, num_windows, window_tokens, sm_scale, out, out_m, out_l, nullptr, 0, stream,
+                       true);
 }
 
 int paged_attn_decode_rows_f4(const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,

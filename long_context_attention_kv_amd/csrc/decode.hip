@@ -38,6 +38,7 @@
 // full precision whatever its magnitude; fp32 accumulation throughout.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "f4kv_internal.h"
 
@@ -905,7 +906,34 @@ int group_size(int32_t R, int32_t Gq) {
   return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : 8;
 }
 
+// The workspace of paged_attn_decode_f4_noalloc: one array per GPU, held by
+// the process until it ends.  Host code never uses the array's name as an
+// address: decode_scratch() looks the device address up once per device.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 }  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 DecodePlan plan_decode(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
                        int32_t window_tokens) {

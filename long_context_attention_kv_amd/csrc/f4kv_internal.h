@@ -78,6 +78,11 @@ struct DecodePlan {
 DecodePlan plan_decode(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx,
                        int32_t num_windows, int32_t window_tokens);
 
+// Fixed device-side workspace for the allocation-free decode entry point: its
+// size, and its device address on the current device (looked up on first use).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
                          const int32_t* ctx, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
                          int32_t max_ctx, int32_t num_windows, int32_t window_tokens,

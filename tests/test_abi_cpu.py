@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +140,24 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=16, ws_bytes=need - 1) == 3
     assert "workspace" in _err(lib)
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=None, ws_bytes=need) == 3
+
+
+def test_decode_noalloc_refuses_beyond_its_scratch(lib):
+    """The allocation-free decode takes no workspace: the same argument checks,
+    and a call whose workspace would exceed the fixed 8 MiB scratch is refused
+    on the host (no launch, no allocation)."""
+    c = _cache()
+
+    def call(B_=1, Hq=16, max_pages=64, max_ctx=4096, W=1, wt=0, q=16):
+        return lib.paged_attn_decode_f4_noalloc(C.byref(c), q, 16, 16, B_, Hq, max_pages, max_ctx, W, wt, 0.0625, 16,
+                                                None, None, None)
+
+    assert call(Hq=6) == 1 and "multiple" in _err(lib)
+    assert call(W=2, wt=100) == 1 and "64" in _err(lib)
+    assert call(B_=0) == 0
+    need = lib.paged_attn_decode_f4_workspace_size(1, 16, 4, 256, 1 << 20, 16384, 64)
+    assert need > 8 << 20
+    assert call(max_pages=16384, max_ctx=1 << 20, W=16384, wt=64) == 2 and "scratch" in _err(lib)
 
 
 def test_decode_rows_argument_checks(lib):
