@@ -89,6 +89,46 @@ def gb(x):
     return x / 1e9
 
 
+def stats(ms):
+    """mean, median and min of per-iteration times (ms)."""
+    return {"ms": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))}
+
+
+def timed(fn, iters, between=None):
+    """Per-iteration times (ms) of fn() by HIP events on the current stream;
+    between() runs outside the timed span before each iteration (e.g. a write
+    of 1 GiB that evicts the 256 MB last-level cache)."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for e0, e1 in evs:
+        if between is not None:
+            between()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+_EVICT = None
+
+
+def evict_llc():
+    """Reads 1 GiB of scratch (four times the 256 MB Infinity Cache), so the
+    next call finds none of its own data in the caches.  The scratch is read,
+    not written: dirty lines left by a write would be written back to HBM while
+    the next, timed call runs and inflate its traffic.  (The first call fills
+    the scratch and flushes it with two reads.)"""
+    global _EVICT
+    if _EVICT is None:
+        _EVICT = torch.empty(1 << 27, dtype=torch.int64, device="cuda")
+        _EVICT.fill_(1)
+        for _ in range(2):
+            _EVICT.sum()
+        torch.cuda.synchronize()
+    _EVICT.sum()
+
+
 def decode_algorithmic_bytes(lengths, windows=1, per_token_head=None):
     kv = sum(lengths) * HKV * (BYTES_PER_TOKEN_HEAD if per_token_head is None else per_token_head)
     q = len(lengths) * HQ * D * 2
@@ -221,6 +261,7 @@ def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
         "kv_tokens_per_step": tokens,
         "value": tokens / (ms_step / 1e3),
         "decode_call_ms_avg": dec_avg_ms,
+        "decode_call_ms_median": float(np.median(dec_ms)),
         "decode_call_ms_min": float(np.min(dec_ms)),
         "decode_kernel_ms_avg": timer.avg_ms,
         "decode_bytes_per_call": dec_bytes,
@@ -229,6 +270,31 @@ def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
         "layers": layers,
         "out_sample": outs[0][0][0, 0, 0, :4].float().cpu().tolist(),
     }
+
+
+def bench_config0(iters=50):
+    """1 sequence x 4,096 tokens, one layer, plain RoPE (theta 1e7): launch-bound,
+    its 4.7 MB stay in the last-level cache; reported, not the target."""
+    dev = "cuda"
+    gen = torch.Generator().manual_seed(synth.BASE_SEED + 0)
+    n = 4096
+    L = DecodeLayer([n], 1.0, gen, outliers=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED + 10)
+    q = torch.randn((1, HQ, D), generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(max(16, f4.decode_workspace_size(1, HQ, HKV, D, n)), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, 1, HQ, D), device=dev)
+    for _ in range(5):
+        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, n, SM, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=iters) as timer:
+        st = stats(timed(lambda: f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, n, SM, out=out, workspace=ws),
+                         iters))
+    by = decode_algorithmic_bytes([n])
+    del L
+    return {"workload": "decode, 1 x 4,096 tokens, one layer, plain RoPE (reported, not the target)", **st,
+            "kv_tokens_per_s": n / (st["ms"] / 1e3), "gbs": by / (st["ms"] / 1e3) / 1e9,
+            "kernel_ms": timer.avg_ms, "bytes": by}
 
 
 def bench_1m(iters=10):
@@ -252,20 +318,18 @@ def bench_1m(iters=10):
     for _ in range(3):
         once()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=iters) as timer:
-        e0.record()
-        for _ in range(iters):
-            once()
-        e1.record()
-        torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+        st = stats(timed(once, iters))
+    ms = st["ms"]
     by = decode_algorithmic_bytes([ctx], windows=W)
     del L
-    return {"workload": "1 x 1,048,576 tokens, 16 windows of 65,536 + lse_merge", "ms": ms,
+    return {"workload": "1 x 1,048,576 tokens, 16 windows of 65,536 + lse_merge", **st,
             "kv_tokens_per_s": ctx / (ms / 1e3), "gbs": by / (ms / 1e3) / 1e9,
             "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_ms": timer.avg_ms, "kernel_hbm_frac": by / (timer.avg_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+            "kv_tokens_per_s_median": ctx / (st["ms_median"] / 1e3),
+            "hbm_frac_median": by / (st["ms_median"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms": timer.avg_ms, "kernel_hbm_frac": by / (timer.avg_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "bytes": by}
 
 
 def bench_vtok(iters=20):
@@ -372,17 +436,19 @@ def bench_ragged(iters=20):
     for _ in range(3):
         f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, mx, SM, workspace=ws)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, mx, SM, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    # the cache (~0.75 GB) would partly stay in the 256 MB Infinity Cache between
+    # calls: 1 GiB of scratch is read before every timed call
+    with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=iters) as timer:
+        st = stats(timed(lambda: f4.paged_attn_decode_f4(L.cache, q, L.pt, L.ctx, mx, SM, workspace=ws), iters,
+                         between=evict_llc))
+    ms = st["ms"]
     by = decode_algorithmic_bytes(lengths)
-    return {"workload": "8 ragged sequences, log-uniform 1,024..320,000", "lengths": lengths, "ms": ms,
+    return {"workload": "8 ragged sequences, log-uniform 1,024..320,000", "lengths": lengths, **st,
             "kv_tokens_per_s": sum(lengths) / (ms / 1e3), "gbs": by / (ms / 1e3) / 1e9,
-            "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "hbm_frac_median": by / (st["ms_median"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_ms": timer.avg_ms, "kernel_hbm_frac": by / (timer.avg_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "between_calls": "1 GiB scratch read (last-level cache evicted, no dirty lines left)"}
 
 
 def prefill_flops(T, pos0):
@@ -420,25 +486,95 @@ def bench_prefill(iters=5, T=2048, window=131072, fp8=False):
     for _ in range(2):
         call(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with f4.KernelTimer(f4.KERNEL_PREFILL_FP8 if fp8 else f4.KERNEL_PREFILL, max_launches=iters) as timer:
-        e0.record()
-        for _ in range(iters):
-            call(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+        st = stats(timed(lambda: call(cache, q, kn, vn, pt, pos0, SM, out=out, workspace=ws), iters))
+    ms = st["ms"]
     fl = prefill_flops(T, pos0)
     tf = fl / (ms / 1e3) / 1e12
     tk = fl / (timer.avg_ms / 1e3) / 1e12
     peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_F16_PEAK_TFLOPS
     r = {"workload": "2,048 queries at 129,024..131,071 over a 131,072-token causal window (write included)",
-         "ms": ms, "tflops": tf, "mfma_frac": tf / peak, "flops": fl,
+         **st, "tflops": tf, "mfma_frac": tf / peak, "flops": fl,
+         "tflops_median": fl / (st["ms_median"] / 1e3) / 1e12,
          "kernel_ms": timer.avg_ms, "kernel_tflops": tk, "kernel_mfma_frac": tk / peak}
     if fp8:
         r["precision"] = "Q.K^T INT8, P.V E4M3 (fractions of the 5.0 PFLOP/s dense FP8 peak)"
         r["kernel_frac_of_fp16_peak"] = tk / MFMA_F16_PEAK_TFLOPS
     return r
+
+
+def measure_ceilings():
+    """On-box ceilings from bench_ceilings.so (built beside this file by
+    __graft_entry__.build()): the best plain HBM read of a 4 GiB buffer over a
+    few grid sizes, and matrix-core loops of the prefill kernels' instructions.
+    None when the ceiling library is not built."""
+    import ctypes as C
+    path = os.path.join(ROOT, "bench_ceilings.so")
+    if not os.path.exists(path):
+        return None
+    lib = C.CDLL(path)
+    lib.ceiling_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+    lib.ceiling_mfma.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.POINTER(C.c_double), C.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    best = {}
+    for unroll in (4, 8, 16):
+        for grid in (2048, 8192, 16384, 32768):
+            def read():
+                assert lib.ceiling_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, stream) == 0
+            read()
+            ms = float(np.median(timed(read, 5)))
+            best[f"grid {grid}, {unroll} loads"] = nbytes / (ms / 1e3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    top = max(best, key=best.get)
+    out = {"hbm_read_gbs": best[top], "hbm_read_config": top, "hbm_read_gbs_by_config": best,
+           "hbm_read": "4 GiB read once per launch, 16-byte loads per thread, grid-stride; best of the "
+                       "configurations, each the median of 5 launches"}
+    for kind, name in ((0, "mfma_f16_tflops"), (1, "mfma_fp8_tflops"), (2, "mfma_i8_tops")):
+        fl = C.c_double(0.0)
+
+        def loop():
+            assert lib.ceiling_mfma(kind, 2048, 1024, sink.data_ptr(), C.byref(fl), stream) == 0
+        loop()
+        ms = float(np.median(timed(loop, 5)))
+        out[name] = fl.value / (ms / 1e3) / 1e12
+    out["mfma"] = "1,024 workgroups of 4 waves, 4 independent accumulator chains, 8,192 matrix instructions per wave"
+    return out
+
+
+def cpu_prefill_sample(rows=4):
+    """The fp64 oracle's prefill on a bounded sample of the chunk workload: the
+    last `rows` query positions of the 2,048-query chunk (all 16 heads) over the
+    full 131,072-token window, host-generated from the same recipe."""
+    from oracle import attention as oatt
+    from oracle import f4 as of4
+    from oracle import yarn as oyarn
+    g = synth.rng(3, 7)
+    n = 131072
+    k = synth.normal_f32(g, (n, HKV, D))
+    v = synth.normal_f32(g, (n, HKV, D))
+    spec = synth.YarnSpec(factor=4.0)
+    pos = np.arange(n)
+    cs, sn = oyarn.yarn_table(spec, pos)
+    k = oyarn.rope_apply(k, cs, sn, 256).astype(np.float32)
+    pages = n // PAGE
+    cache = of4.Cache(pages, HKV, D)
+    perm = synth.page_permutation(g, pages)
+    cache.write(k, v, (perm[pos // PAGE].astype(np.int64) * PAGE + pos % PAGE))
+    T = 2048
+    q = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(synth.normal_f32(g, (T, HQ, D)))).astype(np.float64)
+    sel = list(range(T - rows, T))
+    t0 = time.perf_counter()
+    oatt.prefill(cache, q, perm, n - T, SM, rows=sel)
+    dt = time.perf_counter() - t0
+    fl = 4 * D * HQ * sum(n - T + i + 1 for i in sel)
+    return {"value": fl / dt / 1e9, "unit": "GFLOP/s",
+            "sample": f"query rows {sel[0]}..{sel[-1]} of the 2,048-query chunk (16 heads) over the 131,072-token "
+                      f"window (YaRN x4, N(0,1)), host-generated; {dt:.1f} s"}
 
 
 def cpu_baseline(sample_tokens=458752):
@@ -543,6 +679,8 @@ def main():
     torch.cuda.empty_cache()
     extra = {}
     if not args.no_extra:
+        extra["decode_config0"] = bench_config0()
+        log("config0:", extra["decode_config0"])
         extra["decode_1m_windows"] = bench_1m()
         log("1M:", extra["decode_1m_windows"])
         torch.cuda.empty_cache()
@@ -563,10 +701,31 @@ def main():
             torch.cuda.empty_cache()
             extra[f"decode_rows_{R}"] = bench_rows(R)
             log(f"rows {R}:", extra[f"decode_rows_{R}"])
+    ceil = None
+    if not args.no_extra:
+        torch.cuda.empty_cache()
+        ceil = measure_ceilings()
+        log("ceilings:", ceil)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(args.cpu_tokens)
+        cpu["prefill"] = cpu_prefill_sample()
         log("cpu:", cpu)
+    if ceil:
+        # every rate against the measured ceiling as well as the nominal peak
+        ceil["decode_kernel_frac_of_measured_read"] = r["decode_gbs"] / ceil["hbm_read_gbs"]
+        if "decode_1m_windows" in extra:
+            m1 = extra["decode_1m_windows"]
+            m1["kernel_frac_of_measured_read"] = m1["bytes"] / (m1["kernel_ms"] / 1e3) / 1e9 / ceil["hbm_read_gbs"]
+            m1["frac_of_measured_read"] = m1["gbs"] / ceil["hbm_read_gbs"]
+        if "decode_ragged" in extra:
+            extra["decode_ragged"]["frac_of_measured_read"] = extra["decode_ragged"]["gbs"] / ceil["hbm_read_gbs"]
+        if "prefill" in extra:
+            p = extra["prefill"]
+            p["kernel_frac_of_measured_mfma"] = p["kernel_tflops"] / ceil["mfma_f16_tflops"]
+        if "prefill_fp8" in extra:
+            p = extra["prefill_fp8"]
+            p["kernel_frac_of_measured_mfma"] = p["kernel_tflops"] / ceil["mfma_fp8_tflops"]
     line = {
         "metric": METRIC,
         "value": r["value"],
@@ -589,8 +748,11 @@ def main():
                      "frac": r["decode_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "decode_kernel<4, false> (split-K attention kernel of paged_attn_decode_f4)",
                      "bytes_per_launch": r["decode_bytes_per_call"], "launch_ms_avg": r["decode_kernel_ms_avg"],
-                     "whole_call_ms_avg": r["decode_call_ms_avg"], "whole_call_gbs": r["decode_call_gbs"]},
+                     "whole_call_ms_avg": r["decode_call_ms_avg"], "whole_call_gbs": r["decode_call_gbs"],
+                     "whole_call_ms_median": r["decode_call_ms_median"], "whole_call_ms_min": r["decode_call_ms_min"],
+                     "frac_of_measured_read": (r["decode_gbs"] / ceil["hbm_read_gbs"]) if ceil else None},
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

@@ -1,0 +1,130 @@
+// Measured ceilings of the GPU the benchmark runs on: a plain HBM read kernel
+// and matrix-core loops (fp16, E4M3 and INT8 products, the instructions the
+// prefill kernels issue).  bench.py reports the library's rates against these
+// beside the nominal peaks.  Not part of the library.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Every thread streams 16-byte words with a grid-stride loop, U loads in
+// flight per iteration; the XOR of all words is kept so that no load can be
+// dropped (it is written out only if it hits a value the data never makes).
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+// Four independent accumulator chains per wave, `iters` rounds.  The operands
+// come from the thread index so nothing folds; the accumulators are written
+// only under a condition the caller never meets (iters < 0 is refused).
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ sink) {
+  const int t = threadIdx.x;
+  if (KIND == 0) {
+    half8_t a, b;
+    for (int j = 0; j < 8; ++j) {
+      a[j] = static_cast<_Float16>((t + j) & 7);
+      b[j] = static_cast<_Float16>((t * 3 + j) & 7);
+    }
+    f32x16 c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, b, c3, 0, 0, 0);
+    }
+    if (c0[0] + c1[1] + c2[2] + c3[3] == -1.0f) sink[t] = c0[5];
+  } else if (KIND == 1) {
+    i32x8 a, b;
+    for (int j = 0; j < 8; ++j) {
+      a[j] = 0x38383838 + ((t + j) & 3);  // E4M3 values near 1
+      b[j] = 0x30303030 + ((t * 3 + j) & 3);
+    }
+    f32x16 c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
+      c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c1, 0, 0, 0, 127, 0, 127);
+      c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, c2, 0, 0, 0, 127, 0, 127);
+      c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, b, c3, 0, 0, 0, 127, 0, 127);
+    }
+    if (c0[0] + c1[1] + c2[2] + c3[3] == -1.0f) sink[t] = c0[5];
+  } else {
+    i32x4 a, b;
+    for (int j = 0; j < 4; ++j) {
+      a[j] = 0x01010101 * ((t + j) & 7);
+      b[j] = 0x01010101 * ((t * 3 + j) & 7);
+    }
+    i32x16 c0{}, c1{}, c2{}, c3{};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, b, c3, 0, 0, 0);
+    }
+    if (c0[0] + c1[1] + c2[2] + c3[3] == -1) sink[t] = static_cast<float>(c0[5]);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) at buf with `grid` workgroups of 256
+// threads on `stream`, `unroll` (4, 8 or 16) loads in flight per thread.
+// sink: one device word.  0 = launched.
+int ceiling_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll, hipStream_t stream) {
+  if (!buf || !sink || bytes % 16 != 0 || grid <= 0) return 1;
+  const u32x4* p = static_cast<const u32x4*>(buf);
+  if (unroll == 4)
+    hipLaunchKernelGGL(stream_read_kernel<4>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
+  else if (unroll == 8)
+    hipLaunchKernelGGL(stream_read_kernel<8>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
+  else if (unroll == 16)
+    hipLaunchKernelGGL(stream_read_kernel<16>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
+  else
+    return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// `grid` workgroups of 4 waves, each wave issuing 4 * iters matrix
+// instructions: kind 0 = v_mfma_f32_32x32x16_f16 (32,768 flop each),
+// 1 = v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 (131,072), 2 =
+// v_mfma_i32_32x32x32_i8 (65,536).  sink: 256 floats of device memory.
+// Returns the flops of the launch in *flops; 0 = launched.
+int ceiling_mfma(int kind, int iters, int grid, float* sink, double* flops, hipStream_t stream) {
+  if (!sink || !flops || iters < 0 || grid <= 0 || kind < 0 || kind > 2) return 1;
+  const double per = kind == 0 ? 32768.0 : (kind == 1 ? 131072.0 : 65536.0);
+  *flops = per * 4.0 * iters * 4.0 * grid;
+  if (kind == 0)
+    hipLaunchKernelGGL(mfma_loop_kernel<0>, dim3(grid), dim3(256), 0, stream, iters, sink);
+  else if (kind == 1)
+    hipLaunchKernelGGL(mfma_loop_kernel<1>, dim3(grid), dim3(256), 0, stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_loop_kernel<2>, dim3(grid), dim3(256), 0, stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"

@@ -17,6 +17,11 @@
         SHA-256 of the kernel's source file so that a reader can tell whether
         the figure still belongs to the current kernel.
 
+    python prof_summary.py counters --csv CSV [--csv CSV ...] --cmd "..." [--cmd ...] \\
+            --kernel NAME [--kernel NAME ...]
+        per-dispatch averages of every counter of ``--pmc`` runs for the named
+        kernels, one column per (kernel, launch grid).
+
 Output is Markdown on stdout.
 """
 from __future__ import annotations
@@ -158,6 +163,42 @@ def traffic(a) -> str:
     return "\n".join(out)
 
 
+def counters(paths, cmds, kernels) -> str:
+    """Per-dispatch averages of every counter in the given ``--pmc`` CSVs for
+    each named kernel, one column per (kernel, launch grid)."""
+    cols = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            short = _short(r["Kernel_Name"])
+            if short not in kernels:
+                continue
+            grid = tuple(int(r.get(f"Grid_Size_{a}", r.get("Grid_Size", 0)) or 0) //
+                         max(1, int(r.get(f"Workgroup_Size_{a}", r.get("Workgroup_Size", 1)) or 1)) for a in "XYZ") \
+                if "Grid_Size_X" in r else (int(r.get("Grid_Size", 0)),)
+            key = (short, grid)
+            cols.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not cols:
+        raise SystemExit("none of the kernels found in the counter files")
+    names = sorted({c for v in cols.values() for c in v})
+    keys = sorted(cols)
+    head = ["# Counters per dispatch", "", "Commands (one counter group per pass):", "", "```", *cmds, "```", "",
+            "| counter | " + " | ".join(f"`{k[0]}` grid {' x '.join(map(str, k[1]))}" for k in keys) + " |",
+            "|---|" + "---:|" * len(keys)]
+    rows = []
+    disp = []
+    for k in keys:
+        n = max(len(v) for v in cols[k].values())
+        disp.append(str(n))
+    rows.append("| dispatches | " + " | ".join(disp) + " |")
+    for c in names:
+        vals = []
+        for k in keys:
+            d = cols[k].get(c)
+            vals.append(f"{statistics.mean(d):,.0f}" if d else "")
+        rows.append(f"| {c} | " + " | ".join(vals) + " |")
+    return "\n".join(head + rows) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -174,9 +215,15 @@ def main(argv=None):
     t.add_argument("--source", required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", action="append", required=True)
+    c.add_argument("--cmd", action="append", required=True)
+    c.add_argument("--kernel", action="append", required=True, help="short kernel name, e.g. 'decode_kernel<4, false>'")
     a = ap.parse_args(argv)
     if a.what == "stats":
         sys.stdout.write(stats_table(a.csv, a.cmd, a.timed, [n for n in a.shapes.split(";") if n]))
+    elif a.what == "counters":
+        sys.stdout.write(counters(a.csv, a.cmd, a.kernel))
     else:
         sys.stdout.write(traffic(a))
 
