@@ -308,7 +308,8 @@ int paged_attn_prefill_f4(const f4kv_cache* cache, const uint16_t* q,
  *     max |q| < 2^e, round half to even, clamped to [-127, 127];
  *   - each cached key to INT8 with one power-of-two scale per token,
  *     tau = 2^(E - 4), E = (exponent field of the token's largest fp16 block
- *     scale) - 14, code * scale / tau rounded half up (within [-128, 112]);
+ *     scale) - 14, code * scale / tau rounded to nearest, ties to even
+ *     (within [-128, 112]);
  *   - x = (Qi . Kt) sigma tau qk in log2 units, qk = fp32(sm_scale log2(e));
  *   - per 32-token group (half a page) of a row, G = ceil(max x) and the
  *     weights P8 = e4m3(2^(x - G)) (OCP E4M3, nearest even) carrying 2^G;

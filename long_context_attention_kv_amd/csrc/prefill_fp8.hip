@@ -9,7 +9,8 @@
 //    max |q| < 2^e, round half to even, clamped to +-127;
 //  * each cached key to INT8 with one power-of-two scale per token, tau =
 //    2^(E - 4), E = (fp16 exponent field of the token's largest block scale) -
-//    14, the value c s / tau rounded half up (always within [-128, 112]);
+//    14, the value c s / tau rounded to nearest, ties to even (always within
+//    [-128, 112]);
 //  * scores in log2 units x = S sigma tau qk, S the exact INT8 dot product and
 //    qk = sm_scale log2(e) in fp32;
 //  * weights to E4M3 per 32-token group of a row: G = ceil(max x of the group),
@@ -25,8 +26,8 @@
 // one 16-byte unit of keys and one of values per page; two waves per SIMD
 // hide each other's latencies.  Per page of 64 keys:
 //  1. the workgroup requantises the page's keys into LDS as INT8 [token]
-//     [channel] (packed 16-bit integer arithmetic: c M + round, shifted) and
-//     its values as E4M3 V^T [channel][token];
+//     [channel] (one packed fp16 FMA per pair of values) and its values as
+//     E4M3 V^T [channel][token];
 //  2. each wave forms S^T = K Q^T with the INT8 matrix core
 //     (v_mfma_i32_32x32x32_i8: exact integer sums), 8 per 32-token tile;
 //  3. the softmax runs lane-local in log2 units with a lazily raised running
@@ -142,14 +143,22 @@ __device__ __forceinline__ void stage_vscales(Fp8Smem& sm, const KRaw& r, int ti
 
 // Keys of this thread's unit to INT8.  With the block scale s = M 2^(max(e5, 1) - 25) (M
 // its significand, e5 its exponent field) and tau = 2^(e5max - 18), c s / tau
-// = c M / 2^k for k = e5max + 7 - max(e5, 1) >= 6; rounded half up that is
-// (n M - 8 M + 2^(k-1)) >> k on 16-bit lanes (|c M| <= 16376; k is clamped at
-// 15, where the result is 0 either way).  Nibble pairs (j, j + 4) of a dword
-// come out of one AND; the bytes are stored as channels 0, 1, 4, 5, 2, 3, 6, 7
-// of each group of 8, and the query operands use the same order.
+// = c M 2^-k for k = e5max + 7 - max(e5, 1) >= 6, and |c M 2^-k| <= 256.
+// Rounded to nearest, ties to even, in one packed fp16 FMA per pair of values:
+// fma(c, M 2^-k, 1536) is exact before its single rounding, and fp16 values in
+// [1024, 2048) are the integers, so the result is 1536 + rne(c M 2^-k) (1536
+// is even, so a tie lands on the even integer); its low byte is that integer
+// as an INT8 (1536 = 6 x 256).  c = n - 8 comes exactly out of 1024 + n (the
+// nibble ORed into the mantissa of 1024) minus 1032.  M 2^-k is exact in fp16
+// for k <= 14; for k >= 15 every |c M 2^-k| < 1/2, so the code is 0 whatever
+// the rounding of M 2^-k.  Nibble pairs (j, j + 4) of a dword come out of one
+// AND-OR; the bytes are stored as channels 0, 1, 4, 5, 2, 3, 6, 7 of each group
+// of 8, and the query operands use the same order.
 // tau goes to LDS with the sign of the logit scale, so that the scores up to
 // the positive factor |sigma qk| order like the scores themselves.
-__device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, float tau_sign) {
+typedef _Float16 half2v_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, float tau_sign, uint32_t magic) {
   const int c = tid >> 6, t = tid & 63;
   const uint32_t b01 = word(r.ks, 0), b23 = word(r.ks, 1), b45 = word(r.ks, 2), b67 = word(r.ks, 3);
   // largest of the eight scales (non-negative fp16 bits compare as integers)
@@ -159,11 +168,11 @@ __device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, fl
   const uint32_t sb = (word(r.ks, c >> 1) >> (16 * (c & 1))) & 0xFFFFu;
   const int e5 = static_cast<int>(sb >> 10);
   const int M = static_cast<int>(sb & 1023u) | (e5 ? 1024 : 0);
-  const int k = min(e5max + 7 - max(e5, 1), 15);
-  const short A = static_cast<short>(-8 * M + (1 << (k - 1)));
-  const s16x2 Mv = {static_cast<short>(M), static_cast<short>(M)};
-  const s16x2 Av = {A, A};
-  const s16x2 kv = {static_cast<short>(k), static_cast<short>(k)};
+  const int k = e5max + 7 - max(e5, 1);
+  const _Float16 S = static_cast<_Float16>(__builtin_amdgcn_ldexpf(static_cast<float>(M), -k));
+  const half2v_t Sv = {S, S};
+  const half2v_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+  const half2v_t bias = {static_cast<_Float16>(1536.0f), static_cast<_Float16>(1536.0f)};
   uint32_t out[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -171,8 +180,8 @@ __device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, fl
     uint32_t p[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const s16x2 n = __builtin_bit_cast(s16x2, (w >> (4 * s)) & 0x000F000Fu);
-      p[s] = __builtin_bit_cast(uint32_t, static_cast<s16x2>((n * Mv + Av) >> kv));
+      const half2v_t cn = __builtin_bit_cast(half2v_t, ((w >> (4 * s)) & 0x000F000Fu) | magic) + off;  // n - 8
+      p[s] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(cn, Sv, bias));
     }
     // bytes 0 and 2 of each 16-bit pair: channels (0, 1, 4, 5) and (2, 3, 6, 7)
     out[2 * d] = __builtin_amdgcn_perm(p[1], p[0], 0x06020400u);
@@ -302,6 +311,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
   }
 
   const float tau_sign = a.qk_scale > 0.0f ? 1.0f : (a.qk_scale < 0.0f ? -1.0f : 0.0f);
+  uint32_t nmagic = 0x64006400u;  // fp16 1024 in both halves, kept in a VGPR (one literal per instruction)
+  asm volatile("" : "+v"(nmagic));
   f32x16 acc[8];  // O^T: 8 tiles of 32 value rows (rows 32 ct .. of the LDS order)
 #pragma unroll
   for (int d = 0; d < 8; ++d) acc[d] = f32x16{};
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     const int64_t ph0 = page_handle(pbeg, cur_valid);
     load_k<VT>(a, ph0, tid, kraw);
     load_v(a, ph0, tid, vcur);
-    unpack_k(sm, kraw, tid, tau_sign);
+    unpack_k(sm, kraw, tid, tau_sign, nmagic);
     stage_vscales<VT>(sm, kraw, tid, pbeg & 1);
   }
 
@@ -439,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
 
     // ---- keys of the next page to INT8 and its V scales, while the matrix cores work on P.V ----
     if (lp + 1 < pend) {
-      unpack_k(sm, kraw, tid, tau_sign);
+      unpack_k(sm, kraw, tid, tau_sign, nmagic);
       stage_vscales<VT>(sm, kraw, tid, par ^ 1);
     }
 

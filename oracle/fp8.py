@@ -18,9 +18,10 @@ Readings (for one query row r at position p, head h, KV head g = h // (Hq/Hkv)):
 2. Cached keys to INT8, one power-of-two scale per token: with s_b the token's
    eight fp16 block scales, E_t = max(floor(log2 max_b s_b) + 1, -14) (the
    fp16 exponent field of the largest scale minus 14; -14 when every scale is
-   zero or subnormal), tau_t = 2^(E_t - 4) and Kt = floor(c * s_b / tau_t + 1/2)
-   for the code c = nibble - 8 (round half up).  |c * s_b / tau_t| < 128, so Kt
-   lies in [-128, 112] without clamping.
+   zero or subnormal), tau_t = 2^(E_t - 4) and Kt = rne(c * s_b / tau_t) for
+   the code c = nibble - 8 (to nearest, ties to even: the rule of the F4
+   quantiser and of step 1).  |c * s_b / tau_t| < 128, so Kt lies in
+   [-128, 112] without clamping.
 3. Scores in log2 units: x = S * sigma_r * tau_t * qk, S = sum_d Qi_d Kt_d (an
    exact integer), qk = fp32(fp32(sm_scale) * fp32(log2 e)), the logit scale
    as the library forms it.
@@ -117,7 +118,7 @@ def requantize_keys(codes: np.ndarray, scales: np.ndarray):
     E = scale_exponent(s.max(axis=-1))
     tau = np.ldexp(1.0, E - 4)
     sd = np.repeat(s, BLOCK, axis=-1)
-    Kt = np.floor(codes.astype(np.float64) * sd / tau[:, None] + 0.5).astype(np.int32)
+    Kt = np.rint(codes.astype(np.float64) * sd / tau[:, None]).astype(np.int32)  # c s / tau is exact
     return Kt, tau
 
 

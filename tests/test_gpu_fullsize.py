@@ -321,6 +321,24 @@ def test_config3_prefill_fp8_2048_at_129024():
         for i in PREFILL_ROWS:
             check_group(out[i, h * G:(h + 1) * G], m[i, h * G:(h + 1) * G], l[i, h * G:(h + 1) * G],
                         (ro[i], rm[i], rl[i]), f"8-bit prefill row {i} kv head {h}")
+        # against the exact attention, at the error the E4M3 and INT8 formats predict
+        from fp8_bound import normalised_errors, predicted_sd
+        Kx, Vx = oatt.gather_values(oc, pt, n, 0)
+        codes = [oc.page_codes(int(pt[lp]), 0) for lp in range(len(pt))]
+        ks = np.concatenate([c[1] for c in codes]).astype(np.float64)
+        vs = np.concatenate([c[3] for c in codes]).astype(np.float64)
+        zs = []
+        for i in (0, 1000, 2047):
+            na = pos0 + i + 1
+            qg = qv[i, h * G:(h + 1) * G]
+            ex, _, _ = oatt.decode_head_from_values(qg, Kx[:na], Vx[:na], SM)
+            sd = predicted_sd(qg, Kx[:na], Vx[:na], ks[:na], vs[:na], SM)
+            zs.append(normalised_errors(out[i, h * G:(h + 1) * G], ex[0], sd))
+        z = np.concatenate([x.ravel() for x in zs])
+        rms = float(np.sqrt(np.mean(z ** 2)))
+        print(f"8-bit prefill vs exact, kv head {h}: normalised error RMS {rms:.3f}, max {np.abs(z).max():.2f}",
+              flush=True)
+        assert rms <= 1.2 and np.abs(z).max() <= 6.0
 
 
 # ---- the next rows at the benchmark's shapes --------------------------------

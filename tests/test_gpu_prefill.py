@@ -17,7 +17,7 @@ PAGE = 64
 class Chunk:
     """A sequence whose first pos0 tokens are cached; a chunk of T new tokens follows."""
 
-    def __init__(self, pos0, T, Hkv=4, G=4, D=256, seed=0, extra_pages=2, v_per_token=False):
+    def __init__(self, pos0, T, Hkv=4, G=4, D=256, seed=0, extra_pages=2, v_per_token=False, outliers=False):
         g = synth.rng(600 + seed, 0)
         n = pos0 + T
         npg = (n + PAGE - 1) // PAGE
@@ -30,6 +30,10 @@ class Chunk:
         self.k_new = synth.normal_f32(g, (T, Hkv, D))
         self.v_new = synth.normal_f32(g, (T, Hkv, D))
         self.qbits = synth.f32_to_bf16_bits(synth.normal_f32(g, (T, self.Hq, D)))
+        if outliers:
+            cols = synth.outlier_columns(g, Hkv, D)
+            for x in (k_old, v_old, self.k_new, self.v_new):
+                synth.apply_outliers(x, cols)
         t = np.arange(pos0)
         old_slots = (self.pt[t // PAGE].astype(np.int64) * PAGE + t % PAGE).astype(np.int32)
         self.oc = of4.Cache(self.P, Hkv, D, v_per_token=v_per_token)

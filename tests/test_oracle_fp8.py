@@ -125,7 +125,7 @@ def test_keys_to_int8():
     exact = codes * np.repeat(scales, 32, axis=1)
     assert np.all(np.abs(Kt * tau[:, None] - exact) <= tau[:, None] / 2)
     np.testing.assert_array_equal(np.log2(tau), fp16_exponent_rule(scales.max(axis=1)) - 4)
-    # a half-way case rounds up (toward +inf): scale 1.5 over tau = 1 gives c * 1.5
+    # half-way cases round to the even integer
     c = np.zeros((1, 256), dtype=np.int64)
     c[0, :4] = [1, -1, 3, -3]
     s = np.zeros((1, 8))
@@ -135,7 +135,12 @@ def test_keys_to_int8():
     Kt, tau = fp8.requantize_keys(c, s)
     assert tau[0] == 2.0 ** -3
     assert list(Kt[0, :4]) == [12, -12, 36, -36]
-    assert list(Kt[0, 32:36]) == [1, 0, 2, -1]          # 0.5 -> 1, -0.5 -> 0, 1.5 -> 2, -1.5 -> -1
+    assert list(Kt[0, 32:36]) == [0, 0, 2, -2]          # 0.5 -> 0, -0.5 -> 0, 1.5 -> 2, -1.5 -> -2
+    # ties toward every side: codes -8..7 over scale 2^-4 (c / 2): even neighbours only
+    c2 = np.zeros((1, 256), dtype=np.int64)
+    c2[0, 32:48] = np.arange(-8, 8)
+    Kt2, _ = fp8.requantize_keys(c2, s)
+    np.testing.assert_array_equal(Kt2[0, 32:48], [-4, -4, -3, -2, -2, -2, -1, 0, 0, 0, 1, 2, 2, 2, 3, 4])
 
 
 def exact_case(seed, pos0, T, v_per_token=False):
@@ -219,3 +224,44 @@ def test_model_error_budget_on_random_inputs():
     # score); the total mass l e^m, which is what a fold uses, within ~1%
     assert np.abs(m8 - m).max() <= 0.05 * np.abs(m).max()
     assert np.abs((np.log(l8) + m8) - (np.log(l) + m)).max() <= 0.02
+
+
+def test_model_within_the_error_predicted_from_the_formats():
+    """The 8-bit model against the exact attention, each error divided by the
+    standard deviation predicted from the formats' steps alone (tests/
+    fp8_bound.py): RMS at most ~1 (the INT8 steps use upper bounds) and not
+    vacuous, no value beyond 6.  Both V layouts, with outlier channels."""
+    from fp8_bound import normalised_errors, predicted_sd
+    g = np.random.default_rng(21)
+    for vtok in (False, True):
+        H, D, Hq, pos0, T = 2, 256, 8, 700, 40
+        n = pos0 + T
+        npg = (n + 63) // 64
+        pt = g.permutation(npg + 2)[:npg].astype(np.int32)
+        cache = of4.Cache(npg + 2, H, D, v_per_token=vtok)
+        t = np.arange(n)
+        slots = (pt[t // 64].astype(np.int64) * 64 + t % 64).astype(np.int32)
+        k = g.standard_normal((n, H, D)).astype(np.float32)
+        v = g.standard_normal((n, H, D)).astype(np.float32)
+        k[:, :, [5, 77]] *= 8
+        v[:, :, [5, 77]] *= 8
+        cache.write(k, v, slots)
+        q = of4.bf16_round(g.standard_normal((T, Hq, D)))
+        o8, _, _ = fp8.prefill(cache, q, pt, pos0, 1 / 16)
+        o, _, _ = oatt.prefill(cache, q, pt, pos0, 1 / 16)
+        zs = []
+        for kv in range(H):
+            K, V = oatt.gather_values(cache, pt, n, kv)
+            codes = [cache.page_codes(int(pt[lp]), kv) for lp in range(npg)]
+            ks = np.concatenate([c[1] for c in codes])[:n].astype(np.float64)
+            vs = np.concatenate([c[3] for c in codes])[:n].astype(np.float64)
+            for i in range(0, T, 3):
+                m = pos0 + i + 1
+                hs = slice(kv * 4, kv * 4 + 4)
+                sd = predicted_sd(q[i, hs], K[:m], V[:m], ks[:m], vs[:m], 1 / 16)
+                zs.append(normalised_errors(o8[i, hs], o[i, hs], sd))
+        z = np.concatenate([x.ravel() for x in zs])
+        rms = math.sqrt(float(np.mean(z ** 2)))
+        print(f"8-bit model vs exact: RMS of normalised error {rms:.3f}, max {np.abs(z).max():.2f}")
+        assert 0.3 <= rms <= 1.2, rms
+        assert np.abs(z).max() <= 6.0, np.abs(z).max()
