@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define F4KV_ABI_VERSION 3
+#define F4KV_ABI_VERSION 4
 
 enum {
   F4KV_OK = 0,
@@ -346,6 +346,31 @@ int paged_attn_prefill_f4_fp8(const f4kv_cache* cache, const uint16_t* q,
 int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const int32_t* cu_seq_lens,
                        int32_t B, int32_t max_pages, int32_t total_tokens, void* k_out, void* v_out,
                        int32_t out_dtype, hipStream_t stream);
+
+/*
+ * Device-side checks (a debugging aid).  Context lengths, page ids, slot ids
+ * and row offsets live in device memory, where the host cannot validate them;
+ * the kernels skip out-of-range entries rather than read or write out of
+ * bounds.  f4kv_device_checks(1) makes every following call (on any thread)
+ * first launch a small check kernel on its stream that ORs the flags below
+ * into a word of the current device; f4kv_device_check_word(&w) waits for the
+ * device, returns that word and clears it.  f4kv_device_checks(0) (the
+ * default) launches nothing.  Checked: every context length in
+ * [0, max_context_len] (decode); the page ids of every live page (tokens
+ * below the context length, or pos0 + T for prefill, or the row count for
+ * the gather) in [0, num_pages); every slot id -1 or in [0, num_pages * 64)
+ * (the writer; distinctness is not checked); cu_seq_lens starting at 0,
+ * non-decreasing, lengths at most max_pages * 64, cu_seq_lens[B] <=
+ * total_tokens (the gather).
+ */
+enum {
+  F4KV_CHECK_CONTEXT = 1,  /* a context length outside [0, max_context_len] */
+  F4KV_CHECK_PAGE = 2,     /* a live page id outside [0, num_pages)         */
+  F4KV_CHECK_SLOT = 4,     /* a slot id neither -1 nor a slot of the pool    */
+  F4KV_CHECK_ROWS = 8      /* cu_seq_lens not a valid list of row offsets    */
+};
+int f4kv_device_checks(int32_t on);
+int f4kv_device_check_word(uint32_t* word);
 
 /*
  * Kernel timing (a measurement aid of this library, not an operation of the

@@ -8,6 +8,10 @@ current stream, allocates outputs and workspaces with torch, and raises
 library is not built the calls raise; there is no other code path.
 """
 from ._binding import (  # noqa: F401
+    CHECK_CONTEXT,
+    CHECK_PAGE,
+    CHECK_ROWS,
+    CHECK_SLOT,
     KERNEL_DECODE,
     KERNEL_PREFILL,
     KERNEL_PREFILL_FP8,
@@ -19,6 +23,8 @@ from ._binding import (  # noqa: F401
     cache_bytes,
     decode_rows_workspace_size,
     decode_workspace_size,
+    device_check_word,
+    device_checks,
     gather_kv_cache_f4,
     kv_cache_write_f4,
     library_path,
@@ -51,6 +57,8 @@ EXPORTED_SYMBOLS = (
     "paged_attn_prefill_f4",
     "paged_attn_prefill_f4_fp8",
     "gather_kv_cache_f4",
+    "f4kv_device_checks",
+    "f4kv_device_check_word",
     "f4kv_timing_start",
     "f4kv_timing_stop",
 )

@@ -60,11 +60,14 @@ _SIGS = {
     "paged_attn_prefill_f4_fp8": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                                             _P, _P, _P, _P, C.c_size_t, _P]),
     "gather_kv_cache_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _I, _I, _I, _P, _P, _I, _P]),
+    "f4kv_device_checks": (C.c_int, [_I]),
+    "f4kv_device_check_word": (C.c_int, [C.POINTER(C.c_uint32)]),
     "f4kv_timing_start": (C.c_int, [_I, _I]),
     "f4kv_timing_stop": (C.c_int, [_I, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
 }
 
 KERNEL_DECODE, KERNEL_PREFILL, KERNEL_PREFILL_FP8 = 0, 1, 2
+CHECK_CONTEXT, CHECK_PAGE, CHECK_SLOT, CHECK_ROWS = 1, 2, 4, 8
 
 
 def library_path() -> str:
@@ -448,3 +451,17 @@ class KernelTimer:
     @property
     def avg_ms(self) -> float:
         return self.total_ms / self.launches if self.launches else float("nan")
+
+
+def device_checks(on: bool):
+    """Switch the device-side checks of context lengths, page ids, slot ids and
+    row offsets on or off (process-wide; off by default)."""
+    _check("f4kv_device_checks", load_library().f4kv_device_checks(1 if on else 0))
+
+
+def device_check_word() -> int:
+    """Wait for the device, return the OR of the CHECK_* flags raised on the
+    current device since the last read, and clear it."""
+    w = C.c_uint32(0)
+    _check("f4kv_device_check_word", load_library().f4kv_device_check_word(C.byref(w)))
+    return int(w.value)

@@ -140,6 +140,10 @@ int kv_cache_write_f4(const f4kv_cache* cache, const float* k, const float* v, c
   if (!k || !v || !slot_mapping) return fail(F4KV_ERR_INVALID, "%s: NULL array", fn);
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 4))
     return fail(F4KV_ERR_INVALID, "%s: k, v must be 16-byte aligned", fn);
+  if (f4kv::checks_on()) {
+    hipError_t e = f4kv::check_slots(slot_mapping, T, static_cast<int64_t>(cache->num_pages) * f4kv::kPage, stream);
+    if (e != hipSuccess) return launched(e, fn);
+  }
   return launched(f4kv::launch_kv_write(*cache, k, v, slot_mapping, T, stream), fn);
 }
 
@@ -199,6 +203,11 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4) ||
       (out_m && !aligned(out_m, 4)) || (out_l && !aligned(out_l, 4)))
     return fail(F4KV_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (f4kv::checks_on()) {
+    hipError_t e = f4kv::check_pages(context_lens, 0, page_table, B, max_pages, max_context_len, cache->num_pages,
+                                     stream);
+    if (e != hipSuccess) return launched(e, fn);
+  }
   if (const int32_t sp = f4kv::rows_prefill_splits(B, R, Hq, Hkv, max_context_len, num_windows, window_tokens)) {
     const size_t need = f4kv::rows_prefill_ws_bytes(B, R, Hq, sp);
     if (need > 0) {
@@ -323,6 +332,10 @@ int prefill_common(const char* fn, bool fp8, const f4kv_cache* cache, const uint
                   workspace ? ws_bytes : size_t(0));
     if (!aligned(workspace, 16)) return fail(F4KV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
   }
+  if (f4kv::checks_on()) {
+    hipError_t e = f4kv::check_pages(nullptr, pos0 + T, page_table, 1, max_pages, pos0 + T, cache->num_pages, stream);
+    if (e != hipSuccess) return launched(e, fn);
+  }
   if (k_new) {
     hipError_t e = f4kv::launch_kv_write_paged(*cache, k_new, v_new, page_table, pos0, T, stream);
     if (e != hipSuccess) return launched(e, fn);
@@ -375,9 +388,27 @@ int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const
     return fail(F4KV_ERR_INVALID, "%s: page_table, cu_seq_lens must be 4-byte and the outputs 16-byte aligned", fn);
   if (static_cast<int64_t>(total_tokens) * cache->num_kv_heads * cache->head_dim > (int64_t(1) << 40))
     return fail(F4KV_ERR_INVALID, "%s: output too large", fn);
+  if (f4kv::checks_on()) {
+    hipError_t e = f4kv::check_rows(cu_seq_lens, B, page_table, max_pages, total_tokens, cache->num_pages, stream);
+    if (e != hipSuccess) return launched(e, fn);
+  }
   return launched(f4kv::launch_gather(*cache, page_table, cu_seq_lens, B, max_pages, total_tokens, k_out, v_out,
                                       out_dtype == F4KV_BF16, stream),
                   fn);
+}
+
+int f4kv_device_checks(int32_t on) {
+  if (on != 0 && on != 1) return fail(F4KV_ERR_INVALID, "f4kv_device_checks: on must be 0 or 1 (got %d)", on);
+  f4kv::set_checks(on == 1);
+  return ok();
+}
+
+int f4kv_device_check_word(uint32_t* word) {
+  const char* fn = "f4kv_device_check_word";
+  if (!word) return fail(F4KV_ERR_INVALID, "%s: word is NULL", fn);
+  hipError_t e = f4kv::read_check_word(word);
+  if (e != hipSuccess) return fail(F4KV_ERR_LAUNCH, "%s: reading the device word failed: %s", fn, hipGetErrorString(e));
+  return ok();
 }
 
 int f4kv_timing_start(int32_t kernel, int32_t max_launches) {

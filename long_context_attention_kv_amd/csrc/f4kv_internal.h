@@ -46,6 +46,18 @@ void timing_end(int kernel, hipStream_t s);
 hipError_t timing_start(int kernel, int max_launches);
 hipError_t timing_stop(int kernel, double* total_ms, int64_t* launches);
 
+// ---- device-side checks (host); see f4kv_device_checks ----------------------
+bool checks_on();
+void set_checks(bool on);
+hipError_t read_check_word(uint32_t* out);
+// context lengths (or one fixed length when ctx is null) and the page ids of
+// the live pages of B page-table rows
+hipError_t check_pages(const int32_t* ctx, int32_t fixed_len, const int32_t* pt, int32_t B, int32_t max_pages,
+                       int32_t max_ctx, int32_t num_pages, hipStream_t s);
+hipError_t check_slots(const int32_t* slots, int32_t T, int64_t num_slots, hipStream_t s);
+hipError_t check_rows(const int32_t* cu, int32_t B, const int32_t* pt, int32_t max_pages, int32_t total,
+                      int32_t num_pages, hipStream_t s);
+
 // ---- kernel launchers (host); arguments already validated ------------------
 hipError_t launch_kv_write(const f4kv_cache& c, const float* k, const float* v,
                            const int32_t* slots, int32_t T, hipStream_t s);

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int t = 8 * it + (tid >> 5);
     const int32_t i = lp * kPage + t;
     const int64_t row = static_cast<int64_t>(row0) + i;
-    if (i >= len || row >= a.total) continue;
+    if (i >= len || row < 0 || row >= a.total) continue;  // rows outside [0, total) are never written
     const int64_t e0 = (row * a.H + h) * kD + 8 * l;
     float v[8];
     // K: dword d of unit (c, t) holds elements 8d .. 8d + 7 of block c

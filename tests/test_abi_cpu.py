@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -222,3 +222,12 @@ def test_timing_argument_checks(lib):
     # stopping a timer that never started reports no launches and touches no device
     assert lib.f4kv_timing_stop(0, C.byref(ms), C.byref(n)) == 0
     assert ms.value == 0.0 and n.value == 0
+
+
+def test_device_checks_switch(lib):
+    """The switch takes 0 or 1 and launches nothing by itself; the word query
+    refuses a null pointer (reading the word needs a GPU: the GPU tests)."""
+    assert lib.f4kv_device_checks(2) == 1 and "0 or 1" in _err(lib)
+    assert lib.f4kv_device_checks(1) == 0
+    assert lib.f4kv_device_checks(0) == 0
+    assert lib.f4kv_device_check_word(None) == 1 and "NULL" in _err(lib)
