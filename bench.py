@@ -660,6 +660,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=458752)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run a plain device copy of BYTES bytes 3 times (calibrates HBM byte counters)")
+    ap.add_argument("--only", choices=["1m", "ragged", "prefill", "prefill_fp8"], default=None,
+                    help="run one workload alone (for profiling) and print its result; no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
@@ -670,6 +672,11 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}")
     if args.copy_probe:
         copy_probe(args.copy_probe)
+    if args.only:
+        run = {"1m": bench_1m, "ragged": bench_ragged, "prefill": bench_prefill,
+               "prefill_fp8": lambda: bench_prefill(fp8=True)}[args.only]
+        log(args.only, run())
+        return
     r = bench_config1(args.steps, args.warmup)
     log(f"config1: {r['ms_per_step']:.3f} ms/step ({'HIP graph' if r['step_in_graph'] else 'eager'}; eager "
         f"{r['ms_per_step_eager']:.3f}), {r['value'] / 1e9:.3f} G KV-tokens/s, decode kernel "

@@ -222,6 +222,80 @@ __device__ void build_work_list(const PlanArgs& p) {
   if (tid == 0) *p.n_items = base;
 }
 
+// The same work list, built by one wave when there are at most 64 (window,
+// sequence) ranges (lane r owns range r): reductions and the prefix sum run
+// on the wave's shuffles, with no workgroup barrier.
+__device__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ void build_work_list_wave(const PlanArgs& p) {
+  __shared__ int32_t s_end[64], s_p0[64], s_len[64];
+  const int lane = threadIdx.x;
+  const int n = p.W * p.B;
+  int p0 = 0, p1 = 0;
+  if (lane < n) window_pages(p, lane, p0, p1);
+  const int len = p1 - p0;
+  const int64_t total = wave_sum64(len);
+  const int64_t target = p.per_head_target;
+  int64_t lo = max<int64_t>(kWaves, (total + target - 1) / target);
+  int64_t hi = target > n ? max<int64_t>(lo, (total + target - n - 1) / (target - n)) : lo;
+  while (lo < hi) {  // smallest length in [lo, hi] whose chunk count fits
+    const int64_t mid = (lo + hi) / 2;
+    if (wave_sum64(lane < n ? (len + mid - 1) / mid : 0) <= target)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int pps = static_cast<int>(lo);
+  const int chunks = lane < n ? (len + pps - 1) / pps : 0;
+  int incl = chunks;  // inclusive prefix sum over the lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  s_end[lane] = incl;
+  s_p0[lane] = p0;
+  s_len[lane] = len;
+  if (lane < n) {
+    p.first[lane] = incl - chunks;
+    p.count[lane] = chunks;
+  }
+  const int items = __shfl(incl, 63, 64);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // identity rows of the empty ranges
+  uint64_t empty = __ballot(lane < n && len == 0);
+  while (empty) {
+    const int r = __builtin_ctzll(empty);
+    empty &= empty - 1;
+    const int64_t r0 = static_cast<int64_t>(r) * p.Hr;
+    for (int i = lane; i < p.Hr * kHeadDim; i += 64) p.out[r0 * kHeadDim + i] = 0.0f;
+    for (int i = lane; i < p.Hr; i += 64) {
+      if (p.out_m) p.out_m[r0 + i] = -INFINITY;
+      if (p.out_l) p.out_l[r0 + i] = 0.0f;
+    }
+  }
+  // item j belongs to the first range whose running count exceeds j
+  for (int j = lane; j < items; j += 64) {
+    int r = 0;
+#pragma unroll
+    for (int step = 32; step > 0; step >>= 1)
+      if (s_end[r + step - 1] <= j) r += step;
+    const int c_cnt = s_end[r] - (r ? s_end[r - 1] : 0);
+    const int c = j - (s_end[r] - c_cnt);
+    const int ln = s_len[r], q = ln / c_cnt, rem = ln % c_cnt;
+    const int beg = s_p0[r] + c * q + min(c, rem);
+    const int end = beg + q + (c < rem ? 1 : 0);
+    p.items[j] = make_int4(r, beg, end, j - c);
+  }
+  if (lane == 0) *p.n_items = items;
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                 false);
@@ -343,7 +417,11 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
                                                                int32_t Hkv, float qk_scale, PlanArgs plan,
                                                                int32_t R, int32_t r0, int32_t Gq) {
   if (blockIdx.x == gridDim.x - 1) {
-    build_work_list(plan);
+    if (plan.W * plan.B <= 64) {
+      if (threadIdx.x < 64) build_work_list_wave(plan);
+    } else {
+      build_work_list(plan);
+    }
     return;
   }
   __shared__ float qf[G][kHeadDim];
