@@ -377,7 +377,7 @@ def bench_rows(R, iters=10):
         f4.paged_attn_decode_rows_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # five or more rows (of 4 query heads per KV head) run on the prefill kernel
+    # three or more rows (of 4 query heads per KV head) run on the prefill kernel
     with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=64 * iters) as t, \
             f4.KernelTimer(f4.KERNEL_PREFILL, max_launches=64 * iters) as tp:
         e0.record()
@@ -660,7 +660,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=458752)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run a plain device copy of BYTES bytes 3 times (calibrates HBM byte counters)")
-    ap.add_argument("--only", choices=["1m", "ragged", "prefill", "prefill_fp8"], default=None,
+    ap.add_argument("--only", choices=["1m", "ragged", "prefill", "prefill_fp8", "rows8"], default=None,
                     help="run one workload alone (for profiling) and print its result; no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -674,7 +674,7 @@ def main():
         copy_probe(args.copy_probe)
     if args.only:
         run = {"1m": bench_1m, "ragged": bench_ragged, "prefill": bench_prefill,
-               "prefill_fp8": lambda: bench_prefill(fp8=True)}[args.only]
+               "prefill_fp8": lambda: bench_prefill(fp8=True), "rows8": lambda: bench_rows(8)}[args.only]
         log(args.only, run())
         return
     r = bench_config1(args.steps, args.warmup)

@@ -224,8 +224,14 @@ __device__ __forceinline__ void v_piece(PrefillSmem& sm, const VRaw& r, const VS
 }
 
 // VT: the cache's V scales are one per token and head.
-template <bool VT>
+// ROWS: the query rows of a verification round (at most 8 positions, 32 rows),
+// held by every wave: wave w multiplies token tile w & 1 of each page into
+// channel half w >> 1 of the output, with its own softmax state over the tokens
+// it sees, and the two token tiles of each channel half are folded at the end.
+// The page's dequantisation is shared as in the chunk kernel.
+template <bool VT, bool ROWS>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ pt) {
+  constexpr int kD = ROWS ? 4 : 8;  // 32-channel tiles of O^T per wave
   __shared__ PrefillSmem sm;
   const int seq = blockIdx.x / a.q_tiles;          // sequence
   const int qt = blockIdx.x - seq * a.q_tiles;     // query tile
@@ -233,6 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   const int split = blockIdx.z;  // key-range split
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
+  const int tt_w = wave & 1, ch_w = wave >> 1;  // ROWS: this wave's token tile and channel half
   int pos0 = a.pos0;
   if (a.ctx) pos0 = min(max(a.ctx[seq], 0), a.max_ctx) - a.T;
   pos0 = __builtin_amdgcn_readfirstlane(pos0);
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   const int hq = g * kG + (col & 3);
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
-    qi[c] = qt * kQPos + (wave * kCT + c) * 8 + col / 4;
+    qi[c] = qt * kQPos + ((ROWS ? 0 : wave) * kCT + c) * 8 + col / 4;
     qpos[c] = pos0 + qi[c];
     qexists[c] = qi[c] < a.T;
     qvalid[c] = qexists[c] && qpos[c] >= 0;  // a row at a negative position attends to nothing
@@ -313,11 +320,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   }
 
   static_assert(kCT == 1, "the page loop below is written for one column tile per wave");
-  float16_t acc[kCT][8];  // O^T per column tile: 8 channel tiles of 32
+  float16_t acc[kCT][kD];  // O^T per column tile: channel tiles of 32
 #pragma unroll
   for (int c = 0; c < kCT; ++c)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[c][d] = float16_t{};
+    for (int d = 0; d < kD; ++d) acc[c][d] = float16_t{};
   float m_run[kCT], s_max[kCT], l_lane[kCT];
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
@@ -419,6 +426,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // ROWS: O^T += V^T P^T for token tile tt and this wave's 4 channel tiles;
+  // step = 4 s2 + d as in pv_phase.
+  const char* vt_rows = vt_lane + ch_w * 4 * (32 * kPage * 2);
+  int voff_r[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) voff_r[s2] = 16 * vt_chunk(col, 2 * (2 * tt_w + s2) + half);
+  auto pv_rows = [&](const half8_t* pb, const half8_t* pl, auto&& piece) {
+    auto vread = [&](int step, half8_t* dst) {
+      const char* p = vt_rows + voff_r[step >> 2] + (step & 3) * (32 * kPage * 2);
+      dst[0] = *reinterpret_cast<const half8_t*>(p);
+      dst[1] = *reinterpret_cast<const half8_t*>(p + kHeadDim * kPage * 2);
+    };
+    half8_t vbuf[2][2];
+    vread(0, vbuf[0]);
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {
+      const int s2 = step >> 2, d = step & 3;
+      __builtin_amdgcn_sched_barrier(0);
+      if (step + 1 < 8) vread(step + 1, vbuf[(step + 1) & 1]);
+      const half8_t* vb = vbuf[step & 1];
+      acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[0], pb[s2], acc[0][d], 0, 0, 0);
+      acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[0], pl[s2], acc[0][d], 0, 0, 0);
+      acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[1], pb[s2], acc[0][d], 0, 0, 0);
+      piece(step);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // Softmax, first part: causal mask where the tile needs it, the row max, and
   // the lazy raise of the running max.  The max moves (and the accumulator and
   // any P operands not yet multiplied are rescaled) only when a score exceeds it
@@ -450,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       m_run[0] = mn;
       l_lane[0] *= alpha;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[0][d] *= alpha;
+      for (int d = 0; d < kD; ++d) acc[0][d] *= alpha;
       if (pb_prev) {  // the other tile's P operands, computed with the old max
         const _Float16 ah = static_cast<_Float16>(alpha);
 #pragma unroll
@@ -504,6 +539,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     __syncthreads();  // K of this page is in LDS; every wave is done with the previous V
     __builtin_amdgcn_sched_barrier(0);
 
+    if constexpr (ROWS) {
+      // ---- S^T of this wave's token tile, this thread's V units unpacked meanwhile ----
+      VScales vs;
+      read_vscales<VT>(sm, tid, lp & 1, vs);
+      uint32_t hv[4], lv[4];
+      float16_t st{};
+      s_phase(tt_w, st, [&](int step) { v_piece(sm, vcur, vs, tid, step >> 3, step & 7, hv, lv, nmagic); });
+      softmax_max(st, lp, tt_w, nullptr, nullptr);
+      half8_t pb[2], pl[2];
+      float e[2], psum = 0.0f;
+      const float off = p_offset();
+#pragma unroll
+      for (int h = 0; h < 16; ++h) p_half(st, off, h, e, psum, pb, pl);
+      l_lane[0] += psum * (1.0f / 2048.0f);
+      __syncthreads();  // V of this page is in LDS; every wave is done with this K
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- PV of this wave's tile and channel half, the next page's K meanwhile ----
+      pv_rows(pb, pl, [&](int step) {
+        unpack_k(sm, kraw, tid, step >> 2, step & 3, nmagic);
+        if (step == 7) store_vscales<VT>(sm, kraw, tid, (lp + 1) & 1);
+      });
+    } else {
     // ---- tile 0: S^T, V channels 0-2 of this page unpacked meanwhile ----
     VScales vs;
     read_vscales<VT>(sm, tid, lp & 1, vs);
@@ -554,6 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       else if (step == 3)
         store_vscales<VT>(sm, kraw, tid, (lp + 1) & 1);
     });
+    }
 
     vcur = vnext;
     cur_valid = kraw_valid;
@@ -563,8 +622,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   }
 
 
-  // ---- epilogue: this lane's two query rows ----
+  if constexpr (ROWS) {
+    // Fold the two token tiles of each channel half: the tile-1 wave leaves its
+    // state in LDS (lane-contiguous rows of floats), the tile-0 wave adds it.
+    // Both running maxima are integers, so the factors are exact powers of two.
+    __syncthreads();  // every wave is done with the page tiles
+    constexpr int kX = kD * 16 + 3;
+    float* xs = reinterpret_cast<float*>(&sm.k[0][0][0]) + ch_w * kX * 64;
+    static_assert(2 * kX * 64 * sizeof(float) <= sizeof(sm.k), "fold buffer fits the K tiles");
+    if (tt_w == 1) {
+#pragma unroll
+      for (int d = 0; d < kD; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[(d * 16 + i) * 64 + lane] = acc[0][d][i];
+      xs[(kD * 16) * 64 + lane] = m_run[0];
+      xs[(kD * 16 + 1) * 64 + lane] = s_max[0];
+      xs[(kD * 16 + 2) * 64 + lane] = l_lane[0];
+    }
+    __syncthreads();
+    if (tt_w == 1) return;
+    const float m1 = xs[(kD * 16) * 64 + lane], s1 = xs[(kD * 16 + 1) * 64 + lane];
+    const float l1 = xs[(kD * 16 + 2) * 64 + lane];
+    const float M = fmaxf(m_run[0], m1);
+    const float a0 = m_run[0] == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_run[0] - M));
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m1 - M));
+#pragma unroll
+    for (int d = 0; d < kD; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[0][d][i] = acc[0][d][i] * a0 + xs[(d * 16 + i) * 64 + lane] * a1;
+    l_lane[0] = l_lane[0] * a0 + l1 * a1;
+    s_max[0] = fmaxf(s_max[0], s1);
+    m_run[0] = M;
+  }
+
+  // ---- epilogue: this lane's query row (ROWS: this wave's channel half) ----
   const int64_t R = static_cast<int64_t>(a.B) * a.T * a.Hq;
+  const int d0 = ROWS ? 4 * ch_w : 0;  // first channel tile of acc
 #pragma unroll
   for (int c = 0; c < kCT; ++c) {
     // restore the exact maximum: the normalised output is unchanged, the sum scales
@@ -576,7 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     const float inv = Lr > 0.0f ? 1.0f / (Lr * 2048.0f) : 0.0f;  // P was carried times 2^11
     float* dst = a.o + row * kHeadDim;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+    for (int d = 0; d < kD; ++d)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         float4_t v;
@@ -584,9 +677,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
         v.y = acc[c][d][4 * i4 + 1] * inv;
         v.z = acc[c][d][4 * i4 + 2] * inv;
         v.w = acc[c][d][4 * i4 + 3] * inv;
-        *reinterpret_cast<float4_t*>(dst + d * 32 + i4 * 8 + half * 4) = v;
+        *reinterpret_cast<float4_t*>(dst + (d0 + d) * 32 + i4 * 8 + half * 4) = v;
       }
-    if (half == 0) {
+    if (half == 0 && (!ROWS || wave == 0)) {
       if (a.m) a.m[row] = L > 0.0f ? s_max[c] * kLn2 : -INFINITY;
       if (a.l) a.l[row] = L;
     }
@@ -655,9 +748,9 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
   }
   timing_begin(F4KV_KERNEL_PREFILL, s);
   if (c.v_scale_per_token)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a, pt);
+    hipLaunchKernelGGL((prefill_kernel<true, false>), dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a, pt);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(plan.q_tiles, a.Hkv, plan.kv_splits), dim3(kThreads), 0, s, a,
                        pt);
   hipError_t e = hipGetLastError();
   timing_end(F4KV_KERNEL_PREFILL, s);
@@ -665,14 +758,15 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
   return launch_merge(pm, pl, a.o, plan.kv_splits, static_cast<int32_t>(R), kHeadDim, out, out_m, out_l, s);
 }
 
-// Five or more rows of a group of 4 query heads (20 or more rows per KV head,
-// three or more passes of the decode kernel over the pages) go through this
+// Three or more rows of a group of 4 query heads (12 or more rows per KV head,
+// two or more passes of the decode kernel over the pages) go through this
 // kernel, whose workgroup reads each page once for up to 32 rows with
-// matrix-core products: a verification round is a short causal prefill over
-// the cache.  Whole-context calls only.
+// matrix-core products (the ROWS form: the four waves share the rows and
+// split each page's tokens and output channels): a verification round is a
+// short causal prefill over the cache.  Whole-context calls only.
 int32_t rows_prefill_splits(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
                             int32_t window_tokens) {
-  if (R < 5 || R > 8 || Hq != 4 * Hkv || num_windows != 1 || window_tokens != 0 || B <= 0) return 0;
+  if (R < 3 || R > 8 || Hq != 4 * Hkv || num_windows != 1 || window_tokens != 0 || B <= 0) return 0;
   const int64_t wgs = static_cast<int64_t>(B) * Hkv;
   const int64_t total_pages = (static_cast<int64_t>(max_ctx) + kPage - 1) / kPage;
   int64_t splits = 512 / wgs;  // at most two rounds of one workgroup per CU, as the prefill plans
@@ -686,8 +780,8 @@ size_t rows_prefill_ws_bytes(int32_t B, int32_t R, int32_t Hq, int32_t splits) {
 }
 
 // R <= 8 query rows of each of B sequences, row r at position ctx[b] - R + r,
-// causal over the cache: one query tile per sequence (only the first wave's
-// rows exist), the key range split kv_splits ways and folded by the merge.
+// causal over the cache: one query tile per sequence (every wave holds its
+// rows), the key range split kv_splits ways and folded by the merge.
 hipError_t launch_prefill_rows(const f4kv_cache& c, const uint16_t* q, const int32_t* pt, const int32_t* ctx,
                                int32_t B, int32_t R, int32_t Hq, int32_t max_pages, int32_t max_ctx, float sm_scale,
                                float* out, float* out_m, float* out_l, void* ws, int32_t kv_splits, hipStream_t s) {
@@ -730,9 +824,9 @@ hipError_t launch_prefill_rows(const f4kv_cache& c, const uint16_t* q, const int
   const dim3 grid(B, a.Hkv, kv_splits);
   timing_begin(F4KV_KERNEL_PREFILL, s);
   if (c.v_scale_per_token)
-    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kThreads), 0, s, a, pt);
+    hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kThreads), 0, s, a, pt);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kThreads), 0, s, a, pt);
+    hipLaunchKernelGGL((prefill_kernel<false, true>), grid, dim3(kThreads), 0, s, a, pt);
   hipError_t e = hipGetLastError();
   timing_end(F4KV_KERNEL_PREFILL, s);
   if (e != hipSuccess || kv_splits == 1) return e;

@@ -31,7 +31,7 @@ def _run(ps, R, Hq, seed, W=1, wt=0):
 
 @pytest.mark.parametrize("R", [2, 3, 5, 8])
 def test_rows_group_of_four(R):
-    # 4 query heads per KV head: 2 rows per pass over the pages, so 3 rows take two passes; 5 and more
+    # 4 query heads per KV head: 2 rows run on the decode kernel (one pass over the pages); 3 and more
     # rows of a whole-context call go through the prefill kernel
     ps = PagedSet([700, 130, 64 * 20 + 5], Hkv=4, seed=900 + R)
     (o, m, l), (ro, rm, rl), _ = _run(ps, R, 16, R)
@@ -62,15 +62,19 @@ def test_one_row_is_plain_decode_and_last_row_matches_decode():
     pt, lens = ps.gpu_page_table(), ps.gpu_lengths()
     one = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 2:3].copy()), pt, lens, 2000, SM)[0]
     dec = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits[:, 2].copy()), pt, lens, 2000, SM)[0]
+    # two rows run on the decode kernel too (its products, to within fp32 summation order); three rows
+    # on the prefill kernel (its own products, within the attention tolerance)
+    two = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 1:3].copy()), pt, lens, 2000, SM)[0]
     three = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), pt, lens, 2000, SM)[0]
     torch.cuda.synchronize()
     assert torch.equal(one[:, :, 0], dec)
-    assert torch.allclose(three[:, :, 2], dec, rtol=0, atol=1e-5 * float(dec.abs().max()))
+    assert torch.allclose(two[:, :, 1], dec, rtol=0, atol=1e-5 * float(dec.abs().max()))
+    assert_attention_close(three[:, :, 2].cpu().numpy(), dec.cpu().numpy(), "last of three rows vs decode")
 
 
 @pytest.mark.parametrize("v_per_token", [False, True])
 def test_rows_through_the_prefill_kernel_short_contexts(v_per_token):
-    """Rows of whole-context calls with R >= 5 (group of 4) run on the prefill
+    """Rows of whole-context calls with R >= 3 (group of 4) run on the prefill
     kernel: contexts shorter than R leave the leading rows empty (the merge
     identity), an empty context all of them."""
     print(f"rows via prefill, short contexts, v_per_token={v_per_token}", flush=True)
@@ -99,3 +103,34 @@ def test_rows_through_the_prefill_kernel_agree_with_the_decode_kernel():
     assert_states_close(a[1], a[2], b[1], b[2], "prefill kernel vs decode kernel")
     ro, rm, rl = oatt.decode_rows(ps.oc, qv, ps.pt, ps.lengths, SM)
     assert_attention_close(a[0], ro, "prefill kernel vs oracle")
+
+
+def test_rows_through_the_prefill_kernel_drop_out_of_range_pages():
+    """Out-of-range page ids on the prefill kernel's verification route (R = 4):
+    those pages' tokens are dropped; each row's expected result is the oracle's
+    attention over the remaining tokens up to its position."""
+    print("rows via prefill, out-of-range page ids", flush=True)
+    R = 4
+    ps = PagedSet([1300, 200], Hkv=4, seed=960)
+    pt = ps.pt.copy()
+    dropped = {0: [0, 9], 1: [2]}
+    pt[0, 0] = ps.num_pages + 3
+    pt[0, 9] = -1
+    pt[1, 2] = -5
+    bits, qv = _q(2, R, 16, 60)
+    out, m, l = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), torch.from_numpy(pt).cuda(),
+                                             ps.gpu_lengths(), 1300, SM)
+    torch.cuda.synchronize()
+    out, m, l = out.cpu().numpy()[0], m.cpu().numpy()[0], l.cpu().numpy()[0]
+    for b, n in enumerate(ps.lengths):
+        keep = np.ones(n, bool)
+        for lp in dropped[b]:
+            keep[lp * 64:(lp + 1) * 64] = False
+        for g in range(4):
+            K, V = oatt.gather_values(ps.oc, ps.pt[b], n, g)
+            for r in range(R):
+                sel = keep & (np.arange(n) <= n - R + r)
+                ro, rm, rl = oatt.decode_head_from_values(qv[b, r, 4 * g:4 * g + 4], K[sel], V[sel], SM)
+                hs = slice(4 * g, 4 * g + 4)
+                assert_attention_close(out[b, r, hs], ro[0], f"rows b={b} r={r} kv head {g}")
+                assert_states_close(m[b, r, hs], l[b, r, hs], rm[0], rl[0], f"rows b={b} r={r} g={g}")
