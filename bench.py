@@ -137,11 +137,18 @@ def decode_algorithmic_bytes(lengths, windows=1, per_token_head=None):
     return kv + q + pt + out
 
 
-def run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs):
-    """One step: YaRN rows, rotations, new-token writes, decode per layer."""
+def run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs, one_call=False):
+    """One step: YaRN rows, rotations, new-token writes, decode per layer; with
+    one_call the rotations, the write and the decode of a layer go through
+    paged_attn_decode_step_f4 (the same results, bit for bit)."""
     yp = yarn_params(factor)
     c, s = f4.yarn_rope_table(yp, positions)
     for i, L in enumerate(layers):
+        if one_call:
+            f4.paged_attn_decode_step_f4(L.cache, c, s, q_raw[i], k_new[i], v_new[i], L.new_slots, L.pt, L.ctx,
+                                         max(L.lengths), SM, out=outs[i][0], out_m=outs[i][1], out_l=outs[i][2],
+                                         workspace=ws)
+            continue
         q = f4.yarn_rope_apply(c, s, q_raw[i])
         k = f4.yarn_rope_apply(c, s, k_new[i])
         f4.kv_cache_write_f4(L.cache, k, v_new[i], L.new_slots)
@@ -207,32 +214,37 @@ def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
     ms_step_eager = max(gpu_ms, wall * 1e3) / steps
     tokens = n_layers * lanes * ctx
 
-    # The same step captured once in a HIP graph and replayed: the launches of
-    # the 16 layers (rope, write, query preparation, decode, fold) go out without
-    # host round trips.  Every replay is checked against an eager step first.
-    graph_ok, ms_step_graph = False, None
-    try:
-        ref = [tuple(t.clone() for t in o) for o in outs]  # outputs of the last eager step
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs)  # warm the side stream
+    # The step captured once in a HIP graph and replayed, in both forms: the
+    # separate calls of each layer (rope, rope, write, query preparation, decode,
+    # fold) and the one-call step (query preparation with the rotations and the
+    # write, decode, fold).  The launches of the 16 layers go out without host
+    # round trips.  Every replay is checked against the eager step first.
+    ref = [tuple(t.clone() for t in o) for o in outs]  # outputs of the last eager step
+
+    def graph_step_ms(one_call):
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs, one_call)  # warm up
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=side):
+                    run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs, one_call)
             torch.cuda.synchronize()
-            with torch.cuda.graph(graph, stream=side):
+            ok = True
+            for _ in range(3):  # replays, with eager work in between, each against the eager result
+                for o in outs:
+                    for t in o:
+                        t.fill_(float("nan"))
+                graph.replay()
+                torch.cuda.synchronize()
+                ok = ok and all(torch.equal(a, b) for o, r in zip(outs, ref) for a, b in zip(o, r))
                 run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs)
-        torch.cuda.synchronize()
-        graph_ok = True
-        for _ in range(3):  # replays, with eager work in between, each against the eager result
-            for o in outs:
-                for t in o:
-                    t.fill_(float("nan"))
-            graph.replay()
-            torch.cuda.synchronize()
-            graph_ok = graph_ok and all(torch.equal(a, b) for o, r in zip(outs, ref) for a, b in zip(o, r))
-            run_decode_step(layers, q_raw, k_new, v_new, positions, factor, ws, outs)
-            torch.cuda.synchronize()
-        if graph_ok:
+                torch.cuda.synchronize()
+            if not ok:
+                log(f"graph replay ({'one call' if one_call else 'separate calls'}) differs from the eager step")
+                return None
             for _ in range(warmup):
                 graph.replay()
             torch.cuda.synchronize()
@@ -245,19 +257,27 @@ def bench_config1(steps, warmup, n_layers=16, lanes=3, ctx=262144, factor=4.0):
             g1.record()
             torch.cuda.synchronize()
             wall_g = time.perf_counter() - t_start
-            ms_step_graph = max(g0.elapsed_time(g1), wall_g * 1e3) / steps
-        else:
-            log("graph replay differs from the eager step: reporting the eager step time")
-    except Exception as e:  # graph capture unavailable: the eager step stands
-        log(f"graph capture failed ({type(e).__name__}: {e}); reporting the eager step time")
-        graph_ok = False
+            return max(g0.elapsed_time(g1), wall_g * 1e3) / steps
+        except Exception as e:  # graph capture unavailable: the eager step stands
+            log(f"graph capture failed ({type(e).__name__}: {e})")
+            return None
+
+    ms_step_separate = graph_step_ms(False)
+    ms_step_one_call = graph_step_ms(True)
+    graph_ok = ms_step_one_call is not None or ms_step_separate is not None
+    ms_step_graph = ms_step_one_call if ms_step_one_call is not None else ms_step_separate
+    if not graph_ok:
+        log("reporting the eager step time")
     ms_step = ms_step_graph if graph_ok else ms_step_eager
     dec_avg_ms = float(np.mean(dec_ms))
     dec_bytes = decode_algorithmic_bytes([ctx] * lanes)
     return {
         "ms_per_step": ms_step,
         "ms_per_step_eager": ms_step_eager,
+        "ms_per_step_separate_calls": ms_step_separate,
+        "ms_per_step_one_call": ms_step_one_call,
         "step_in_graph": graph_ok,
+        "step_one_call": ms_step_one_call is not None,
         "kv_tokens_per_step": tokens,
         "value": tokens / (ms_step / 1e3),
         "decode_call_ms_avg": dec_avg_ms,
@@ -678,7 +698,9 @@ def main():
         log(args.only, run())
         return
     r = bench_config1(args.steps, args.warmup)
-    log(f"config1: {r['ms_per_step']:.3f} ms/step ({'HIP graph' if r['step_in_graph'] else 'eager'}; eager "
+    fmt = lambda x: "-" if x is None else f"{x:.3f}"
+    log(f"config1: {r['ms_per_step']:.3f} ms/step ({'HIP graph' if r['step_in_graph'] else 'eager'}; one-call step "
+        f"{fmt(r['ms_per_step_one_call'])}, separate calls {fmt(r['ms_per_step_separate_calls'])}, eager "
         f"{r['ms_per_step_eager']:.3f}), {r['value'] / 1e9:.3f} G KV-tokens/s, decode kernel "
         f"{r['decode_kernel_ms_avg'] * 1e3:.1f} us -> {r['decode_gbs']:.0f} GB/s, whole call "
         f"{r['decode_call_ms_avg'] * 1e3:.1f} us -> {r['decode_call_gbs']:.0f} GB/s")
@@ -704,7 +726,7 @@ def main():
         torch.cuda.empty_cache()
         extra["gather_bf16"] = bench_gather()
         log("gather:", extra["gather_bf16"])
-        for R in (2, 5, 8):
+        for R in (2, 4, 8):
             torch.cuda.empty_cache()
             extra[f"decode_rows_{R}"] = bench_rows(R)
             log(f"rows {R}:", extra[f"decode_rows_{R}"])
@@ -749,7 +771,11 @@ def main():
         "config": {"workload": "decode: 16 layers x 3 lanes x 262,144 cached tokens, 16 query / 4 KV heads, "
                                "head_dim 256, 64-token pages, F4 KV, YaRN x4, 1% outlier channels x8",
                    "lanes": 3, "context": 262144, "layers": 16,
-                   "step": "HIP graph replay" if r["step_in_graph"] else "eager launches",
+                   "step": ("HIP graph replay" if r["step_in_graph"] else "eager launches") +
+                           (" of paged_attn_decode_step_f4 per layer" if r["step_one_call"] else
+                            " of yarn_rope_apply x2, kv_cache_write_f4, paged_attn_decode_f4 per layer"),
+                   "ms_per_step_one_call": r["ms_per_step_one_call"],
+                   "ms_per_step_separate_calls": r["ms_per_step_separate_calls"],
                    "ms_per_step_eager": r["ms_per_step_eager"]},
         "roofline": {"bound": "hbm", "achieved": r["decode_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": r["decode_gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define F4KV_ABI_VERSION 4
+#define F4KV_ABI_VERSION 5
 
 enum {
   F4KV_OK = 0,
@@ -223,6 +223,39 @@ int paged_attn_decode_f4_noalloc(const f4kv_cache* cache, const uint16_t* q,
                                  int32_t B, int32_t Hq, int32_t max_pages, int32_t max_context_len,
                                  int32_t num_windows, int32_t window_tokens, float sm_scale,
                                  float* out, float* out_m, float* out_l, hipStream_t stream);
+
+/*
+ * paged_attn_decode_step_f4 [MRS items 1 and 2: the keys are rotated before
+ * they are quantised into the cache, the queries at attention time; FT item 2]
+ * One decode step of a layer in one call: the new token of each sequence is
+ * rotated and written, then each sequence's query attends over its cache, the
+ * new token included.  Equivalent, bit for bit, to
+ *   yarn_rope_apply(cos_rows, sin_rows, q  -> bf16 q_rot,  T = B, H = Hq)
+ *   yarn_rope_apply(cos_rows, sin_rows, k_new -> fp32 k_rot, T = B, H = num_kv_heads)
+ *   kv_cache_write_f4(cache, k_rot, v_new, slots, T = B)
+ *   paged_attn_decode_f4(cache, q_rot, ...)
+ * with the rotation, the write and the query preparation in one launch (the
+ * decode's own), so the step costs the decode's launches only.
+ *   cos_rows, sin_rows  fp32 [B][rotary_dim / 2]: row b is the table row of
+ *                       sequence b's new token (yarn_rope_table at its position)
+ *   rotary_dim          even, in (0, head_dim]; channels from it on pass through
+ *   q                   bf16 [B][Hq][D], not yet rotated, 16-byte aligned
+ *   k_new, v_new        fp32 [B][num_kv_heads][D], k not yet rotated, 16-byte aligned
+ *   slots               int32 [B]: cache slot (page * 64 + offset) of each new
+ *                       token; -1 (or a slot outside the pool) writes nothing.
+ *                       context_lens must already count the new token.
+ *   other arguments, the workspace (paged_attn_decode_f4_workspace_size) and
+ *   the outputs as paged_attn_decode_f4.
+ * The inputs q, k_new and v_new are not modified.
+ */
+int paged_attn_decode_step_f4(const f4kv_cache* cache, const float* cos_rows, const float* sin_rows,
+                              int32_t rotary_dim, const uint16_t* q, const float* k_new,
+                              const float* v_new, const int32_t* slots,
+                              const int32_t* page_table, const int32_t* context_lens,
+                              int32_t B, int32_t Hq, int32_t max_pages, int32_t max_context_len,
+                              int32_t num_windows, int32_t window_tokens, float sm_scale,
+                              float* out, float* out_m, float* out_l,
+                              void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * paged_attn_decode_rows_f4 [IGN --spec-draft-tokens / --spec-draft-rows: a

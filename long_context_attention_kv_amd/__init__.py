@@ -32,6 +32,7 @@ from ._binding import (  # noqa: F401
     lse_merge,
     paged_attn_decode_f4,
     paged_attn_decode_f4_noalloc,
+    paged_attn_decode_step_f4,
     paged_attn_decode_rows_f4,
     paged_attn_prefill_f4,
     paged_attn_prefill_f4_fp8,
@@ -50,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "paged_attn_decode_f4_workspace_size",
     "paged_attn_decode_f4",
     "paged_attn_decode_f4_noalloc",
+    "paged_attn_decode_step_f4",
     "paged_attn_decode_rows_f4_workspace_size",
     "paged_attn_decode_rows_f4",
     "lse_merge",

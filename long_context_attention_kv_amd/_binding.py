@@ -50,6 +50,8 @@ _SIGS = {
                                        _P, _P, _P, _P, C.c_size_t, _P]),
     "paged_attn_decode_f4_noalloc": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, C.c_float,
                                                _P, _P, _P, _P]),
+    "paged_attn_decode_step_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                            _I, _I, C.c_float, _P, _P, _P, _P, C.c_size_t, _P]),
     "paged_attn_decode_rows_f4_workspace_size": (C.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "paged_attn_decode_rows_f4": (C.c_int, [C.POINTER(_CacheC), _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, C.c_float,
                                             _P, _P, _P, _P, C.c_size_t, _P]),
@@ -261,6 +263,49 @@ def paged_attn_decode_f4(cache: F4Cache, q, page_table, context_lens, max_contex
                                     page_table.shape[1], int(max_context_len), W, int(window_tokens),
                                     float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _ptr(workspace), ws_bytes,
                                     _stream()))
+    return out, out_m, out_l
+
+
+def paged_attn_decode_step_f4(cache: F4Cache, cos_rows, sin_rows, q, k_new, v_new, slots, page_table, context_lens,
+                              max_context_len: int, sm_scale: float, num_windows: int = 1, window_tokens: int = 0,
+                              rotary_dim=None, out=None, out_m=None, out_l=None, workspace=None):
+    """One decode step: rotate q [B, Hq, D] (bf16) and k_new [B, Hkv, D] (fp32) with
+    table rows [B, rotary_dim/2], write k and v_new at slots [B], then decode;
+    returns (out [W, B, Hq, D], m [W, B, Hq], l [W, B, Hq])."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(q, torch.bfloat16, (B, Hq, D), "q")
+    kv_shape = (B, cache.num_kv_heads, cache.head_dim)
+    _need(k_new, torch.float32, kv_shape, "k_new")
+    _need(v_new, torch.float32, kv_shape, "v_new")
+    _need(slots, torch.int32, (B,), "slots")
+    rd = rotary_dim if rotary_dim is not None else 2 * cos_rows.shape[-1]
+    _need(cos_rows, torch.float32, (B, rd // 2), "cos_rows")
+    _need(sin_rows, torch.float32, (B, rd // 2), "sin_rows")
+    _need(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    _need(context_lens, torch.int32, (B,), "context_lens")
+    W = num_windows
+    dev = q.device
+    if out is None:
+        out = torch.empty((W, B, Hq, D), dtype=torch.float32, device=dev)
+    if out_m is None:
+        out_m = torch.empty((W, B, Hq), dtype=torch.float32, device=dev)
+    if out_l is None:
+        out_l = torch.empty((W, B, Hq), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, (W, B, Hq, D), "out")
+    ws_need = decode_workspace_size(B, Hq, cache.num_kv_heads, cache.head_dim, max_context_len, W, window_tokens)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    c = cache._c()
+    _check("paged_attn_decode_step_f4",
+           lib.paged_attn_decode_step_f4(C.byref(c), _ptr(cos_rows), _ptr(sin_rows), int(rd), _ptr(q), _ptr(k_new),
+                                         _ptr(v_new), _ptr(slots), _ptr(page_table), _ptr(context_lens), B, Hq,
+                                         page_table.shape[1], int(max_context_len), W, int(window_tokens),
+                                         float(sm_scale), _ptr(out), _ptr(out_m), _ptr(out_l), _ptr(workspace),
+                                         ws_bytes, _stream()))
     return out, out_m, out_l
 
 

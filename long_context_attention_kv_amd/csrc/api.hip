@@ -175,7 +175,7 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
                   const int32_t* context_lens, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
                   int32_t max_context_len, int32_t num_windows, int32_t window_tokens, float sm_scale, float* out,
                   float* out_m, float* out_l, void* workspace, size_t ws_bytes, hipStream_t stream,
-                  bool fixed_scratch = false) {
+                  bool fixed_scratch = false, const f4kv::DecodeStep* step = nullptr) {
   if (int r = check_cache(cache, fn)) return r;
   const int32_t Hkv = cache->num_kv_heads;
   if (B < 0 || Hq <= 0 || max_pages <= 0 || max_context_len < 0)
@@ -203,11 +203,15 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4) ||
       (out_m && !aligned(out_m, 4)) || (out_l && !aligned(out_l, 4)))
     return fail(F4KV_ERR_INVALID, "%s: q and out must be 16-byte aligned", fn);
-  if (f4kv::checks_on()) {
+  // device-side checks, once every host-side check has passed
+  auto device_checks = [&]() -> hipError_t {
+    if (!f4kv::checks_on()) return hipSuccess;
     hipError_t e = f4kv::check_pages(context_lens, 0, page_table, B, max_pages, max_context_len, cache->num_pages,
                                      stream);
-    if (e != hipSuccess) return launched(e, fn);
-  }
+    if (e == hipSuccess && step)
+      e = f4kv::check_slots(step->slots, B, static_cast<int64_t>(cache->num_pages) * f4kv::kPage, stream);
+    return e;
+  };
   if (const int32_t sp = f4kv::rows_prefill_splits(B, R, Hq, Hkv, max_context_len, num_windows, window_tokens)) {
     const size_t need = f4kv::rows_prefill_ws_bytes(B, R, Hq, sp);
     if (need > 0) {
@@ -216,6 +220,7 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
                     workspace ? ws_bytes : size_t(0));
       if (!aligned(workspace, 16)) return fail(F4KV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
     }
+    if (hipError_t e = device_checks()) return launched(e, fn);
     return launched(f4kv::launch_prefill_rows(*cache, q, page_table, context_lens, B, R, Hq, max_pages,
                                               max_context_len, sm_scale, out, out_m, out_l, workspace, sp, stream),
                     fn);
@@ -238,9 +243,10 @@ int decode_common(const char* fn, const f4kv_cache* cache, const uint16_t* q, co
                   workspace ? ws_bytes : size_t(0));
     if (!aligned(workspace, 16)) return fail(F4KV_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
   }
+  if (hipError_t e = device_checks()) return launched(e, fn);
   return launched(f4kv::launch_decode(*cache, q, page_table, context_lens, B, R, Hq, max_pages, max_context_len,
                                       num_windows, window_tokens, sm_scale, out, out_m, out_l, workspace, plan,
-                                      stream),
+                                      step, stream),
                   fn);
 }
 
@@ -265,6 +271,27 @@ int paged_attn_decode_f4_noalloc(const f4kv_cache* cache, const uint16_t* q, con
   return decode_common("paged_attn_decode_f4_noalloc", cache, q, page_table, context_lens, B, 1, Hq, max_pages,
                        max_context_len, num_windows, window_tokens, sm_scale, out, out_m, out_l, nullptr, 0, stream,
                        true);
+}
+
+int paged_attn_decode_step_f4(const f4kv_cache* cache, const float* cos_rows, const float* sin_rows,
+                              int32_t rotary_dim, const uint16_t* q, const float* k_new, const float* v_new,
+                              const int32_t* slots, const int32_t* page_table, const int32_t* context_lens,
+                              int32_t B, int32_t Hq, int32_t max_pages, int32_t max_context_len, int32_t num_windows,
+                              int32_t window_tokens, float sm_scale, float* out, float* out_m, float* out_l,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "paged_attn_decode_step_f4";
+  if (int r = check_cache(cache, fn)) return r;
+  if (rotary_dim <= 0 || rotary_dim % 2 != 0 || rotary_dim > cache->head_dim)
+    return fail(F4KV_ERR_INVALID, "%s: rotary_dim must be even and in (0, head_dim]", fn);
+  if (B > 0) {
+    if (!cos_rows || !sin_rows || !k_new || !v_new || !slots) return fail(F4KV_ERR_INVALID, "%s: NULL array", fn);
+    if (!aligned(cos_rows, 4) || !aligned(sin_rows, 4) || !aligned(slots, 4) || !aligned(k_new, 16) ||
+        !aligned(v_new, 16))
+      return fail(F4KV_ERR_INVALID, "%s: k_new, v_new must be 16-byte aligned, the tables and slots 4-byte", fn);
+  }
+  const f4kv::DecodeStep step{cos_rows, sin_rows, rotary_dim, k_new, v_new, slots};
+  return decode_common(fn, cache, q, page_table, context_lens, B, 1, Hq, max_pages, max_context_len, num_windows,
+                       window_tokens, sm_scale, out, out_m, out_l, workspace, ws_bytes, stream, false, &step);
 }
 
 int paged_attn_decode_rows_f4(const f4kv_cache* cache, const uint16_t* q, const int32_t* page_table,

@@ -25,14 +25,15 @@
 //    the accumulator's start value (-8 * 2^-24 * sum of the block's query
 //    values), and the block scale is applied once per block.
 //  * values: lane = 4 consecutive channels.  The V tile stores 8 tokens x 4
-//    channels per 16-byte unit, two tokens per dword, so the same AND trick
-//    yields fp16 pairs over two tokens and a dot product accumulates
-//    p_t s_t (n_t - 8) over token pairs.  The weights w = p_t * s_t (softmax
-//    weight times the token's block scale) travel from the key phase to the
-//    value phase through LDS in fp32 and enter the products through the
-//    mixed-precision FMA (fp32 weight times fp16 nibble operand): an fp16
-//    weight (11 bits) would leave ~2e-3 of the output RMS on channels whose
-//    values are many times the others' (outlier channels).  The "- 8" is
+//    channels per 16-byte unit, two tokens per dword, so the same AND masks
+//    yield 16-bit integer pairs (n, or 16 n) over two tokens.  The weights
+//    w = p_t * s_t (softmax weight times the token's block scale) travel from
+//    the key phase to the value phase through LDS in fp32 and are turned into
+//    16-bit fixed point per (page, head, block), in units of the block's
+//    largest weight / 65535; one v_dot2_u32_u16 then accumulates two tokens'
+//    u_t n_t exactly in a 32-bit integer, flushed into fp32 once per page.
+//    (An fp16 weight, 11 bits, would leave ~2e-3 of the output RMS on
+//    channels whose values are many times the others'.)  The "- 8" is
 //    corrected once, at the end, with the summed weights of the lane's block.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
@@ -40,7 +41,7 @@
 #include <atomic>
 #include <mutex>
 
-#include "f4kv_internal.h"
+#include "f4kv_device.h"
 
 namespace f4kv {
 namespace {
@@ -52,6 +53,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the running max by
 constexpr float kInvU16 = 1.0f / 65535.0f;
+constexpr int kNumBlocks = kHeadDim / kBlock;  // scale blocks per head row
 
 // Query operands of one (sequence, KV head), prepared once per call and read by
 // the decode kernel with scalar loads (the same for every lane).
@@ -60,6 +62,23 @@ struct __align__(64) QPrep {
   uint32_t pair[G][8][4][4];  // fp16 pairs [head][block][dword][pair], scaled by 2^e_h
   float qinit[G][8];          // -8 * 2^-24 * sum of the block's scaled query values
   float kscale[G];            // 2^(24 - e_h) * sm_scale * log2(e)
+};
+
+// The new token of each sequence for a decode step (paged_attn_decode_step_f4):
+// cos / sin rows [B][rd/2] at its position, q not yet rotated, k_new / v_new
+// fp32 [B][Hkv][D] (k not yet rotated), slots [B].  cos == null: no step.
+struct StepArgs {
+  const float* cos;
+  const float* sin;
+  int32_t rd;
+  const float* k_new;
+  const float* v_new;
+  const int32_t* slots;
+  uint8_t* k_nib;
+  uint16_t* k_scale;
+  uint8_t* v_nib;
+  uint16_t* v_scale;
+  int32_t num_pages, v_per_token;
 };
 
 struct DecodeArgs {
@@ -296,6 +315,53 @@ __device__ void build_work_list_wave(const PlanArgs& p) {
   if (lane == 0) *p.n_items = items;
 }
 
+// The new token of sequence b, KV head g: K rotated in fp64 and rounded to
+// fp32 (yarn_rope_apply on fp32 rows), then K and V quantised and stored at
+// slot slots[b] (kv_cache_write_f4: -1 or a slot outside the pool writes
+// nothing).  Threads 0-7 take the K blocks, 8-15 the V blocks; the rotated K
+// row goes through LDS.
+__device__ void step_write_token(const StepArgs& st, int b, int g, int Hkv) {
+  __shared__ float kr[kHeadDim];
+  const int tid = threadIdx.x;
+  const float* krow = st.k_new + (static_cast<int64_t>(b) * Hkv + g) * kHeadDim;
+  const int half = st.rd / 2;
+  for (int e = tid; e < half + (kHeadDim - st.rd); e += kThreads) {
+    if (e < half) {
+      const double c = st.cos[static_cast<int64_t>(b) * half + e], sn = st.sin[static_cast<int64_t>(b) * half + e];
+      double y0, y1;
+      rope_rotate_pair(krow[e], krow[e + half], c, sn, y0, y1);
+      kr[e] = static_cast<float>(y0);
+      kr[e + half] = static_cast<float>(y1);
+    } else {
+      const int d = st.rd + (e - half);
+      kr[d] = krow[d];
+    }
+  }
+  __syncthreads();
+  const int32_t slot = st.slots[b];
+  if (tid >= 2 * kNumBlocks || slot < 0 || slot >= static_cast<int64_t>(st.num_pages) * kPage) return;
+  const int kind = tid / kNumBlocks, c = tid % kNumBlocks;
+  const float* vrow = st.v_new + (static_cast<int64_t>(b) * Hkv + g) * kHeadDim;
+  float x[kBlock];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    x[i] = kind ? vrow[c * kBlock + i] : kr[c * kBlock + i];
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  if (kind == 1 && st.v_per_token) {
+    amax = 0.0f;
+    for (int i = 0; i < kHeadDim; ++i) amax = fmaxf(amax, fabsf(vrow[i]));
+  }
+  uint32_t nib[kBlock];
+  const uint16_t sbits = f4_quantize_block(x, amax, nib);
+  const int64_t ph = static_cast<int64_t>(slot / kPage) * Hkv + g;
+  if (kind == 0)
+    f4_store_k_block(st.k_nib, st.k_scale, ph, kNumBlocks, c, slot % kPage, nib, sbits);
+  else
+    f4_store_v_block(st.v_nib, st.v_scale, ph, kHeadDim, c, slot % kPage, nib, sbits, st.v_per_token != 0);
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                 false);
@@ -354,6 +420,27 @@ __device__ __forceinline__ float max8_nonneg(float4_t x, float4_t y) {
   return __uint_as_float(m);
 }
 
+// Floats as int32 keys of the same order (negative values have their
+// magnitude bits flipped), so that maxima run on integer DPP max without the
+// float max's operand canonicalisation.
+__device__ __forceinline__ int32_t order_key(float x) {
+  const int32_t b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+
+__device__ __forceinline__ float key_value(int32_t k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+// Largest key of the wave (uniform).
+__device__ __forceinline__ int32_t wave_max_key(int32_t k) {
+  k = max(k, static_cast<int32_t>(dpp_u<kDppQuadXor1>(static_cast<uint32_t>(k))));
+  k = max(k, static_cast<int32_t>(dpp_u<kDppQuadXor2>(static_cast<uint32_t>(k))));
+  k = max(k, static_cast<int32_t>(dpp_u<kDppHalfMirror>(static_cast<uint32_t>(k))));
+  k = max(k, static_cast<int32_t>(dpp_u<kDppMirror>(static_cast<uint32_t>(k))));
+  const int32_t r0 = __builtin_amdgcn_readlane(k, 0), r1 = __builtin_amdgcn_readlane(k, 16);
+  const int32_t r2 = __builtin_amdgcn_readlane(k, 32), r3 = __builtin_amdgcn_readlane(k, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 // Two values in [0, 1] to unsigned 16-bit fixed point, nearest (v_cvt_pknorm_u16_f32):
@@ -410,12 +497,18 @@ __device__ __forceinline__ void lds_wave_sync() {
 
 // One workgroup per (sequence, KV head): query rows -> QPrep.
 // Workgroups 0 .. B*Hkv-1 prepare the query operands of one (sequence, KV
-// head) each; the last workgroup builds the work list.
+// head) each; the last workgroup builds the work list.  With step arguments
+// (a decode step that also takes the new token of each sequence; R == 1) the
+// workgroup of (b, g) first rotates the query rows (as yarn_rope_apply on bf16
+// rows, through the shared rotation) and rotates and writes the new token's K
+// and V of KV head g (as yarn_rope_apply on fp32 rows, then kv_cache_write_f4,
+// through the shared quantiser), so the step's results equal those of the
+// separate entry points bit for bit.
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* __restrict__ q,
                                                                QPrep<G>* __restrict__ out, int32_t Hq,
                                                                int32_t Hkv, float qk_scale, PlanArgs plan,
-                                                               int32_t R, int32_t r0, int32_t Gq) {
+                                                               int32_t R, int32_t r0, int32_t Gq, StepArgs st) {
   if (blockIdx.x == gridDim.x - 1) {
     if (plan.W * plan.B <= 64) {
       if (threadIdx.x < 64) build_work_list_wave(plan);
@@ -430,11 +523,34 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   QPrep<G>& P = out[blockIdx.x];
   // row h of the group: query row r0 + h / Gq (clamped: rows past R are computed, never written), head g Gq + h % Gq
-  for (int i = tid; i < G * kHeadDim; i += kThreads) {
-    const int h = i / kHeadDim, r = min(r0 + h / Gq, R - 1);
-    const int64_t row = (static_cast<int64_t>(b) * R + r) * Hq + g * Gq + h % Gq;
-    qf[h][i % kHeadDim] = bf16_to_f32(q[row * kHeadDim + i % kHeadDim]);
+  if (st.cos) {
+    // rotation pairs (e, e + rd / 2) of each row, rounded to bf16 as the rotated
+    // query would be stored; channels from rd on pass through
+    const int half = st.rd / 2;
+    const int per_row = half + (kHeadDim - st.rd);
+    for (int i = tid; i < G * per_row; i += kThreads) {
+      const int h = i / per_row, e = i % per_row;
+      const int r = min(r0 + h / Gq, R - 1);
+      const uint16_t* qrow = q + ((static_cast<int64_t>(b) * R + r) * Hq + g * Gq + h % Gq) * kHeadDim;
+      if (e < half) {
+        const double c = st.cos[static_cast<int64_t>(b) * half + e], sn = st.sin[static_cast<int64_t>(b) * half + e];
+        double y0, y1;
+        rope_rotate_pair(bf16_to_f32(qrow[e]), bf16_to_f32(qrow[e + half]), c, sn, y0, y1);
+        qf[h][e] = bf16_to_f32(f32_to_bf16(static_cast<float>(y0)));
+        qf[h][e + half] = bf16_to_f32(f32_to_bf16(static_cast<float>(y1)));
+      } else {
+        const int d = st.rd + (e - half);
+        qf[h][d] = bf16_to_f32(qrow[d]);
+      }
+    }
+  } else {
+    for (int i = tid; i < G * kHeadDim; i += kThreads) {
+      const int h = i / kHeadDim, r = min(r0 + h / Gq, R - 1);
+      const int64_t row = (static_cast<int64_t>(b) * R + r) * Hq + g * Gq + h % Gq;
+      qf[h][i % kHeadDim] = bf16_to_f32(q[row * kHeadDim + i % kHeadDim]);
+    }
   }
+  if (st.k_new) step_write_token(st, b, g, Hkv);
   __syncthreads();
   for (int h = wave; h < G; h += kWaves) {
     float mx = 0.0f;
@@ -670,11 +786,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int c = 0; c < 8; ++c) vq[c] = load16(rv, lane16, c * 1024);
 
     // Online softmax in log2 units with a lazily raised running max: m_run
-    // moves (and the state is rescaled) only when some logit of the page
+    // moves (and the state is rescaled) only when the page's largest logit
     // exceeds it by more than kSlack, so weights stay below 2^kSlack and
-    // most pages skip the wave-wide max and the rescale.  The exact maximum is
-    // tracked per lane and restored at the end.
-    float p[G], s[G];
+    // most pages skip the rescale.  The exact maximum is tracked per lane and
+    // restored at the end.  The page's largest logit per head also names its
+    // top token (the lowest lane among ties), whose weights bypass the 16-bit
+    // fixed point below.
+    float p[G], s[G], pm[G];
+    int ttop[G];
     bool raise = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -682,12 +801,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       // phase into a branch on the token's validity
       s[h] = fmaf(logit[h], qp->kscale[h], tok < lim[h] ? tmask : -INFINITY);
       s_max[h] = fmaxf(s_max[h], s[h]);
-      raise |= s[h] > m_run[h] + kSlack;
+      const int32_t key = order_key(s[h]);
+      const int32_t kmax = wave_max_key(key);
+      pm[h] = key_value(kmax);
+      raise |= pm[h] > m_run[h] + kSlack;
+      // all lanes -inf (nothing valid): token 0, whose weights are 0
+      const uint64_t at_max = __builtin_amdgcn_ballot_w64(key == kmax);
+      ttop[h] = at_max ? static_cast<int>(__builtin_ctzll(at_max)) : 0;
     }
+    // the top token's V dword of this lane's channels (tokens 2k, 2k + 1 of
+    // its group): a cached read of cells just requested, used before the
+    // value products
+    uint32_t vtop[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      vtop[h] = __builtin_amdgcn_raw_buffer_load_b32(rv, lane16, (ttop[h] >> 3) * 1024 + ((ttop[h] & 7) >> 1) * 4,
+                                                     0);
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m_run[h], wave_max(s[h]));
+        const float mn = fmaxf(m_run[h], pm[h]);
         // mn == -inf only while no valid token has been seen: nothing to rescale
         const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - mn);
         l_lane[h] *= alpha;
@@ -721,14 +854,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     lds_wave_sync();
     const int wrow = VT ? 0 : cj;  // fp32 weight row of this lane's value block
 
+    // The top token of each head leaves the rows: its fp32 weight for this
+    // lane's block is kept and a zero takes its place (every lane of a block
+    // reads, then writes, the same element; LDS keeps one wave's order).
+    float wtop[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) wtop[h] = sm.u.w[wave][h][wrow][ttop[h]];
+    lds_wave_sync();
+#pragma unroll
+    for (int h = 0; h < G; ++h) sm.u.w[wave][h][wrow][ttop[h]] = 0.0f;
+    lds_wave_sync();
+
     // Weights to 16-bit fixed point.  The 8 lanes of block cj share the row of
     // the block's 64 weights per head; lane sub converts tokens 8 sub .. 8 sub
-    // + 7.  The row's largest weight w_max = f 2^e (f in [1/2, 1)) sets the
-    // unit 2^e / 65535, so u = nearest(w 2^-e 65535) keeps 16 bits for the
-    // page's dominant tokens and an absolute error of at most 2^(e-17) for the
-    // rest; the sums of u n over the page are exact in 32-bit integers.  The
-    // 16-bit rows overwrite the first half of the fp32 rows once every lane of
-    // the wave has read its part (LDS serves one wave's instructions in order).
+    // + 7.  The row's largest weight w_max sets the unit w_max / 65535, so
+    // u = nearest(w 65535 / w_max) keeps 16 bits for the largest weight and an
+    // absolute error of at most w_max / 131070 for every weight; the sums of
+    // u n over the page are exact in 32-bit integers.  With the page's top
+    // token taken out, w_max is the second largest weight of the row: a
+    // dominant token no longer coarsens the unit of all the others (that
+    // error, summed over the page's tokens and multiplied by outlier values,
+    // would approach 2e-3 of the output RMS when a few tokens hold most of the
+    // attention).  The 16-bit rows overwrite the first half of the fp32 rows
+    // once every lane of the wave has read its part.
     float4_t wx[G], wy[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -741,21 +889,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int h = 0; h < G; ++h) {
       const float4_t x = wx[h], y = wy[h];
       const float mx = max8_nonneg(x, y);
-      const int e = __builtin_amdgcn_frexp_expf(mx);  // 0 when the row is all zero
+      // 1 / w_max (a zero row scales by 1e30 and stays zero); x r <= 1 up to
+      // the reciprocal's rounding, and pknorm clamps to [0, 1]
+      const float r = __builtin_amdgcn_rcpf(fmaxf(mx, 1e-30f));
       uint4 u;
-      u.x = pknorm_u16(__builtin_amdgcn_ldexpf(x.x, -e), __builtin_amdgcn_ldexpf(x.y, -e));
-      u.y = pknorm_u16(__builtin_amdgcn_ldexpf(x.z, -e), __builtin_amdgcn_ldexpf(x.w, -e));
-      u.z = pknorm_u16(__builtin_amdgcn_ldexpf(y.x, -e), __builtin_amdgcn_ldexpf(y.y, -e));
-      u.w = pknorm_u16(__builtin_amdgcn_ldexpf(y.z, -e), __builtin_amdgcn_ldexpf(y.w, -e));
+      u.x = pknorm_u16(x.x * r, x.y * r);
+      u.y = pknorm_u16(x.z * r, x.w * r);
+      u.z = pknorm_u16(y.x * r, y.y * r);
+      u.w = pknorm_u16(y.z * r, y.w * r);
       *reinterpret_cast<uint4*>(&urow(sm, wave, h, cj)[sub * 8]) = u;
       // "- 8" correction, part 1: this lane's 8 tokens of the block's
       // (rounded) weights; the sum over the lanes waits for the epilogue
       const uint32_t usum = udot2(u.x, 0x00010001u, udot2(u.y, 0x00010001u,
                                   udot2(u.z, 0x00010001u, udot2(u.w, 0x00010001u, 0u))));
-      wpart[h] = fmaf(static_cast<float>(usum), __builtin_amdgcn_ldexpf(kInvU16, e), wpart[h]);
-      funit[h] = __builtin_amdgcn_ldexpf(kInvU16, e - 24);
+      wpart[h] = fmaf(static_cast<float>(usum), mx * kInvU16, wpart[h]);
+      funit[h] = mx * (kInvU16 * 0x1p-24f);
     }
     lds_wave_sync();
+
+    // The top tokens in fp32: weight x (n - 8) for this lane's 4 channels,
+    // in the units of the value products (n 2^-24, x16 for channels 1 and 3:
+    // the masked nibbles are exactly those fp16 subnormals); the "- 8" goes
+    // with the block's summed weights, counted once per block (lane sub 0).
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint32_t hw = vtop[h] >> ((ttop[h] & 1) * 16);
+      const uint32_t h8 = hw >> 8;
+      o[h][0] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, hw & 0x000Fu).x), o[h][0]);
+      o[h][1] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, hw & 0x00F0u).x), o[h][1]);
+      o[h][2] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, h8 & 0x000Fu).x), o[h][2]);
+      o[h][3] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, h8 & 0x00F0u).x), o[h][3]);
+      wpart[h] = fmaf(wtop[h], sub == 0 ? 1.0f : 0.0f, wpart[h]);
+    }
 
     // values: lane = channels 4*lane .. 4*lane+3 (block cj); per token pair
     // one 16-bit dot product (two tokens' weights x their nibbles, 32-bit
@@ -922,10 +1087,10 @@ __global__ __launch_bounds__(64 * kFoldWaves) void decode_fold_kernel(const floa
 
 template <int G, bool VT>
 hipError_t launch_decode_g(const DecodeArgs& a, void* qprep, const PlanArgs& plan, int max_items,
-                           hipStream_t s) {
+                           const StepArgs& st, hipStream_t s) {
   QPrep<G>* qp = static_cast<QPrep<G>*>(qprep);
   hipLaunchKernelGGL(decode_qprep_kernel<G>, dim3(a.B * a.Hkv + 1), dim3(kThreads), 0, s, a.q, qp, a.Hq, a.Hkv,
-                     a.qk_scale, plan, a.R, a.r0, a.Gq);
+                     a.qk_scale, plan, a.R, a.r0, a.Gq, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_begin(F4KV_KERNEL_DECODE, s);
@@ -1044,8 +1209,23 @@ DecodePlan plan_decode(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t ma
 hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* pt, const int32_t* ctx,
                          int32_t B, int32_t R, int32_t Hq, int32_t max_pages, int32_t max_ctx, int32_t num_windows,
                          int32_t window_tokens, float sm_scale, float* out, float* out_m, float* out_l,
-                         void* ws, const DecodePlan& plan, hipStream_t s) {
+                         void* ws, const DecodePlan& plan, const DecodeStep* step, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  StepArgs st{};
+  if (step) {
+    st.cos = step->cos;
+    st.sin = step->sin;
+    st.rd = step->rotary_dim;
+    st.k_new = step->k_new;
+    st.v_new = step->v_new;
+    st.slots = step->slots;
+    st.k_nib = c.k_nib;
+    st.k_scale = c.k_scale;
+    st.v_nib = c.v_nib;
+    st.v_scale = c.v_scale;
+    st.num_pages = c.num_pages;
+    st.v_per_token = c.v_scale_per_token;
+  }
   char* base = static_cast<char*>(ws);
   const int64_t wb = static_cast<int64_t>(num_windows) * B;
   DecodeArgs a;
@@ -1104,14 +1284,14 @@ hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* 
     a.r0 = r0;
     hipError_t e;
     switch (G) {
-      case 1: e = vt ? launch_decode_g<1, true>(a, qprep, pa, plan.max_items, s)
-                     : launch_decode_g<1, false>(a, qprep, pa, plan.max_items, s); break;
-      case 2: e = vt ? launch_decode_g<2, true>(a, qprep, pa, plan.max_items, s)
-                     : launch_decode_g<2, false>(a, qprep, pa, plan.max_items, s); break;
-      case 4: e = vt ? launch_decode_g<4, true>(a, qprep, pa, plan.max_items, s)
-                     : launch_decode_g<4, false>(a, qprep, pa, plan.max_items, s); break;
-      default: e = vt ? launch_decode_g<8, true>(a, qprep, pa, plan.max_items, s)
-                      : launch_decode_g<8, false>(a, qprep, pa, plan.max_items, s); break;
+      case 1: e = vt ? launch_decode_g<1, true>(a, qprep, pa, plan.max_items, st, s)
+                     : launch_decode_g<1, false>(a, qprep, pa, plan.max_items, st, s); break;
+      case 2: e = vt ? launch_decode_g<2, true>(a, qprep, pa, plan.max_items, st, s)
+                     : launch_decode_g<2, false>(a, qprep, pa, plan.max_items, st, s); break;
+      case 4: e = vt ? launch_decode_g<4, true>(a, qprep, pa, plan.max_items, st, s)
+                     : launch_decode_g<4, false>(a, qprep, pa, plan.max_items, st, s); break;
+      default: e = vt ? launch_decode_g<8, true>(a, qprep, pa, plan.max_items, st, s)
+                      : launch_decode_g<8, false>(a, qprep, pa, plan.max_items, st, s); break;
     }
     if (e != hipSuccess) return e;
     const int rows = std::min(Rp, R - r0);

@@ -95,11 +95,24 @@ DecodePlan plan_decode(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t ma
 size_t decode_scratch_bytes();
 hipError_t decode_scratch(void** ptr);
 
+// The new token of each sequence, for a decode step that rotates the queries
+// and rotates and writes the token's K and V before attending (R == 1):
+// cos / sin [B][rotary_dim / 2], k_new / v_new fp32 [B][Hkv][D], slots [B].
+struct DecodeStep {
+  const float* cos;
+  const float* sin;
+  int32_t rotary_dim;
+  const float* k_new;
+  const float* v_new;
+  const int32_t* slots;
+};
+
+// step: null for a plain decode (q already rotated).
 hipError_t launch_decode(const f4kv_cache& c, const uint16_t* q, const int32_t* pt,
                          const int32_t* ctx, int32_t B, int32_t R, int32_t Hq, int32_t max_pages,
                          int32_t max_ctx, int32_t num_windows, int32_t window_tokens,
                          float sm_scale, float* out, float* out_m, float* out_l,
-                         void* ws, const DecodePlan& plan, hipStream_t s);
+                         void* ws, const DecodePlan& plan, const DecodeStep* step, hipStream_t s);
 
 // Query rows of B sequences (row r at position ctx[b] - R + r) through the
 // prefill kernel: 4 query heads per KV head, head_dim 256, R <= 8.

@@ -17,7 +17,7 @@
 // token's whole V row (the 8 threads of a row read it each; the
 // writer is not on the decode clock), quantises its own block against that
 // scale, and the thread of block 0 writes the scale.
-#include "f4kv_internal.h"
+#include "f4kv_device.h"
 
 namespace f4kv {
 namespace {
@@ -86,55 +86,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(x[i]));
   }
 
-  // absmax * 0.125 is exact in fp32; a single rounding to fp16 follows.
-  const _Float16 s16 = static_cast<_Float16>(fminf(amax * 0.125f, 65504.0f));
-  const double sd = static_cast<double>(static_cast<float>(s16));
-
   uint32_t nib[kBlock];
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) {
-    int code = 0;
-    if (sd > 0.0) {
-      double qd = __builtin_rint(static_cast<double>(x[i]) / sd);
-      qd = fmin(fmax(qd, -8.0), 7.0);
-      code = static_cast<int>(qd);
-    }
-    nib[i] = static_cast<uint32_t>(code + 8);
-  }
-
+  const uint16_t sbits = f4_quantize_block(x, amax, nib);
   const int64_t ph = static_cast<int64_t>(page) * a.H + h;
-  const uint16_t sbits = __builtin_bit_cast(uint16_t, s16);
-  if (kind == 0) {
-    uint32_t w[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v |= nib[8 * d + e] << (4 * e);
-      w[d] = v;
-    }
-    uint8_t* dst = a.k_nib + ((ph * nb + c) * kPage + off) * 16;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    a.k_scale[(ph * kPage + off) * nb + c] = sbits;
-  } else {
-    const int quads = a.D / 4;
-    uint8_t* tile = a.v_nib + ph * (static_cast<int64_t>(kPage) * a.D / 2);
-    const int unit_c = off / 8;
-    const int byte_in_unit = 4 * ((off % 8) / 2) + 2 * (off % 2);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = c * 8 + q;  // dim quad 4j .. 4j+3
-      const uint32_t b0 = nib[4 * q + 0] | (nib[4 * q + 1] << 4);
-      const uint32_t b1 = nib[4 * q + 2] | (nib[4 * q + 3] << 4);
-      uint16_t* dst = reinterpret_cast<uint16_t*>(
-          tile + (static_cast<int64_t>(unit_c) * quads + j) * 16 + byte_in_unit);
-      *dst = static_cast<uint16_t>(b0 | (b1 << 8));
-    }
-    if (!a.v_per_token)
-      a.v_scale[(ph * kPage + off) * nb + c] = sbits;
-    else if (c == 0)
-      a.v_scale[ph * kPage + off] = sbits;
-  }
+  if (kind == 0)
+    f4_store_k_block(a.k_nib, a.k_scale, ph, nb, c, off, nib, sbits);
+  else
+    f4_store_v_block(a.v_nib, a.v_scale, ph, a.D, c, off, nib, sbits, a.v_per_token != 0);
 }
 
 }  // namespace

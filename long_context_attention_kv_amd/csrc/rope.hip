@@ -9,7 +9,7 @@
 // over the original context.  Positions reach 2^24, so p * theta' and the
 // trigonometry are evaluated in fp64 (an fp32 angle is off by ~1e-2 radians at
 // a million positions).
-#include "f4kv_internal.h"
+#include "f4kv_device.h"
 
 namespace f4kv {
 namespace {
@@ -79,8 +79,10 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeApplyArgs a) {
     const double s = a.s[t * half + e];
     const double x0 = load_elem(a.x, a.xdt, row + e);
     const double x1 = load_elem(a.x, a.xdt, row + e + half);
-    store_elem(a.y, a.ydt, row + e, x0 * c - x1 * s);
-    store_elem(a.y, a.ydt, row + e + half, x1 * c + x0 * s);
+    double y0, y1;
+    rope_rotate_pair(x0, x1, c, s, y0, y1);
+    store_elem(a.y, a.ydt, row + e, y0);
+    store_elem(a.y, a.ydt, row + e + half, y1);
   } else {
     const int d = a.rd + (e - half);
     store_elem(a.y, a.ydt, row + d, load_elem(a.x, a.xdt, row + d));

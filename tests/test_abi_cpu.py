@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     assert set(names) == set(f4.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +140,26 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=16, ws_bytes=need - 1) == 3
     assert "workspace" in _err(lib)
     assert _decode(lib, c, max_pages=16384, max_ctx=1 << 20, W=16, wt=65536, ws=None, ws_bytes=need) == 3
+
+
+def _step(lib, c, B_=1, rd=256, tables=16, kv=16, slots=16, **kw):
+    return lib.paged_attn_decode_step_f4(C.byref(c), tables, tables, rd, 16, kv, kv, slots, 16, 16, B_, 16, 64, 4096,
+                                         1, 0, 0.0625, 16, None, None, kw.get("ws"), kw.get("ws_bytes", 0), None)
+
+
+def test_decode_step_argument_checks(lib):
+    """The one-call decode step refuses bad rotation and new-token arguments on
+    the host, besides the decode's own checks; nothing is launched."""
+    c = _cache()
+    assert _step(lib, c, rd=0) == 1 and "rotary_dim" in _err(lib)
+    assert _step(lib, c, rd=255) == 1 and "rotary_dim" in _err(lib)
+    assert _step(lib, c, rd=258) == 1 and "rotary_dim" in _err(lib)
+    assert _step(lib, c, tables=None) == 1 and "NULL" in _err(lib)
+    assert _step(lib, c, slots=None) == 1 and "NULL" in _err(lib)
+    assert _step(lib, c, kv=8) == 1 and "aligned" in _err(lib)
+    assert _step(lib, c, slots=18) == 1 and "aligned" in _err(lib)
+    assert _step(lib, _cache(dim=128), rd=128) == 2 and "head_dim" in _err(lib)
+    assert _step(lib, c, B_=0, tables=None, kv=None, slots=None) == 0
 
 
 def test_decode_noalloc_refuses_beyond_its_scratch(lib):

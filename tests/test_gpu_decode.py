@@ -128,6 +128,26 @@ def test_dominant_tokens(sinks, mag):
     assert_states_close(m, l, rm, rl, f"sinks {sinks}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_concentrated_attention_over_outlier_values(seed):
+    """Short contexts (a few pages), outlier channels in K and V and queries
+    x1.5: a handful of tokens hold most of the weight and the outputs of the
+    outlier channels are many times the output RMS, the case that shows the
+    rounding of the value weights most (in the tolerance's units)."""
+    r = np.random.default_rng(4000 + seed)
+    lengths = [int(x) for x in r.integers(8, 700, 3)]
+    print(f"decode, concentrated attention: lengths {lengths}", flush=True)
+    ps = PagedSet(lengths, Hkv=4, seed=400 + seed, outliers=True)
+    bits, qv = random_q(3, 16, 256, seed=400 + seed, scale=1.5)
+    out, m, l = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), ps.gpu_lengths(),
+                                        max(lengths), SM)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle_decode(ps, qv, SM)
+    rel = assert_attention_close(out.cpu().numpy(), ro, f"concentrated attention, lengths {lengths}")
+    print(f"decode, concentrated attention: max |delta| / RMS = {rel:.2e}", flush=True)
+    assert_states_close(m.cpu().numpy(), l.cpu().numpy(), rm, rl, "concentrated attention")
+
+
 def test_outliers_and_scaled_values():
     ps = PagedSet([2000], Hkv=4, seed=10, outliers=True, v_scale=100.0)
     (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=10)
