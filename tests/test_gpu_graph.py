@@ -1,4 +1,5 @@
-"""The decode step captured in a HIP graph: every replay equals the eager result.
+"""The decode step captured in a HIP graph, as separate calls and as the
+one-call step: every replay equals the eager result (of the separate calls).
 
 The library's launches go on the caller's stream and use no memset nodes, so a
 captured step (YaRN rows, query and key rotation, F4 write, decode with its
@@ -16,7 +17,8 @@ pytestmark = pytest.mark.gpu
 SM = 1.0 / 16.0
 
 
-def test_decode_step_graph_replays_match_eager():
+@pytest.mark.parametrize("one_call", [False, True])
+def test_decode_step_graph_replays_match_eager(one_call):
     ps = PagedSet([5000, 777, 3000], Hkv=4, seed=21, extra_pages=8)
     bits, _ = random_q(3, 16, 256, 21)
     q_raw = bf16_tensor(bits)
@@ -34,13 +36,18 @@ def test_decode_step_graph_replays_match_eager():
     om = torch.empty((1, 3, 16), device="cuda")
     ol = torch.empty((1, 3, 16), device="cuda")
 
-    def step():
+    def step(one=False):
         c, s = f4.yarn_rope_table(yp, pos)
+        if one:  # the one-call step: the same results, bit for bit
+            f4.paged_attn_decode_step_f4(ps.gc, c, s, q_raw, k_new, v_new, slots, pt, lens, 5000, SM, out=out,
+                                         out_m=om, out_l=ol, workspace=ws)
+            return
         q = f4.yarn_rope_apply(c, s, q_raw)
         k = f4.yarn_rope_apply(c, s, k_new)
         f4.kv_cache_write_f4(ps.gc, k, v_new, slots)
         f4.paged_attn_decode_f4(ps.gc, q, pt, lens, 5000, SM, out=out, out_m=om, out_l=ol, workspace=ws)
 
+    print(f"graph replays, {'one-call step' if one_call else 'separate calls'}", flush=True)
     step()
     torch.cuda.synchronize()
     ref = [t.clone() for t in (out, om, ol)]
@@ -50,10 +57,10 @@ def test_decode_step_graph_replays_match_eager():
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
-        step()
+        step(one_call)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=side):
-            step()
+            step(one_call)
     torch.cuda.synchronize()
     for rep in range(4):
         for t in (out, om, ol):
