@@ -34,7 +34,7 @@ import sys
 
 
 def _short(name: str) -> str:
-    name = name.replace("f4kv::(anonymous namespace)::", "")
+    name = name.replace("f4kv::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     if "(" in name:
         name = name[:name.index("(")]
     return name.replace("void ", "").strip()

@@ -115,3 +115,10 @@ def test_launch_shapes_split_one_kernel_by_grid(tmp_path):
     assert "| `prefill_kernel<false>` | 64 x 4 x 2 | 2 | 10.0 | 9.0 | 11.0 |" in out
     assert "| `prefill_kernel<false>` | 3 x 4 x 42 | 2 | 2.0 | 1.0 | 3.0 |" in out
     assert "decode_kernel" not in out.split("from the kernel trace:")[1]
+
+
+def test_short_names_drop_namespaces_and_arguments():
+    assert ps._short(DECODE) == "decode_kernel<4, false>"
+    # a kernel in an anonymous namespace outside f4kv (the ceiling kernels beside bench.py)
+    assert ps._short("void (anonymous namespace)::stream_read_kernel<16>(uint4 const*, long, unsigned int*)") == \
+        "stream_read_kernel<16>"
