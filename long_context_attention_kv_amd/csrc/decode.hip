@@ -315,53 +315,6 @@ __device__ void build_work_list_wave(const PlanArgs& p) {
   if (lane == 0) *p.n_items = items;
 }
 
-// The new token of sequence b, KV head g: K rotated in fp64 and rounded to
-// fp32 (yarn_rope_apply on fp32 rows), then K and V quantised and stored at
-// slot slots[b] (kv_cache_write_f4: -1 or a slot outside the pool writes
-// nothing).  Threads 0-7 take the K blocks, 8-15 the V blocks; the rotated K
-// row goes through LDS.
-__device__ void step_write_token(const StepArgs& st, int b, int g, int Hkv) {
-  __shared__ float kr[kHeadDim];
-  const int tid = threadIdx.x;
-  const float* krow = st.k_new + (static_cast<int64_t>(b) * Hkv + g) * kHeadDim;
-  const int half = st.rd / 2;
-  for (int e = tid; e < half + (kHeadDim - st.rd); e += kThreads) {
-    if (e < half) {
-      const double c = st.cos[static_cast<int64_t>(b) * half + e], sn = st.sin[static_cast<int64_t>(b) * half + e];
-      double y0, y1;
-      rope_rotate_pair(krow[e], krow[e + half], c, sn, y0, y1);
-      kr[e] = static_cast<float>(y0);
-      kr[e + half] = static_cast<float>(y1);
-    } else {
-      const int d = st.rd + (e - half);
-      kr[d] = krow[d];
-    }
-  }
-  __syncthreads();
-  const int32_t slot = st.slots[b];
-  if (tid >= 2 * kNumBlocks || slot < 0 || slot >= static_cast<int64_t>(st.num_pages) * kPage) return;
-  const int kind = tid / kNumBlocks, c = tid % kNumBlocks;
-  const float* vrow = st.v_new + (static_cast<int64_t>(b) * Hkv + g) * kHeadDim;
-  float x[kBlock];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) {
-    x[i] = kind ? vrow[c * kBlock + i] : kr[c * kBlock + i];
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  if (kind == 1 && st.v_per_token) {
-    amax = 0.0f;
-    for (int i = 0; i < kHeadDim; ++i) amax = fmaxf(amax, fabsf(vrow[i]));
-  }
-  uint32_t nib[kBlock];
-  const uint16_t sbits = f4_quantize_block(x, amax, nib);
-  const int64_t ph = static_cast<int64_t>(slot / kPage) * Hkv + g;
-  if (kind == 0)
-    f4_store_k_block(st.k_nib, st.k_scale, ph, kNumBlocks, c, slot % kPage, nib, sbits);
-  else
-    f4_store_v_block(st.v_nib, st.v_scale, ph, kHeadDim, c, slot % kPage, nib, sbits, st.v_per_token != 0);
-}
-
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                 false);
@@ -493,6 +446,75 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The new token of sequence b, KV head g: K rotated in fp64 and rounded to
+// fp32 (yarn_rope_apply on fp32 rows), then K and V quantised and stored at
+// slot slots[b] (kv_cache_write_f4: -1 or a slot outside the pool writes
+// nothing).  Thread t = 128 kind + j (kind 0: K, 1: V) quantises channels
+// 2 j and 2 j + 1 into byte j of the row; the 16 lanes of a scale block are
+// one DPP row, which takes the block's absolute maximum (the row's, through
+// LDS, when V has one scale per token); 16 threads then store the blocks.
+__device__ void step_write_token(const StepArgs& st, int b, int g, int Hkv) {
+  __shared__ float kr[kHeadDim];
+  __shared__ uint32_t vrow_max;
+  __shared__ uint8_t nb[2][kHeadDim / 2];
+  __shared__ uint16_t sb[2][kNumBlocks];
+  const int tid = threadIdx.x;
+  const float* krow = st.k_new + (static_cast<int64_t>(b) * Hkv + g) * kHeadDim;
+  const int half = st.rd / 2;
+  for (int e = tid; e < half + (kHeadDim - st.rd); e += kThreads) {
+    if (e < half) {
+      const double c = st.cos[static_cast<int64_t>(b) * half + e], sn = st.sin[static_cast<int64_t>(b) * half + e];
+      double y0, y1;
+      rope_rotate_pair(krow[e], krow[e + half], c, sn, y0, y1);
+      kr[e] = static_cast<float>(y0);
+      kr[e + half] = static_cast<float>(y1);
+    } else {
+      const int d = st.rd + (e - half);
+      kr[d] = krow[d];
+    }
+  }
+  if (tid == 0) vrow_max = 0u;
+  __syncthreads();
+  const int32_t slot = st.slots[b];
+  if (slot < 0 || slot >= static_cast<int64_t>(st.num_pages) * kPage) return;  // the same for every thread
+  static_assert(kThreads == kHeadDim, "one thread per byte of the K and V rows");
+  const int kind = tid >> 7, j = tid & 127, c = j >> 4;
+  const float* vrow = st.v_new + (static_cast<int64_t>(b) * Hkv + g) * kHeadDim;
+  const float x0 = kind ? vrow[2 * j] : kr[2 * j];
+  const float x1 = kind ? vrow[2 * j + 1] : kr[2 * j + 1];
+  // absolute values as integer bits (they order as the floats; a NaN counts
+  // as 0, as the writer's fmaxf ignores it)
+  auto abits = [](float x) { return fabsf(x) == fabsf(x) ? __float_as_uint(fabsf(x)) : 0u; };
+  uint32_t m = max(abits(x0), abits(x1));
+  m = max(m, dpp_u<kDppQuadXor1>(m));
+  m = max(m, dpp_u<kDppQuadXor2>(m));
+  m = max(m, dpp_u<kDppHalfMirror>(m));
+  m = max(m, dpp_u<kDppMirror>(m));  // the 16 lanes of the block
+  const bool row_scale = kind == 1 && st.v_per_token;
+  if (row_scale && (j & 15) == 0) atomicMax(&vrow_max, m);
+  __syncthreads();
+  if (row_scale) m = vrow_max;
+  double sd;
+  const uint16_t sbits = f4_scale(__uint_as_float(m), sd);
+  nb[kind][j] = static_cast<uint8_t>(f4_nibble(x0, sd) | (f4_nibble(x1, sd) << 4));
+  if ((j & 15) == 0) sb[kind][c] = sbits;
+  __syncthreads();
+  if (tid >= 2 * kNumBlocks) return;
+  const int sk = tid / kNumBlocks, sc = tid % kNumBlocks;
+  uint32_t nib[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock / 2; ++i) {
+    const uint32_t byte = nb[sk][16 * sc + i];
+    nib[2 * i] = byte & 15u;
+    nib[2 * i + 1] = byte >> 4;
+  }
+  const int64_t ph = static_cast<int64_t>(slot / kPage) * Hkv + g;
+  if (sk == 0)
+    f4_store_k_block(st.k_nib, st.k_scale, ph, kNumBlocks, sc, slot % kPage, nib, sb[0][sc]);
+  else
+    f4_store_v_block(st.v_nib, st.v_scale, ph, kHeadDim, sc, slot % kPage, nib, sb[1][sc], st.v_per_token != 0);
 }
 
 // One workgroup per (sequence, KV head): query rows -> QPrep.

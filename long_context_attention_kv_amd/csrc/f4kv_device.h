@@ -27,20 +27,30 @@ __device__ __forceinline__ void rope_rotate_pair(double x0, double x1, double c,
 // so fp64 decides every tie and near-tie exactly.  amax is the block's
 // absolute maximum, or the row's when V carries one scale per token.
 // Returns the scale's fp16 bits.
-__device__ __forceinline__ uint16_t f4_quantize_block(const float* x, float amax, uint32_t* nib) {
+// The block's scale: its fp16 bits, and its value in fp64 for the quotients.
+__device__ __forceinline__ uint16_t f4_scale(float amax, double& sd) {
   const _Float16 s16 = static_cast<_Float16>(fminf(amax * 0.125f, 65504.0f));
-  const double sd = static_cast<double>(static_cast<float>(s16));
-#pragma unroll
-  for (int i = 0; i < kBlock; ++i) {
-    int code = 0;
-    if (sd > 0.0) {
-      double qd = __builtin_rint(static_cast<double>(x[i]) / sd);
-      qd = fmin(fmax(qd, -8.0), 7.0);
-      code = static_cast<int>(qd);
-    }
-    nib[i] = static_cast<uint32_t>(code + 8);
-  }
+  sd = static_cast<double>(static_cast<float>(s16));
   return __builtin_bit_cast(uint16_t, s16);
+}
+
+// The nibble of one value under the scale sd (0 codes to 8 when sd is 0).
+__device__ __forceinline__ uint32_t f4_nibble(float x, double sd) {
+  int code = 0;
+  if (sd > 0.0) {
+    double qd = __builtin_rint(static_cast<double>(x) / sd);
+    qd = fmin(fmax(qd, -8.0), 7.0);
+    code = static_cast<int>(qd);
+  }
+  return static_cast<uint32_t>(code + 8);
+}
+
+__device__ __forceinline__ uint16_t f4_quantize_block(const float* x, float amax, uint32_t* nib) {
+  double sd;
+  const uint16_t sbits = f4_scale(amax, sd);
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) nib[i] = f4_nibble(x[i], sd);
+  return sbits;
 }
 
 // K block c of token slot `off` in page-head ph (= page * H + head): 16 bytes
