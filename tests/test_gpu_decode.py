@@ -62,6 +62,27 @@ def test_windows_and_empty_windows():
     assert_attention_close(out.cpu().numpy(), wo[0], "window fold")
 
 
+@pytest.mark.parametrize("B,W,wt", [(70, 1, 0), (90, 3, 256)])
+def test_many_ranges_block_planner(B, W, wt):
+    """More than 64 (window, sequence) ranges: the work list is built by the
+    whole planning workgroup (W * B = 270 spans two batches of its 256 threads),
+    with empty ranges (zero-length sequences, windows past a short sequence's
+    end) among them."""
+    print(f"decode: {B} sequences, {W} windows of {wt} tokens", flush=True)
+    g = synth.rng(1300 + B, 0)
+    lengths = [int(x) for x in g.integers(0, 900, B)]
+    lengths[::11] = [0] * len(lengths[::11])
+    lengths[5] = 64 * 12 + 3
+    ps = PagedSet(lengths, Hkv=4, seed=1300 + B)
+    (o, m, l), (ro, rm, rl) = _run(ps, 16, seed=B, W=W, wt=wt)
+    for b, n in enumerate(lengths):
+        for w in range(W):
+            if n <= w * wt:  # outputs are [W, B, ...]
+                assert np.all(np.isneginf(m[w, b])) and np.all(l[w, b] == 0) and not o[w, b].any()
+    assert_attention_close(o, ro, f"{B} sequences, {W} windows")
+    assert_states_close(m, l, rm, rl, f"{B} sequences, {W} windows")
+
+
 def test_large_and_small_query_scale():
     ps = PagedSet([777], Hkv=4, seed=9)
     for sc in (1e-3, 30.0):
