@@ -20,11 +20,14 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-I", INCLUDE, "-I", CSRC]
 
 
-# Per-file flags.  The prefill kernel rescales its MFMA accumulators with VALU
-# multiplies; MFMA in the VGPR form keeps them in VGPRs instead of copying them
-# between AGPRs and VGPRs every iteration.
+# Per-file flags.  The prefill kernels rescale their MFMA accumulators with
+# VALU multiplies, and the decode kernel starts each key block's accumulator
+# from VALU values and reads it back after 8 products; MFMA in the VGPR form
+# keeps the accumulators in VGPRs instead of copying them between AGPRs and
+# VGPRs (for the decode kernel that copy would also cost it a wave per SIMD).
 FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "prefill_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "prefill_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

@@ -17,13 +17,17 @@
 // Per page (64 tokens) a wave does two phases:
 //  * keys: lane = token.  The lane loads its token's 8 blocks (8 x 16 B, each
 //    load instruction of the wave reads 1 KB contiguous thanks to the
-//    block-major K tile) and forms the G logits with packed fp16 dot products.
-//    A nibble n is turned into an fp16 operand with one AND: 0x000F000F picks
-//    two nibbles into the mantissas of an fp16 pair, i.e. the subnormals
-//    n * 2^-24; 0x00F000F0 picks the next two as 16 n * 2^-24 (the matching
-//    query pair is pre-divided by 16).  The "- 8" of (n - 8) * s is folded into
-//    the accumulator's start value (-8 * 2^-24 * sum of the block's query
-//    values), and the block scale is applied once per block.
+//    block-major K tile); the G logits are formed on the matrix cores with
+//    the 4 x 4 x 4 fp16 product in 16 blocks, whose lane layout is exactly
+//    lane = token (4 tokens per block, A = 4 query heads x 4 channels, read
+//    from LDS).  A nibble n is turned into an fp16 operand with one AND:
+//    0x000F000F picks two nibbles into the mantissas of an fp16 pair, i.e.
+//    the subnormals n * 2^-24; 0x00F000F0 picks the next two as 16 n * 2^-24
+//    (the matching query pair is pre-divided by 16).  The "- 8" of (n - 8) * s
+//    is folded into the accumulator's start value (-8 * 2^-24 * sum of the
+//    block's query values), and the block scale is applied once per block.
+//    This takes the 512 dot products per page off the vector ALUs, which
+//    otherwise bound the kernel below the memory rate.
 //  * values: lane = 4 consecutive channels.  The V tile stores 8 tokens x 4
 //    channels per 16-byte unit, two tokens per dword, so the same AND masks
 //    yield 16-bit integer pairs (n, or 16 n) over two tokens.  The weights
@@ -315,9 +319,23 @@ __device__ void build_work_list_wave(const PlanArgs& p) {
   if (lane == 0) *p.n_items = items;
 }
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
-                                false);
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// v_mfma_f32_4x4x4_16b_f16: 16 independent 4 x 4 x 4 products.  Lane 4 b + i
+// gives row i of block b's A (4 fp16 in a0, a1), lane 4 b + j column j of its
+// B (b0, b1); lane 4 b + j receives D[i][j] in element i.  With A = 4 query
+// heads (the same in every block) and B = the masked nibbles of token 4 b + j
+// (= the lane), element h of the result is head h's partial logit of the
+// lane's own token.  fp16 subnormal operands (the masked nibbles) are exact.
+__device__ __forceinline__ float4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, float4_t c) {
+  u32x2_t a, b;
+  a.x = a0;
+  a.y = a1;
+  b.x = b0;
+  b.y = b1;
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c, 0, 0,
+                                            0);
 }
 
 // DPP lane permutations within a row of 16 lanes (gfx9 encodings).
@@ -626,6 +644,7 @@ struct __align__(16) DecodeSmem {
   } u;
   float fold_m[kWaves][G];
   float fold_l[kWaves][G];
+  uint4 qa[G][8][4];  // the query pairs of QPrep, read as matrix-core operands
 };
 
 // Combines the per-wave states in LDS (max in log2 units, sum, normalised
@@ -714,6 +733,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     lim[h] = __builtin_amdgcn_readfirstlane(min(t1, ctx - (a.R - 1 - (a.r0 + h / a.Gq))));
 
   const QPrep<G>* QP = qprep + __builtin_amdgcn_readfirstlane(b * a.Hkv + g);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(&QP->pair[0][0][0][0]);
+    for (int i = tid; i < G * 32; i += kThreads) (&sm.qa[0][0][0])[i] = src[i];
+  }
+  __syncthreads();
   float m_run[G], s_max[G], l_lane[G], o[G][4];
   float wpart[G];  // this lane's share (8 tokens of each page) of the summed weights of block cj
 #pragma unroll
@@ -725,6 +749,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
   }
+  constexpr int kSets = (G + 3) / 4;  // matrix-core head sets of 4
+  const int qh = (lane & 3) % G;      // this lane's row of A: head 4 set + qh
   const int cj = lane >> 3;  // block holding this lane's 4 value channels
   const int sub = lane & 7;
   const int32_t* ptrow = a.pt + static_cast<int64_t>(b) * a.max_pages;
@@ -764,13 +790,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     const int tok = lp * kPage + lane;
     const float tmask = (pvalid && tok >= t0 && tok < t1) ? 0.0f : -INFINITY;
 
-    // keys: lane = token
+    // keys: lane = token, on the matrix cores (mfma4): per block 8 products
+    // of 4 channels each, started from the block's "- 8" term; the block
+    // scale is applied once per block
     float logit[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) logit[h] = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      // one block's query operands (G x 16 dwords) in SGPRs at a time
       __builtin_amdgcn_sched_barrier(0);
       int qo = 0;
       asm volatile("" : "+s"(qo));
@@ -778,9 +805,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       pin(kq[c]);
       const uint32_t sw = word(ks, c >> 1);
       const float sc = (c & 1) ? f16_hi(sw) : f16_lo(sw);
-      float acc[G];
+      uint4 qa[kSets][4];  // this lane's head: pairs [dword][4] of block c
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = qb->qinit[h][c];
+      for (int st = 0; st < kSets; ++st)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qa[st][k] = sm.qa[4 * st + qh][c][k];
+      float4_t acc[kSets];
+#pragma unroll
+      for (int st = 0; st < kSets; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[st][i] = 4 * st + i < G ? qb->qinit[4 * st + i][c] : 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t wd = word(kq[c], k);
@@ -790,15 +824,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
         const uint32_t p2 = w8 & 0x000F000Fu;
         const uint32_t p3 = w8 & 0x00F000F0u;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h] = dot2(p0, qb->pair[h][c][k][0], acc[h]);
-          acc[h] = dot2(p1, qb->pair[h][c][k][1], acc[h]);
-          acc[h] = dot2(p2, qb->pair[h][c][k][2], acc[h]);
-          acc[h] = dot2(p3, qb->pair[h][c][k][3], acc[h]);
+        for (int st = 0; st < kSets; ++st) {
+          acc[st] = mfma4(qa[st][k].x, qa[st][k].y, p0, p1, acc[st]);
+          acc[st] = mfma4(qa[st][k].z, qa[st][k].w, p2, p3, acc[st]);
         }
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) logit[h] = fmaf(sc, acc[h], logit[h]);
+      for (int h = 0; h < G; ++h) logit[h] = fmaf(sc, acc[h / 4][h % 4], logit[h]);
     }
 
     // the values are requested only now, so they do not hold registers through
