@@ -566,6 +566,40 @@ def measure_ceilings():
     return out
 
 
+def measure_paged_read(L, n_pages):
+    """The decode kernel's loads without its arithmetic (bench_ceilings.so
+    ceiling_paged_read) over one benchmark layer: its K and V tiles and scale
+    rows per (page, head), page order and work split as in the decode kernel,
+    the last-level cache evicted before each launch; best over a few grid
+    sizes.  None when the ceiling library is not built."""
+    import ctypes as C
+    path = os.path.join(ROOT, "bench_ceilings.so")
+    if not os.path.exists(path):
+        return None
+    lib = C.CDLL(path)
+    lib.ceiling_paged_read.argtypes = [C.c_void_p] * 5 + [C.c_int] * 5 + [C.c_void_p, C.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    c = L.cache
+    B = len(L.lengths)
+    nbytes = B * n_pages * HKV * PAGE * BYTES_PER_TOKEN_HEAD
+    best = {}
+    for grid in (1024, 2048, 4096):
+        def read():
+            assert lib.ceiling_paged_read(c.k_nib.data_ptr(), c.v_nib.data_ptr(), c.k_scale.data_ptr(),
+                                          c.v_scale.data_ptr(), L.pt.data_ptr(), B, L.max_pages, n_pages, HKV,
+                                          grid, sink.data_ptr(), stream) == 0
+        read()
+        ms = float(np.median(timed(read, 5, between=evict_llc)))
+        best[f"grid {grid}"] = nbytes / (ms / 1e3) / 1e9
+    top = max(best, key=best.get)
+    return {"hbm_paged_read_gbs": best[top], "hbm_paged_read_config": top, "hbm_paged_read_gbs_by_config": best,
+            "hbm_paged_read": f"the decode kernel's loads without its arithmetic over one benchmark layer "
+                              f"({nbytes / 1e6:.1f} MB: K and V tiles and scale rows of {B} x {n_pages} pages x "
+                              f"{HKV} heads), workgroups of 4 waves on contiguous page ranges of one (sequence, "
+                              f"head); best of the grids, each the median of 5 launches"}
+
+
 def cpu_prefill_sample(rows=4):
     """The fp64 oracle's prefill on a bounded sample of the chunk workload: the
     last `rows` query positions of the 2,048-query chunk (all 16 heads) over the
@@ -704,6 +738,10 @@ def main():
         f"{r['ms_per_step_eager']:.3f}), {r['value'] / 1e9:.3f} G KV-tokens/s, decode kernel "
         f"{r['decode_kernel_ms_avg'] * 1e3:.1f} us -> {r['decode_gbs']:.0f} GB/s, whole call "
         f"{r['decode_call_ms_avg'] * 1e3:.1f} us -> {r['decode_call_gbs']:.0f} GB/s")
+    paged = None
+    if not args.no_extra:
+        paged = measure_paged_read(r["layers"][0], 262144 // PAGE)
+        log("paged read:", paged)
     del r["layers"]
     torch.cuda.empty_cache()
     extra = {}
@@ -740,6 +778,9 @@ def main():
         cpu = cpu_baseline(args.cpu_tokens)
         cpu["prefill"] = cpu_prefill_sample()
         log("cpu:", cpu)
+    if ceil and paged:
+        ceil.update(paged)
+        ceil["decode_kernel_frac_of_paged_read"] = r["decode_gbs"] / paged["hbm_paged_read_gbs"]
     if ceil:
         # every rate against the measured ceiling as well as the nominal peak
         ceil["decode_kernel_frac_of_measured_read"] = r["decode_gbs"] / ceil["hbm_read_gbs"]
@@ -783,7 +824,8 @@ def main():
                      "bytes_per_launch": r["decode_bytes_per_call"], "launch_ms_avg": r["decode_kernel_ms_avg"],
                      "whole_call_ms_avg": r["decode_call_ms_avg"], "whole_call_gbs": r["decode_call_gbs"],
                      "whole_call_ms_median": r["decode_call_ms_median"], "whole_call_ms_min": r["decode_call_ms_min"],
-                     "frac_of_measured_read": (r["decode_gbs"] / ceil["hbm_read_gbs"]) if ceil else None},
+                     "frac_of_measured_read": (r["decode_gbs"] / ceil["hbm_read_gbs"]) if ceil else None,
+                     "frac_of_paged_read": (r["decode_gbs"] / paged["hbm_paged_read_gbs"]) if paged else None},
         "cpu_baseline": cpu,
         "ceilings": ceil,
         "extra": extra,

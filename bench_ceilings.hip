@@ -1,5 +1,5 @@
-// Measured ceilings of the GPU the benchmark runs on: a plain HBM read kernel
-// and matrix-core loops (fp16, E4M3 and INT8 products, the instructions the
+// Measured ceilings of the GPU the benchmark runs on: a plain HBM read kernel,
+// the decode kernel's paged loads without its arithmetic, and matrix-core loops (fp16, E4M3 and INT8 products, the instructions the
 // prefill kernels issue).  bench.py reports the library's rates against these
 // beside the nominal peaks.  Not part of the library.
 #include <hip/hip_runtime.h>
@@ -33,6 +33,42 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   for (; i < n16; i += stride) {
     const u32x4 a = p[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+// The loads of the decode kernel without its arithmetic: for B sequences of
+// n_pages pages and Hkv KV heads, per (page, head) the K tile (8 KB), its
+// scale row (1 KB), then the V tile (8 KB) and its scale row (1 KB), 16-byte
+// loads with lane = 16-byte column as in the decode kernel.  Work split as in
+// the decode kernel: a workgroup of 4 waves owns a contiguous range of one
+// (sequence, head)'s pages, wave w takes every 4th page of it.
+__global__ __launch_bounds__(256) void paged_read_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                         const u32x4* __restrict__ ks,
+                                                         const u32x4* __restrict__ vs, const int32_t* __restrict__ pt,
+                                                         int B, int max_pages, int n_pages, int Hkv,
+                                                         int chunks_per_head, uint32_t* __restrict__ sink) {
+  const int x = blockIdx.x;
+  const int bh = x / chunks_per_head, c = x % chunks_per_head;
+  if (bh >= B * Hkv) return;
+  const int b = bh / Hkv, h = bh % Hkv;
+  const int per = (n_pages + chunks_per_head - 1) / chunks_per_head;
+  const int p0 = c * per, p1 = min(n_pages, p0 + per);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint32_t acc = 0;
+  for (int p = p0 + wave; p < p1; p += 4) {
+    const int64_t ph = static_cast<int64_t>(pt[static_cast<int64_t>(b) * max_pages + p]) * Hkv + h;
+    u32x4 w[9];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = k[ph * 512 + i * 64 + lane];  // 512 x 16 B per tile
+    w[8] = ks[ph * 64 + lane];                                        // 64 x 16 B per scale row
+#pragma unroll
+    for (int i = 0; i < 9; ++i) acc ^= w[i].x ^ w[i].y ^ w[i].z ^ w[i].w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = v[ph * 512 + i * 64 + lane];
+    w[8] = vs[ph * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) acc ^= w[i].x ^ w[i].y ^ w[i].z ^ w[i].w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
@@ -106,6 +142,26 @@ int ceiling_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid,
     hipLaunchKernelGGL(stream_read_kernel<16>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
   else
     return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// The decode kernel's loads over a paged F4 cache (one fp16 scale per 32
+// values for K and V): k_nib / v_nib [pages][Hkv][8 KB], k_scale / v_scale
+// [pages][Hkv][1 KB], page table pt [B][max_pages] whose first n_pages
+// entries of every row are valid page ids; `grid` workgroups of 4 waves
+// (rounded down to a multiple of B * Hkv).  sink: one device word.
+// 0 = launched.
+int ceiling_paged_read(const void* k_nib, const void* v_nib, const void* k_scale, const void* v_scale,
+                       const int32_t* pt, int B, int max_pages, int n_pages, int Hkv, int grid, uint32_t* sink,
+                       hipStream_t stream) {
+  if (!k_nib || !v_nib || !k_scale || !v_scale || !pt || !sink || B <= 0 || Hkv <= 0 || n_pages <= 0 ||
+      n_pages > max_pages || grid < B * Hkv)
+    return 1;
+  const int chunks = grid / (B * Hkv);
+  hipLaunchKernelGGL(paged_read_kernel, dim3(chunks * B * Hkv), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(k_nib), static_cast<const u32x4*>(v_nib),
+                     static_cast<const u32x4*>(k_scale), static_cast<const u32x4*>(v_scale), pt, B, max_pages,
+                     n_pages, Hkv, chunks, sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -20,25 +20,29 @@
 //    block-major K tile); the G logits are formed on the matrix cores with
 //    the 4 x 4 x 4 fp16 product in 16 blocks, whose lane layout is exactly
 //    lane = token (4 tokens per block, A = 4 query heads x 4 channels, read
-//    from LDS).  A nibble n is turned into an fp16 operand with one AND:
-//    0x000F000F picks two nibbles into the mantissas of an fp16 pair, i.e.
-//    the subnormals n * 2^-24; 0x00F000F0 picks the next two as 16 n * 2^-24
-//    (the matching query pair is pre-divided by 16).  The "- 8" of (n - 8) * s
-//    is folded into the accumulator's start value (-8 * 2^-24 * sum of the
-//    block's query values), and the block scale is applied once per block.
-//    This takes the 512 dot products per page off the vector ALUs, which
-//    otherwise bound the kernel below the memory rate.
-//  * values: lane = 4 consecutive channels.  The V tile stores 8 tokens x 4
-//    channels per 16-byte unit, two tokens per dword, so the same AND masks
-//    yield 16-bit integer pairs (n, or 16 n) over two tokens.  The weights
+//    from LDS).  A nibble n becomes an exact fp16 operand with one AND and one
+//    packed fp16 add: 0x000F000F picks two nibbles into the mantissas of an
+//    fp16 pair, i.e. the subnormals n * 2^-24, and adding -8 * 2^-24 gives
+//    (n - 8) * 2^-24; 0x00F000F0 picks the next two as 16 n * 2^-24 (minus
+//    128 * 2^-24; the matching query pair is pre-divided by 16).  The block
+//    scale is applied once per block.  This takes the 512 dot products per
+//    page off the vector ALUs, which otherwise bound the kernel below the
+//    memory rate.
+//  * values: lane = 4 consecutive channels, on the matrix cores as well.  The
+//    V tile stores 8 tokens x 4 channels per 16-byte unit, two tokens per
+//    dword, so the same masks and add yield fp16 pairs (n - 8) * 2^-24 (x16
+//    for two of the channels) over two tokens: two dwords give one channel
+//    over 4 tokens, a column of the 4 x 4 x 4 product.  The weights
 //    w = p_t * s_t (softmax weight times the token's block scale) travel from
 //    the key phase to the value phase through LDS in fp32 and are turned into
-//    16-bit fixed point per (page, head, block), in units of the block's
-//    largest weight / 65535; one v_dot2_u32_u16 then accumulates two tokens'
-//    u_t n_t exactly in a 32-bit integer, flushed into fp32 once per page.
-//    (An fp16 weight, 11 bits, would leave ~2e-3 of the output RMS on
-//    channels whose values are many times the others'.)  The "- 8" is
-//    corrected once, at the end, with the summed weights of the lane's block.
+//    fp16 pairs hi + lo per (page, head, block), in units of the block's
+//    largest weight (about 21 bits each; a single fp16 weight, 11 bits, would
+//    leave ~2e-3 of the output RMS on channels whose values are many times
+//    the others').
+//    The operands are centred (n - 8, not n with the 8 taken off the sums
+//    afterwards) because the 4 x 4 x 4 product sums with a relative error of
+//    ~2^-19 (measured), which the cancellation of sum w n against 8 sum w
+//    would multiply on channels whose outputs are near zero.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
 #include <algorithm>
@@ -56,15 +60,14 @@ constexpr int kWRow = 68;  // fp32 weights per (head, block) row: 64 tokens + 16
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 units a logit may exceed the running max by
-constexpr float kInvU16 = 1.0f / 65535.0f;
 constexpr int kNumBlocks = kHeadDim / kBlock;  // scale blocks per head row
 
-// Query operands of one (sequence, KV head), prepared once per call and read by
-// the decode kernel with scalar loads (the same for every lane).
+// Query operands of one (sequence, KV head), prepared once per call: the
+// decode kernel copies the pairs to LDS (each lane reads its head's row as
+// matrix-core operands) and reads the logit scales with scalar loads.
 template <int G>
 struct __align__(64) QPrep {
   uint32_t pair[G][8][4][4];  // fp16 pairs [head][block][dword][pair], scaled by 2^e_h
-  float qinit[G][8];          // -8 * 2^-24 * sum of the block's scaled query values
   float kscale[G];            // 2^(24 - e_h) * sm_scale * log2(e)
 };
 
@@ -320,6 +323,7 @@ __device__ void build_work_list_wave(const PlanArgs& p) {
 }
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __fp16 pk16_t __attribute__((ext_vector_type(2)));  // v_cvt_pkrtz_f16_f32's result
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // v_mfma_f32_4x4x4_16b_f16: 16 independent 4 x 4 x 4 products.  Lane 4 b + i
@@ -336,6 +340,13 @@ __device__ __forceinline__ float4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0,
   b.y = b1;
   return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b), c, 0, 0,
                                             0);
+}
+
+// x - bias on two fp16 lanes (v_pk_add_f16 with the negated bias).
+constexpr uint32_t kM8 = 0x80088008u;    // -8 2^-24 in both halves
+constexpr uint32_t kM128 = 0x80808080u;  // -128 2^-24 (the x16 slots)
+__device__ __forceinline__ uint32_t centre(uint32_t x, uint32_t neg_bias) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x) + __builtin_bit_cast(half2_t, neg_bias));
 }
 
 // DPP lane permutations within a row of 16 lanes (gfx9 encodings).
@@ -363,14 +374,6 @@ __device__ __forceinline__ float wave_max(float x) {
   const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
-// Sum over each group of 8 consecutive lanes, returned in all 8.
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp<kDppQuadXor1>(x);
-  x += dpp<kDppQuadXor2>(x);
-  x += dpp<kDppHalfMirror>(x);
-  return x;
 }
 
 template <int kCtrl>
@@ -410,19 +413,6 @@ __device__ __forceinline__ int32_t wave_max_key(int32_t k) {
   const int32_t r0 = __builtin_amdgcn_readlane(k, 0), r1 = __builtin_amdgcn_readlane(k, 16);
   const int32_t r2 = __builtin_amdgcn_readlane(k, 32), r3 = __builtin_amdgcn_readlane(k, 48);
   return max(max(r0, r1), max(r2, r3));
-}
-
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
-
-// Two values in [0, 1] to unsigned 16-bit fixed point, nearest (v_cvt_pknorm_u16_f32):
-// lo = nearest(a 65535), hi = nearest(b 65535).
-__device__ __forceinline__ uint32_t pknorm_u16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_u16(a, b));
-}
-
-// a.lo b.lo + a.hi b.hi + c on unsigned 16-bit pairs, 32-bit accumulate (v_dot2_u32_u16).
-__device__ __forceinline__ uint32_t udot2(uint32_t a, uint32_t b, uint32_t c) {
-  return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b), c, false);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -622,18 +612,6 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
     P.pair[h][c][k][p] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
-  for (int i = tid; i < G * 8; i += kThreads) {
-    const int h = i / 8, c = i % 8;
-    float sum = 0.0f;
-    for (int d = 0; d < kBlock; ++d) {
-      const float v = qf[h][32 * c + d];
-      // the value each channel contributes through its fp16 operand
-      const float rep = (d & 1) ? 16.0f * static_cast<float>(static_cast<_Float16>(ldexpf(v, qexp[h] - 4)))
-                                : static_cast<float>(static_cast<_Float16>(ldexpf(v, qexp[h])));
-      sum += rep;
-    }
-    P.qinit[h][c] = -8.0f * ldexpf(sum, -24);
-  }
 }
 
 template <int G>
@@ -690,8 +668,8 @@ __device__ __forceinline__ void fold_waves(const DecodeSmem<G>& sm, float* dst, 
 
 static_assert((kWRow * 4) % 16 == 0, "weight rows must be 16-byte aligned");
 
-// The 16-bit weights of (wave, head, block): 64 tokens in the first half of
-// that fp32 weight row.
+// The fp16 weights of (wave, head, block), in the place of that fp32 weight
+// row: 64 tokens' hi parts, then their 64 lo parts.
 template <int G>
 __device__ __forceinline__ uint16_t* urow(DecodeSmem<G>& sm, int wave, int h, int c) {
   return reinterpret_cast<uint16_t*>(&sm.u.w[wave][h][c][0]);
@@ -738,14 +716,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int i = tid; i < G * 32; i += kThreads) (&sm.qa[0][0][0])[i] = src[i];
   }
   __syncthreads();
-  float m_run[G], s_max[G], l_lane[G], o[G][4];
-  float wpart[G];  // this lane's share (8 tokens of each page) of the summed weights of block cj
+  float m_run[G], l_lane[G], o[G][4];
+  int32_t kmax_run[G];  // order key of the largest logit so far (uniform)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
-    s_max[h] = -INFINITY;
+    kmax_run[h] = order_key(-INFINITY);
     l_lane[h] = 0.0f;
-    wpart[h] = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
   }
@@ -756,6 +733,55 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   const int32_t* ptrow = a.pt + static_cast<int64_t>(b) * a.max_pages;
   const int lane16 = lane * 16;
 
+  // Tiles of a page go through buffer resources with a scalar base: the lane
+  // offsets are constants, so no per-page address arithmetic runs on the
+  // VALU.  An out-of-range page id (or the page after the wave's last) gets
+  // empty resources: its loads return 0 without memory traffic, and a mask
+  // drops its tokens.
+  struct PageRes {
+    __amdgpu_buffer_rsrc_t k, v, ks, vs;
+    bool valid;
+  };
+  // the page table is read-only here: read through the constant address
+  // space, whose uniform loads are scalar (a vector load of a page id would
+  // have to wait for every tile load issued before it)
+  const auto ptc = (const __attribute__((address_space(4))) int32_t*)(ptrow);
+  auto page_res = [&](int lp) {
+    const int32_t pid = lp < pend ? ptc[lp] : -1;
+    PageRes r;
+    r.valid = static_cast<uint32_t>(pid) < static_cast<uint32_t>(a.num_pages);
+    const int64_t ph = static_cast<int64_t>(r.valid ? pid : 0) * a.Hkv + g;
+    const int tile_bytes = r.valid ? kPage * kHeadDim / 2 : 0;
+    r.k = tile_rsrc(a.k_nib + ph * (kPage * kHeadDim / 2), tile_bytes);
+    r.v = tile_rsrc(a.v_nib + ph * (kPage * kHeadDim / 2), tile_bytes);
+    r.ks = tile_rsrc(a.k_scale + ph * (kPage * 8), r.valid ? kPage * 8 * 2 : 0);
+    r.vs = VT ? tile_rsrc(a.v_scale + ph * kPage, r.valid ? kPage * 2 : 0)
+              : tile_rsrc(a.v_scale + ph * (kPage * 8), r.valid ? kPage * 8 * 2 : 0);
+    return r;
+  };
+  // The loads run one phase ahead through 8 register slots of 1 KB per wave:
+  // slot c holds K block c of the page during the key phase, is then
+  // refilled with the page's V block c; during the value phase it is refilled
+  // with K block c of the wave's next page as soon as its V block is
+  // unpacked, so the next page's keys are on their way while this page's
+  // values are multiplied.  (The compiler copies parts of some slots in the
+  // value phase, which makes those waits cover the slots' loads in flight; a
+  // form without the copies, where every wait is for the oldest load only,
+  // measured 2% slower.)
+  uint4 tl[8];
+  uint4 ks = make_uint4(0, 0, 0, 0), vs = make_uint4(0, 0, 0, 0);
+  uint32_t vs1 = 0;  // this token's V scale (VT)
+  {
+    const PageRes r0 = page_res(pbeg + wave);
+    ks = load16(r0.ks, lane16);
+    if (VT)
+      vs1 = __builtin_amdgcn_raw_buffer_load_b16(r0.vs, lane * 2, 0, 0);
+    else
+      vs = load16(r0.vs, lane16);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) tl[c] = load16(r0.k, lane16, c * 1024);
+  }
+
   for (int lp = pbeg + wave; lp < pend; lp += kWaves) {
     // The query operands are re-read (scalar loads) every page.  An offset the
     // compiler cannot see through keeps it from hoisting all 512 of them out
@@ -763,29 +789,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     int qoff = 0;
     asm volatile("" : "+s"(qoff));
     const QPrep<G>* qp = reinterpret_cast<const QPrep<G>*>(reinterpret_cast<const char*>(QP) + qoff);
-    // Tiles of this page through buffer resources with a scalar base: the lane
-    // offsets are constants, so no per-page address arithmetic runs on the VALU.
-    // An out-of-range page id gets empty resources (loads return 0, no traffic)
-    // and a mask that drops its tokens.
-    const int32_t pid = ptrow[lp];
-    const bool pvalid = static_cast<uint32_t>(pid) < static_cast<uint32_t>(a.num_pages);
-    const int64_t ph = static_cast<int64_t>(pvalid ? pid : 0) * a.Hkv + g;
-    const int tile_bytes = pvalid ? kPage * kHeadDim / 2 : 0;
-    const int scale_bytes = pvalid ? kPage * 8 * 2 : 0;
-    const auto rk = tile_rsrc(a.k_nib + ph * (kPage * kHeadDim / 2), tile_bytes);
-    const auto rv = tile_rsrc(a.v_nib + ph * (kPage * kHeadDim / 2), tile_bytes);
-    uint4 kq[8], vq[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) kq[c] = load16(rk, lane16, c * 1024);
+    const PageRes cur = page_res(lp);
+    const bool pvalid = cur.valid;
+    const auto rv = cur.v;
     __builtin_amdgcn_s_setprio(0);
-    const uint4 ks = load16(tile_rsrc(a.k_scale + ph * (kPage * 8), scale_bytes), lane16);
-    uint4 vs = make_uint4(0, 0, 0, 0);
-    uint32_t vs1 = 0;  // this token's V scale (VT)
-    if (VT)
-      vs1 = __builtin_amdgcn_raw_buffer_load_b16(tile_rsrc(a.v_scale + ph * kPage, pvalid ? kPage * 2 : 0),
-                                                 lane * 2, 0, 0);
-    else
-      vs = load16(tile_rsrc(a.v_scale + ph * (kPage * 8), scale_bytes), lane16);
 
     const int tok = lp * kPage + lane;
     const float tmask = (pvalid && tok >= t0 && tok < t1) ? 0.0f : -INFINITY;
@@ -799,10 +806,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       __builtin_amdgcn_sched_barrier(0);
-      int qo = 0;
-      asm volatile("" : "+s"(qo));
-      const QPrep<G>* qb = reinterpret_cast<const QPrep<G>*>(reinterpret_cast<const char*>(qp) + qo);
-      pin(kq[c]);
+      pin(tl[c]);
       const uint32_t sw = word(ks, c >> 1);
       const float sc = (c & 1) ? f16_hi(sw) : f16_lo(sw);
       uint4 qa[kSets][4];  // this lane's head: pairs [dword][4] of block c
@@ -812,17 +816,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
         for (int k = 0; k < 4; ++k) qa[st][k] = sm.qa[4 * st + qh][c][k];
       float4_t acc[kSets];
 #pragma unroll
-      for (int st = 0; st < kSets; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[st][i] = 4 * st + i < G ? qb->qinit[4 * st + i][c] : 0.0f;
+      for (int st = 0; st < kSets; ++st) acc[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t wd = word(kq[c], k);
-        const uint32_t p0 = wd & 0x000F000Fu;
-        const uint32_t p1 = wd & 0x00F000F0u;
+        // centred operands (n - 8) 2^-24 (x16 for p1, p3), as for the values
+        const uint32_t wd = word(tl[c], k);
+        const uint32_t p0 = centre(wd & 0x000F000Fu, kM8);
+        const uint32_t p1 = centre(wd & 0x00F000F0u, kM128);
         const uint32_t w8 = wd >> 8;
-        const uint32_t p2 = w8 & 0x000F000Fu;
-        const uint32_t p3 = w8 & 0x00F000F0u;
+        const uint32_t p2 = centre(w8 & 0x000F000Fu, kM8);
+        const uint32_t p3 = centre(w8 & 0x00F000F0u, kM128);
+        if (k == 3) {
+          // the slot's next tile, V block c, requested once the K block is
+          // unpacked (issued earlier, the load would need registers of its
+          // own, and the loop would copy the slots at every page)
+          __builtin_amdgcn_sched_barrier(0);
+          tl[c] = load16(rv, lane16, c * 1024);
+        }
 #pragma unroll
         for (int st = 0; st < kSets; ++st) {
           acc[st] = mfma4(qa[st][k].x, qa[st][k].y, p0, p1, acc[st]);
@@ -832,45 +842,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 #pragma unroll
       for (int h = 0; h < G; ++h) logit[h] = fmaf(sc, acc[h / 4][h % 4], logit[h]);
     }
-
-    // the values are requested only now, so they do not hold registers through
-    // the key phase (other waves cover their latency)
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vq[c] = load16(rv, lane16, c * 1024);
 
     // Online softmax in log2 units with a lazily raised running max: m_run
     // moves (and the state is rescaled) only when the page's largest logit
     // exceeds it by more than kSlack, so weights stay below 2^kSlack and
     // most pages skip the rescale.  The exact maximum is tracked per lane and
-    // restored at the end.  The page's largest logit per head also names its
-    // top token (the lowest lane among ties), whose weights bypass the 16-bit
-    // fixed point below.
+    // restored at the end.
     float p[G], s[G], pm[G];
-    int ttop[G];
     bool raise = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       // additive mask: written as a select, the compiler turns the whole key
       // phase into a branch on the token's validity
       s[h] = fmaf(logit[h], qp->kscale[h], tok < lim[h] ? tmask : -INFINITY);
-      s_max[h] = fmaxf(s_max[h], s[h]);
-      const int32_t key = order_key(s[h]);
-      const int32_t kmax = wave_max_key(key);
+      const int32_t kmax = wave_max_key(order_key(s[h]));
+      kmax_run[h] = max(kmax_run[h], kmax);
       pm[h] = key_value(kmax);
       raise |= pm[h] > m_run[h] + kSlack;
-      // all lanes -inf (nothing valid): token 0, whose weights are 0
-      const uint64_t at_max = __builtin_amdgcn_ballot_w64(key == kmax);
-      ttop[h] = at_max ? static_cast<int>(__builtin_ctzll(at_max)) : 0;
     }
-    // the top token's V dword of this lane's channels (tokens 2k, 2k + 1 of
-    // its group): a cached read of cells just requested, used before the
-    // value products
-    uint32_t vtop[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      vtop[h] = __builtin_amdgcn_raw_buffer_load_b32(rv, lane16, (ttop[h] >> 3) * 1024 + ((ttop[h] & 7) >> 1) * 4,
-                                                     0);
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -878,10 +868,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
         // mn == -inf only while no valid token has been seen: nothing to rescale
         const float alpha = m_run[h] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - mn);
         l_lane[h] *= alpha;
-        wpart[h] *= alpha;
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[h][d] *= alpha;
-        m_run[h] = mn;
+        m_run[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));
       }
     }
 #pragma unroll
@@ -908,29 +897,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     lds_wave_sync();
     const int wrow = VT ? 0 : cj;  // fp32 weight row of this lane's value block
 
-    // The top token of each head leaves the rows: its fp32 weight for this
-    // lane's block is kept and a zero takes its place (every lane of a block
-    // reads, then writes, the same element; LDS keeps one wave's order).
-    float wtop[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) wtop[h] = sm.u.w[wave][h][wrow][ttop[h]];
-    lds_wave_sync();
-#pragma unroll
-    for (int h = 0; h < G; ++h) sm.u.w[wave][h][wrow][ttop[h]] = 0.0f;
-    lds_wave_sync();
-
-    // Weights to 16-bit fixed point.  The 8 lanes of block cj share the row of
-    // the block's 64 weights per head; lane sub converts tokens 8 sub .. 8 sub
-    // + 7.  The row's largest weight w_max sets the unit w_max / 65535, so
-    // u = nearest(w 65535 / w_max) keeps 16 bits for the largest weight and an
-    // absolute error of at most w_max / 131070 for every weight; the sums of
-    // u n over the page are exact in 32-bit integers.  With the page's top
-    // token taken out, w_max is the second largest weight of the row: a
-    // dominant token no longer coarsens the unit of all the others (that
-    // error, summed over the page's tokens and multiplied by outlier values,
-    // would approach 2e-3 of the output RMS when a few tokens hold most of the
-    // attention).  The 16-bit rows overwrite the first half of the fp32 rows
-    // once every lane of the wave has read its part.
+    // Weights to fp16 pairs hi + lo in units of the row's largest weight.
+    // The 8 lanes of block cj share the row of the block's 64 weights per
+    // head; lane sub converts tokens 8 sub .. 8 sub + 7.  u = w / w_max is in
+    // [0, 1]; hi = fp16(u) (toward zero) and lo = fp16(u - hi) carry u to
+    // ~2^-21 of itself, with an absolute floor of 2^-25 (fp16 subnormals),
+    // so every weight keeps about 21 bits, the small ones included.  The
+    // 16-bit rows [hi: 64 tokens][lo: 64 tokens] overwrite the fp32 row once
+    // every lane of the wave has read its part.
     float4_t wx[G], wy[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -938,96 +912,98 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
       wy[h] = *reinterpret_cast<const float4_t*>(&sm.u.w[wave][h][wrow][sub * 8 + 4]);
     }
     lds_wave_sync();
-    float funit[G];  // value of one unit of u in the units of the value products (n 2^-24)
+    float funit[G];  // w_max of the lane's block row, per head
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float4_t x = wx[h], y = wy[h];
       const float mx = max8_nonneg(x, y);
-      // 1 / w_max (a zero row scales by 1e30 and stays zero); x r <= 1 up to
-      // the reciprocal's rounding, and pknorm clamps to [0, 1]
+      // 1 / w_max (a zero row scales by 1e30 and stays zero)
       const float r = __builtin_amdgcn_rcpf(fmaxf(mx, 1e-30f));
-      uint4 u;
-      u.x = pknorm_u16(x.x * r, x.y * r);
-      u.y = pknorm_u16(x.z * r, x.w * r);
-      u.z = pknorm_u16(y.x * r, y.y * r);
-      u.w = pknorm_u16(y.z * r, y.w * r);
-      *reinterpret_cast<uint4*>(&urow(sm, wave, h, cj)[sub * 8]) = u;
-      // "- 8" correction, part 1: this lane's 8 tokens of the block's
-      // (rounded) weights; the sum over the lanes waits for the epilogue
-      const uint32_t usum = udot2(u.x, 0x00010001u, udot2(u.y, 0x00010001u,
-                                  udot2(u.z, 0x00010001u, udot2(u.w, 0x00010001u, 0u))));
-      wpart[h] = fmaf(static_cast<float>(usum), mx * kInvU16, wpart[h]);
-      funit[h] = mx * (kInvU16 * 0x1p-24f);
+      const float xs[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const pk16_t hp = __builtin_amdgcn_cvt_pkrtz(xs[2 * i] * r, xs[2 * i + 1] * r);
+        const float r0 = fmaf(xs[2 * i], r, -static_cast<float>(hp.x));
+        const float r1 = fmaf(xs[2 * i + 1], r, -static_cast<float>(hp.y));
+        hi[i] = __builtin_bit_cast(uint32_t, hp);
+        lo[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+      }
+      uint16_t* row = urow(sm, wave, h, wrow);
+      *reinterpret_cast<uint4*>(&row[sub * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&row[64 + sub * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      funit[h] = mx;
     }
     lds_wave_sync();
 
-    // The top tokens in fp32: weight x (n - 8) for this lane's 4 channels,
-    // in the units of the value products (n 2^-24, x16 for channels 1 and 3:
-    // the masked nibbles are exactly those fp16 subnormals); the "- 8" goes
-    // with the block's summed weights, counted once per block (lane sub 0).
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint32_t hw = vtop[h] >> ((ttop[h] & 1) * 16);
-      const uint32_t h8 = hw >> 8;
-      o[h][0] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, hw & 0x000Fu).x), o[h][0]);
-      o[h][1] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, hw & 0x00F0u).x), o[h][1]);
-      o[h][2] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, h8 & 0x000Fu).x), o[h][2]);
-      o[h][3] = fmaf(wtop[h], static_cast<float>(__builtin_bit_cast(half2_t, h8 & 0x00F0u).x), o[h][3]);
-      wpart[h] = fmaf(wtop[h], sub == 0 ? 1.0f : 0.0f, wpart[h]);
-    }
-
-    // values: lane = channels 4*lane .. 4*lane+3 (block cj); per token pair
-    // one 16-bit dot product (two tokens' weights x their nibbles, 32-bit
-    // integer accumulate); this wave's VALU stream goes first while it holds
-    // its operands
+    // values: lane = channels 4 lane .. 4 lane + 3 (block cj), on the matrix
+    // cores (mfma4) with lane = column: slot e of 4 is channel 4 lane + e, B
+    // = its nibbles over 4 tokens (the masked 16-bit pairs of two V dwords),
+    // A = the 4 tokens' weights (hi, then lo) of head 4 set + (lane & 3) in
+    // block cj, the block of all 4 lanes of a 16-lane matrix block.  Element
+    // h of slot e's result is head h's sum for the lane's channel e.
     __builtin_amdgcn_s_setprio(2);
-    uint32_t oi[G][4];
+    // the next page's K scales (this page's are consumed), then its K blocks
+    // into the slots; its V scales last (they are needed after its key phase)
+    const PageRes nxt = page_res(lp + kWaves);
+    ks = load16(nxt.ks, lane16);
+    float4_t ov[kSets][4];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int st = 0; st < kSets; ++st)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) oi[h][d] = 0u;
+      for (int e = 0; e < 4; ++e) ov[st][e] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       if ((ct & 1) == 0) __builtin_amdgcn_sched_barrier(0);  // two token groups' weights in flight
-      pin(vq[ct]);
-      uint4 uw[G];  // 16-bit weight pairs of tokens 8ct .. 8ct+7
+      pin(tl[ct]);
+      uint4 whi[kSets], wlo[kSets];  // fp16 weights of tokens 8 ct .. 8 ct + 7
 #pragma unroll
-      for (int h = 0; h < G; ++h) uw[h] = *reinterpret_cast<const uint4*>(&urow(sm, wave, h, cj)[ct * 8]);
+      for (int st = 0; st < kSets; ++st) {
+        const uint16_t* row = urow(sm, wave, 4 * st + qh, wrow);
+        whi[st] = *reinterpret_cast<const uint4*>(&row[ct * 8]);
+        wlo[st] = *reinterpret_cast<const uint4*>(&row[64 + ct * 8]);
+      }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t wd = word(vq[ct], k);
-        // 16-bit pairs (token 8ct+2k, token 8ct+2k+1) of channels 0..3 (x16 for 1 and 3)
-        const uint32_t v0 = wd & 0x000F000Fu;
-        const uint32_t v1 = wd & 0x00F000F0u;
-        const uint32_t w8 = wd >> 8;
-        const uint32_t v2 = w8 & 0x000F000Fu;
-        const uint32_t v3 = w8 & 0x00F000F0u;
+      for (int q = 0; q < 2; ++q) {  // tokens 8 ct + 4 q .. 8 ct + 4 q + 3: V dwords 2 q, 2 q + 1
+        const uint32_t d0 = word(tl[ct], 2 * q), d1 = word(tl[ct], 2 * q + 1);
+        const uint32_t e0 = d0 >> 8, e1 = d1 >> 8;
+        // fp16 pairs (n - 8) 2^-24 of channels 0..3 (x16 for 1 and 3) over the
+        // 4 tokens: the masked nibbles, then the "- 8" by one packed fp16 add
+        // (exact: integer multiples of 2^-24 within the subnormal range).
+        // Centred operands keep the matrix product away from the cancellation
+        // of sum u n against 8 sum u, whose relative error (~2^-19 per 4 x 4 x
+        // 4 product, measured) would otherwise grow with the ratio of the two.
+        const uint32_t b[4][2] = {{centre(d0 & 0x000F000Fu, kM8), centre(d1 & 0x000F000Fu, kM8)},
+                                  {centre(d0 & 0x00F000F0u, kM128), centre(d1 & 0x00F000F0u, kM128)},
+                                  {centre(e0 & 0x000F000Fu, kM8), centre(e1 & 0x000F000Fu, kM8)},
+                                  {centre(e0 & 0x00F000F0u, kM128), centre(e1 & 0x00F000F0u, kM128)}};
+        if (q == 1) {
+          // the slot's next tile, the next page's K block ct, once the V block
+          // is unpacked
+          __builtin_amdgcn_sched_barrier(0);
+          tl[ct] = load16(nxt.k, lane16, ct * 1024);
+        }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint32_t up = word(uw[h], k);
-          oi[h][0] = udot2(up, v0, oi[h][0]);
-          oi[h][1] = udot2(up, v1, oi[h][1]);
-          oi[h][2] = udot2(up, v2, oi[h][2]);
-          oi[h][3] = udot2(up, v3, oi[h][3]);
+        for (int st = 0; st < kSets; ++st) {
+          const uint32_t h0 = word(whi[st], 2 * q), h1 = word(whi[st], 2 * q + 1);
+          const uint32_t l0 = word(wlo[st], 2 * q), l1 = word(wlo[st], 2 * q + 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ov[st][e] = mfma4(h0, h1, b[e][0], b[e][1], ov[st][e]);
+            ov[st][e] = mfma4(l0, l1, b[e][0], b[e][1], ov[st][e]);
+          }
         }
       }
     }
-    // the page's integer sums (< 64 x 65535 x 240 < 2^32) into the fp32 accumulators
+    if (VT)
+      vs1 = __builtin_amdgcn_raw_buffer_load_b16(nxt.vs, lane * 2, 0, 0);
+    else
+      vs = load16(nxt.vs, lane16);
+    // the page's sums, in units of w_max, into the running accumulators
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) o[h][d] = fmaf(static_cast<float>(oi[h][d]), funit[h], o[h][d]);
-  }
-
-  // "- 8" correction, part 2: the summed weights of block cj over every page of
-  // the wave, times 8 (in the units of the nibble operands, 2^-24 and 16 x 2^-24)
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float c1 = sum8(wpart[h]) * 4.76837158203125e-07f;  // 8 * 2^-24
-    o[h][0] -= c1;
-    o[h][1] -= 16.0f * c1;
-    o[h][2] -= c1;
-    o[h][3] -= 16.0f * c1;
+      for (int e = 0; e < 4; ++e) o[h][e] = fmaf(ov[h / 4][e][h % 4], funit[h], o[h][e]);
   }
 
   // ---- epilogue: restore the exact maximum, fold the 4 waves ---------------
@@ -1035,7 +1011,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   float l_w[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mx = wave_max(s_max[h]);  // <= m_run + kSlack
+    const float mx = key_value(kmax_run[h]);  // <= m_run + kSlack
     if (mx != -INFINITY) {
       const float f = __builtin_amdgcn_exp2f(m_run[h] - mx);
       l_lane[h] *= f;

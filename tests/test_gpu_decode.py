@@ -91,6 +91,26 @@ def test_large_and_small_query_scale():
         assert_states_close(m, l, rm, rl, f"q scale {sc}")
 
 
+@pytest.mark.parametrize("offset", [3.0, -6.0])
+def test_query_with_a_common_offset(offset):
+    """Queries N(0, 1) + offset over outlier channels: the logits carry a large
+    common term sum_c q_c (n_c - 8) s that an uncentred product (sum q n, then
+    8 sum q taken off) would have to cancel."""
+    print(f"decode, queries N(0,1) + {offset}", flush=True)
+    ps = PagedSet([700, 130, 2000], Hkv=4, seed=31, outliers=True)
+    g = synth.rng(231, 1)
+    qf = synth.normal_f32(g, (3, 16, 256)) + np.float32(offset)
+    bits = synth.f32_to_bf16_bits(qf)
+    qv = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    out, m, l = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits), ps.gpu_page_table(), ps.gpu_lengths(), 2000,
+                                        SM / 4)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle_decode(ps, qv, SM / 4)
+    rel = assert_attention_close(out.cpu().numpy(), ro, f"query offset {offset}")
+    print(f"decode, queries N(0,1) + {offset}: max |delta| / RMS = {rel:.2e}", flush=True)
+    assert_states_close(m.cpu().numpy(), l.cpu().numpy(), rm, rl, f"query offset {offset}")
+
+
 @pytest.mark.parametrize("sm", [0.0, -1.0 / 16.0, 0.25])
 def test_logit_scale_signs(sm):
     """A zero logit scale (uniform weights), a negative one and a large one."""
