@@ -397,7 +397,7 @@ def bench_rows(R, iters=10):
         f4.paged_attn_decode_rows_f4(L.cache, q, L.pt, L.ctx, 262144, SM, out=out, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # three or more rows (of 4 query heads per KV head) run on the prefill kernel
+    # five or more rows (of 4 query heads per KV head) run on the prefill kernel
     with f4.KernelTimer(f4.KERNEL_DECODE, max_launches=64 * iters) as t, \
             f4.KernelTimer(f4.KERNEL_PREFILL, max_launches=64 * iters) as tp:
         e0.record()

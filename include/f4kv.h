@@ -271,7 +271,7 @@ int paged_attn_decode_step_f4(const f4kv_cache* cache, const float* cos_rows, co
  *   paged_attn_decode_rows_f4_workspace_size().
  * The rows of a KV head's query heads are processed together, up to 8 per
  * pass over the pages (Hq / H * R rows; more take several passes).  With
- * Hq / H == 4, R >= 3 and one window over the whole context (num_windows == 1,
+ * Hq / H == 4, R >= 5 and one window over the whole context (num_windows == 1,
  * window_tokens == 0), a verification round is a short causal prefill: the
  * rows then run on the prefill kernel (fp16 matrix cores with exact splits,
  * one pass over the pages for all R rows), within the same tolerance.
@@ -419,7 +419,7 @@ int f4kv_device_check_word(uint32_t* word);
  *           preparation or fold);
  *           F4KV_KERNEL_PREFILL: the attention kernel of paged_attn_prefill_f4,
  *           which also runs the verification rounds of paged_attn_decode_rows_f4
- *           that go to it (R >= 3, see there).
+ *           that go to it (R >= 5, see there).
  *           F4KV_KERNEL_PREFILL_FP8: that of paged_attn_prefill_f4_fp8.
  * Timing one kernel from two host threads at once is not supported.
  */

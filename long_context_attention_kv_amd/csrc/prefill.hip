@@ -758,15 +758,15 @@ hipError_t launch_prefill(const f4kv_cache& c, const uint16_t* q, const int32_t*
   return launch_merge(pm, pl, a.o, plan.kv_splits, static_cast<int32_t>(R), kHeadDim, out, out_m, out_l, s);
 }
 
-// Three or more rows of a group of 4 query heads (12 or more rows per KV head,
-// two or more passes of the decode kernel over the pages) go through this
+// Five or more rows of a group of 4 query heads (20 or more rows per KV head,
+// three or more passes of the decode kernel over the pages) go through this
 // kernel, whose workgroup reads each page once for up to 32 rows with
 // matrix-core products (the ROWS form: the four waves share the rows and
 // split each page's tokens and output channels): a verification round is a
 // short causal prefill over the cache.  Whole-context calls only.
 int32_t rows_prefill_splits(int32_t B, int32_t R, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t num_windows,
                             int32_t window_tokens) {
-  if (R < 3 || R > 8 || Hq != 4 * Hkv || num_windows != 1 || window_tokens != 0 || B <= 0) return 0;
+  if (R < 5 || R > 8 || Hq != 4 * Hkv || num_windows != 1 || window_tokens != 0 || B <= 0) return 0;
   const int64_t wgs = static_cast<int64_t>(B) * Hkv;
   const int64_t total_pages = (static_cast<int64_t>(max_ctx) + kPage - 1) / kPage;
   int64_t splits = 512 / wgs;  // at most two rounds of one workgroup per CU, as the prefill plans

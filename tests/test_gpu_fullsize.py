@@ -354,7 +354,7 @@ def test_v_per_token_decode_3x262144():
                     (ref[0][0], ref[1][0], ref[2][0]), f"per-token V, lane {b} kv head {h}")
 
 
-@pytest.mark.parametrize("R", [2, 8])
+@pytest.mark.parametrize("R", [2, 4, 8])  # one decode pass, two decode passes, the prefill kernel
 def test_rows_decode_3x262144(R):
     print(f"case: {R} query rows per lane, 3 lanes x 262,144 tokens", flush=True)
     n = 262144

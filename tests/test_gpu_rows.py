@@ -31,8 +31,8 @@ def _run(ps, R, Hq, seed, W=1, wt=0):
 
 @pytest.mark.parametrize("R", [2, 3, 5, 8])
 def test_rows_group_of_four(R):
-    # 4 query heads per KV head: 2 rows run on the decode kernel (one pass over the pages); 3 and more
-    # rows of a whole-context call go through the prefill kernel
+    # 4 query heads per KV head: 2 rows run on the decode kernel in one pass over the pages, 3 in two;
+    # 5 and more rows of a whole-context call go through the prefill kernel
     ps = PagedSet([700, 130, 64 * 20 + 5], Hkv=4, seed=900 + R)
     (o, m, l), (ro, rm, rl), _ = _run(ps, R, 16, R)
     assert_attention_close(o, ro, f"R={R}")
@@ -58,23 +58,26 @@ def test_rows_short_contexts_and_windows():
 
 def test_one_row_is_plain_decode_and_last_row_matches_decode():
     ps = PagedSet([2000, 77], Hkv=4, seed=930)
-    bits, _ = _q(2, 3, 16, 30)
+    bits, _ = _q(2, 5, 16, 30)
     pt, lens = ps.gpu_page_table(), ps.gpu_lengths()
-    one = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 2:3].copy()), pt, lens, 2000, SM)[0]
-    dec = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits[:, 2].copy()), pt, lens, 2000, SM)[0]
-    # two rows run on the decode kernel too (its products, to within fp32 summation order); three rows
-    # on the prefill kernel (its own products, within the attention tolerance)
-    two = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 1:3].copy()), pt, lens, 2000, SM)[0]
-    three = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), pt, lens, 2000, SM)[0]
+    one = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 4:5].copy()), pt, lens, 2000, SM)[0]
+    dec = f4.paged_attn_decode_f4(ps.gc, bf16_tensor(bits[:, 4].copy()), pt, lens, 2000, SM)[0]
+    # two and three rows run on the decode kernel too (its products, to within fp32 summation order);
+    # five rows on the prefill kernel (its own products, within the attention tolerance)
+    two = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 3:5].copy()), pt, lens, 2000, SM)[0]
+    three = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits[:, 2:5].copy()), pt, lens, 2000, SM)[0]
+    five = f4.paged_attn_decode_rows_f4(ps.gc, bf16_tensor(bits), pt, lens, 2000, SM)[0]
     torch.cuda.synchronize()
     assert torch.equal(one[:, :, 0], dec)
-    assert torch.allclose(two[:, :, 1], dec, rtol=0, atol=1e-5 * float(dec.abs().max()))
-    assert_attention_close(three[:, :, 2].cpu().numpy(), dec.cpu().numpy(), "last of three rows vs decode")
+    tol = 1e-5 * float(dec.abs().max())
+    assert torch.allclose(two[:, :, 1], dec, rtol=0, atol=tol)
+    assert torch.allclose(three[:, :, 2], dec, rtol=0, atol=tol)
+    assert_attention_close(five[:, :, 4].cpu().numpy(), dec.cpu().numpy(), "last of five rows vs decode")
 
 
 @pytest.mark.parametrize("v_per_token", [False, True])
 def test_rows_through_the_prefill_kernel_short_contexts(v_per_token):
-    """Rows of whole-context calls with R >= 3 (group of 4) run on the prefill
+    """Rows of whole-context calls with R >= 5 (group of 4) run on the prefill
     kernel: contexts shorter than R leave the leading rows empty (the merge
     identity), an empty context all of them."""
     print(f"rows via prefill, short contexts, v_per_token={v_per_token}", flush=True)
@@ -106,11 +109,11 @@ def test_rows_through_the_prefill_kernel_agree_with_the_decode_kernel():
 
 
 def test_rows_through_the_prefill_kernel_drop_out_of_range_pages():
-    """Out-of-range page ids on the prefill kernel's verification route (R = 4):
+    """Out-of-range page ids on the prefill kernel's verification route (R = 5):
     those pages' tokens are dropped; each row's expected result is the oracle's
     attention over the remaining tokens up to its position."""
     print("rows via prefill, out-of-range page ids", flush=True)
-    R = 4
+    R = 5
     ps = PagedSet([1300, 200], Hkv=4, seed=960)
     pt = ps.pt.copy()
     dropped = {0: [0, 9], 1: [2]}
