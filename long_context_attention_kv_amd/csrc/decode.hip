@@ -783,12 +783,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
   }
 
   for (int lp = pbeg + wave; lp < pend; lp += kWaves) {
-    // The query operands are re-read (scalar loads) every page.  An offset the
-    // compiler cannot see through keeps it from hoisting all 512 of them out
-    // of the loop, which would spill.
-    int qoff = 0;
-    asm volatile("" : "+s"(qoff));
-    const QPrep<G>* qp = reinterpret_cast<const QPrep<G>*>(reinterpret_cast<const char*>(QP) + qoff);
     const PageRes cur = page_res(lp);
     const bool pvalid = cur.valid;
     const auto rv = cur.v;
@@ -855,7 +849,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     for (int h = 0; h < G; ++h) {
       // additive mask: written as a select, the compiler turns the whole key
       // phase into a branch on the token's validity
-      s[h] = fmaf(logit[h], qp->kscale[h], tok < lim[h] ? tmask : -INFINITY);
+      s[h] = fmaf(logit[h], QP->kscale[h], tok < lim[h] ? tmask : -INFINITY);
       const int32_t kmax = wave_max_key(order_key(s[h]));
       kmax_run[h] = max(kmax_run[h], kmax);
       pm[h] = key_value(kmax);
@@ -903,7 +897,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     // [0, 1]; hi = fp16(u) (toward zero) and lo = fp16(u - hi) carry u to
     // ~2^-21 of itself, with an absolute floor of 2^-25 (fp16 subnormals),
     // so every weight keeps about 21 bits, the small ones included.  The
-    // 16-bit rows [hi: 64 tokens][lo: 64 tokens] overwrite the fp32 row once
+    // fp16 rows [hi: 64 tokens][lo: 64 tokens] overwrite the fp32 row once
     // every lane of the wave has read its part.
     float4_t wx[G], wy[G];
 #pragma unroll
@@ -938,7 +932,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
 
     // values: lane = channels 4 lane .. 4 lane + 3 (block cj), on the matrix
     // cores (mfma4) with lane = column: slot e of 4 is channel 4 lane + e, B
-    // = its nibbles over 4 tokens (the masked 16-bit pairs of two V dwords),
+    // = its centred nibbles over 4 tokens (the fp16 pairs of two V dwords),
     // A = the 4 tokens' weights (hi, then lo) of head 4 set + (lane & 3) in
     // block cj, the block of all 4 lanes of a 16-lane matrix block.  Element
     // h of slot e's result is head h's sum for the lane's channel e.
