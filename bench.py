@@ -533,7 +533,7 @@ def measure_ceilings():
     if not os.path.exists(path):
         return None
     lib = C.CDLL(path)
-    lib.ceiling_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int, C.c_void_p]
+    lib.ceiling_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
     lib.ceiling_mfma.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.POINTER(C.c_double), C.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 4 << 30
@@ -541,19 +541,21 @@ def measure_ceilings():
     buf.fill_(3)
     sink = torch.zeros(256, dtype=torch.float32, device="cuda")
     best = {}
-    for unroll in (4, 8, 16):
-        for grid in (2048, 8192, 16384, 32768):
-            def read():
-                assert lib.ceiling_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, stream) == 0
-            read()
-            ms = float(np.median(timed(read, 5)))
-            best[f"grid {grid}, {unroll} loads"] = nbytes / (ms / 1e3) / 1e9
+    for nt in (0, 1):
+        for unroll in (4, 8, 16):
+            for grid in (2048, 8192, 16384, 32768):
+                def read():
+                    assert lib.ceiling_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, nt,
+                                                   stream) == 0
+                read()
+                ms = float(np.median(timed(read, 5)))
+                best[f"grid {grid}, {unroll} loads{', non-temporal' if nt else ''}"] = nbytes / (ms / 1e3) / 1e9
     del buf
     torch.cuda.empty_cache()
     top = max(best, key=best.get)
     out = {"hbm_read_gbs": best[top], "hbm_read_config": top, "hbm_read_gbs_by_config": best,
-           "hbm_read": "4 GiB read once per launch, 16-byte loads per thread, grid-stride; best of the "
-                       "configurations, each the median of 5 launches"}
+           "hbm_read": "4 GiB read once per launch, 16-byte loads per thread, grid-stride, with and without the "
+                       "non-temporal hint; best of the configurations, each the median of 5 launches"}
     for kind, name in ((0, "mfma_f16_tflops"), (1, "mfma_fp8_tflops"), (2, "mfma_i8_tops")):
         fl = C.c_double(0.0)
 
@@ -577,27 +579,29 @@ def measure_paged_read(L, n_pages):
     if not os.path.exists(path):
         return None
     lib = C.CDLL(path)
-    lib.ceiling_paged_read.argtypes = [C.c_void_p] * 5 + [C.c_int] * 5 + [C.c_void_p, C.c_void_p]
+    lib.ceiling_paged_read.argtypes = [C.c_void_p] * 5 + [C.c_int] * 6 + [C.c_void_p, C.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     c = L.cache
     B = len(L.lengths)
     nbytes = B * n_pages * HKV * PAGE * BYTES_PER_TOKEN_HEAD
     best = {}
-    for grid in (1024, 2048, 4096):
-        def read():
-            assert lib.ceiling_paged_read(c.k_nib.data_ptr(), c.v_nib.data_ptr(), c.k_scale.data_ptr(),
-                                          c.v_scale.data_ptr(), L.pt.data_ptr(), B, L.max_pages, n_pages, HKV,
-                                          grid, sink.data_ptr(), stream) == 0
-        read()
-        ms = float(np.median(timed(read, 5, between=evict_llc)))
-        best[f"grid {grid}"] = nbytes / (ms / 1e3) / 1e9
+    for nt in (0, 1):
+        for grid in (1024, 2048, 4096):
+            def read():
+                assert lib.ceiling_paged_read(c.k_nib.data_ptr(), c.v_nib.data_ptr(), c.k_scale.data_ptr(),
+                                              c.v_scale.data_ptr(), L.pt.data_ptr(), B, L.max_pages, n_pages, HKV,
+                                              grid, nt, sink.data_ptr(), stream) == 0
+            read()
+            ms = float(np.median(timed(read, 5, between=evict_llc)))
+            best[f"grid {grid}{', non-temporal' if nt else ''}"] = nbytes / (ms / 1e3) / 1e9
     top = max(best, key=best.get)
     return {"hbm_paged_read_gbs": best[top], "hbm_paged_read_config": top, "hbm_paged_read_gbs_by_config": best,
             "hbm_paged_read": f"the decode kernel's loads without its arithmetic over one benchmark layer "
                               f"({nbytes / 1e6:.1f} MB: K and V tiles and scale rows of {B} x {n_pages} pages x "
                               f"{HKV} heads), workgroups of 4 waves on contiguous page ranges of one (sequence, "
-                              f"head); best of the grids, each the median of 5 launches"}
+                              f"head), with and without the non-temporal hint; best of the configurations, each "
+                              f"the median of 5 launches"}
 
 
 def cpu_prefill_sample(rows=4):

@@ -14,10 +14,20 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// A 16-byte load, with the non-temporal hint (nt: the line is not kept for
+// reuse) when NT.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
 // Every thread streams 16-byte words with a grid-stride loop, U loads in
 // flight per iteration; the XOR of all words is kept so that no load can be
 // dropped (it is written out only if it hits a value the data never makes).
-template <int U>
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
                                                           uint32_t* __restrict__ sink) {
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
@@ -26,12 +36,12 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   for (; i + (U - 1) * stride < n16; i += U * stride) {
     u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = p[i + u * stride];
+    for (int u = 0; u < U; ++u) w[u] = ld<NT>(p + i + u * stride);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
   }
   for (; i < n16; i += stride) {
-    const u32x4 a = p[i];
+    const u32x4 a = ld<NT>(p + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
@@ -43,6 +53,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 // loads with lane = 16-byte column as in the decode kernel.  Work split as in
 // the decode kernel: a workgroup of 4 waves owns a contiguous range of one
 // (sequence, head)'s pages, wave w takes every 4th page of it.
+template <bool NT>
 __global__ __launch_bounds__(256) void paged_read_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
                                                          const u32x4* __restrict__ ks,
                                                          const u32x4* __restrict__ vs, const int32_t* __restrict__ pt,
@@ -60,13 +71,13 @@ __global__ __launch_bounds__(256) void paged_read_kernel(const u32x4* __restrict
     const int64_t ph = static_cast<int64_t>(pt[static_cast<int64_t>(b) * max_pages + p]) * Hkv + h;
     u32x4 w[9];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = k[ph * 512 + i * 64 + lane];  // 512 x 16 B per tile
-    w[8] = ks[ph * 64 + lane];                                        // 64 x 16 B per scale row
+    for (int i = 0; i < 8; ++i) w[i] = ld<NT>(k + ph * 512 + i * 64 + lane);  // 512 x 16 B per tile
+    w[8] = ld<NT>(ks + ph * 64 + lane);                                        // 64 x 16 B per scale row
 #pragma unroll
     for (int i = 0; i < 9; ++i) acc ^= w[i].x ^ w[i].y ^ w[i].z ^ w[i].w;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = v[ph * 512 + i * 64 + lane];
-    w[8] = vs[ph * 64 + lane];
+    for (int i = 0; i < 8; ++i) w[i] = ld<NT>(v + ph * 512 + i * 64 + lane);
+    w[8] = ld<NT>(vs + ph * 64 + lane);
 #pragma unroll
     for (int i = 0; i < 9; ++i) acc ^= w[i].x ^ w[i].y ^ w[i].z ^ w[i].w;
   }
@@ -124,22 +135,32 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
   }
 }
 
+template <int U>
+void launch_stream_read(const u32x4* p, size_t n, uint32_t* sink, int grid, bool nt, hipStream_t stream) {
+  if (nt)
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(stream_read_kernel<U, true>), dim3(grid), dim3(256), 0, stream, p, n, sink);
+  else
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(stream_read_kernel<U, false>), dim3(grid), dim3(256), 0, stream, p, n, sink);
+}
+
 }  // namespace
 
 extern "C" {
 
 // Reads `bytes` (a multiple of 16) at buf with `grid` workgroups of 256
-// threads on `stream`, `unroll` (4, 8 or 16) loads in flight per thread.
-// sink: one device word.  0 = launched.
-int ceiling_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll, hipStream_t stream) {
+// threads on `stream`, `unroll` (4, 8 or 16) loads in flight per thread, with
+// the non-temporal hint when nt != 0.  sink: one device word.  0 = launched.
+int ceiling_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, int unroll, int nt,
+                        hipStream_t stream) {
   if (!buf || !sink || bytes % 16 != 0 || grid <= 0) return 1;
   const u32x4* p = static_cast<const u32x4*>(buf);
+  const size_t n = bytes / 16;
   if (unroll == 4)
-    hipLaunchKernelGGL(stream_read_kernel<4>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
+    launch_stream_read<4>(p, n, sink, grid, nt != 0, stream);
   else if (unroll == 8)
-    hipLaunchKernelGGL(stream_read_kernel<8>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
+    launch_stream_read<8>(p, n, sink, grid, nt != 0, stream);
   else if (unroll == 16)
-    hipLaunchKernelGGL(stream_read_kernel<16>, dim3(grid), dim3(256), 0, stream, p, bytes / 16, sink);
+    launch_stream_read<16>(p, n, sink, grid, nt != 0, stream);
   else
     return 1;
   return hipGetLastError() == hipSuccess ? 0 : 4;
@@ -149,19 +170,23 @@ int ceiling_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid,
 // values for K and V): k_nib / v_nib [pages][Hkv][8 KB], k_scale / v_scale
 // [pages][Hkv][1 KB], page table pt [B][max_pages] whose first n_pages
 // entries of every row are valid page ids; `grid` workgroups of 4 waves
-// (rounded down to a multiple of B * Hkv).  sink: one device word.
-// 0 = launched.
+// (rounded down to a multiple of B * Hkv); the non-temporal hint when
+// nt != 0.  sink: one device word.  0 = launched.
 int ceiling_paged_read(const void* k_nib, const void* v_nib, const void* k_scale, const void* v_scale,
-                       const int32_t* pt, int B, int max_pages, int n_pages, int Hkv, int grid, uint32_t* sink,
-                       hipStream_t stream) {
+                       const int32_t* pt, int B, int max_pages, int n_pages, int Hkv, int grid, int nt,
+                       uint32_t* sink, hipStream_t stream) {
   if (!k_nib || !v_nib || !k_scale || !v_scale || !pt || !sink || B <= 0 || Hkv <= 0 || n_pages <= 0 ||
       n_pages > max_pages || grid < B * Hkv)
     return 1;
   const int chunks = grid / (B * Hkv);
-  hipLaunchKernelGGL(paged_read_kernel, dim3(chunks * B * Hkv), dim3(256), 0, stream,
-                     static_cast<const u32x4*>(k_nib), static_cast<const u32x4*>(v_nib),
-                     static_cast<const u32x4*>(k_scale), static_cast<const u32x4*>(v_scale), pt, B, max_pages,
-                     n_pages, Hkv, chunks, sink);
+  const auto k = static_cast<const u32x4*>(k_nib), v = static_cast<const u32x4*>(v_nib);
+  const auto ks = static_cast<const u32x4*>(k_scale), vs = static_cast<const u32x4*>(v_scale);
+  if (nt)
+    hipLaunchKernelGGL(paged_read_kernel<true>, dim3(chunks * B * Hkv), dim3(256), 0, stream, k, v, ks, vs, pt, B,
+                       max_pages, n_pages, Hkv, chunks, sink);
+  else
+    hipLaunchKernelGGL(paged_read_kernel<false>, dim3(chunks * B * Hkv), dim3(256), 0, stream, k, v, ks, vs, pt, B,
+                       max_pages, n_pages, Hkv, chunks, sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -55,6 +55,12 @@ __device__ __forceinline__ void dequant8(uint32_t x, float sc, float* v) {
   for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(static_cast<int>((x >> (4 * e)) & 15u) - 8) * sc;
 }
 
+// 16 bytes with the non-temporal hint (the line is not kept for reuse).
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   // The KV heads of one page are adjacent in dispatch order, so the
@@ -78,17 +84,18 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   __shared__ uint16_t ks[kPage][nb];
   __shared__ uint16_t vs[kPage][nb];
   const uint4 zero = make_uint4(0, 0, 0, 0);
+  // (non-temporal loads: each cell is read once)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int u = tid + 256 * s;
-    (&kt[0][0])[u] = valid ? reinterpret_cast<const uint4*>(a.k_nib)[ph * (nb * kPage) + u] : zero;
-    (&vt[0][0])[u] = valid ? reinterpret_cast<const uint4*>(a.v_nib)[ph * (kPage / 8 * kD / 4) + u] : zero;
+    (&kt[0][0])[u] = valid ? nt_load(reinterpret_cast<const uint4*>(a.k_nib) + ph * (nb * kPage) + u) : zero;
+    (&vt[0][0])[u] = valid ? nt_load(reinterpret_cast<const uint4*>(a.v_nib) + ph * (kPage / 8 * kD / 4) + u) : zero;
   }
   for (int i = tid; i < kPage * nb; i += 256) {
-    (&ks[0][0])[i] = valid ? a.k_scale[ph * kPage * nb + i] : 0;
-    if (!a.v_per_token) (&vs[0][0])[i] = valid ? a.v_scale[ph * kPage * nb + i] : 0;
+    (&ks[0][0])[i] = valid ? __builtin_nontemporal_load(a.k_scale + ph * kPage * nb + i) : 0;
+    if (!a.v_per_token) (&vs[0][0])[i] = valid ? __builtin_nontemporal_load(a.v_scale + ph * kPage * nb + i) : 0;
   }
-  if (a.v_per_token && tid < kPage) vs[tid][0] = valid ? a.v_scale[ph * kPage + tid] : 0;
+  if (a.v_per_token && tid < kPage) vs[tid][0] = valid ? __builtin_nontemporal_load(a.v_scale + ph * kPage + tid) : 0;
   __syncthreads();
 
   const int l = tid & 31;  // channels 8l .. 8l + 7: block l / 4

@@ -132,25 +132,45 @@ struct VRaw {
   uint4 v[2];
 };
 
-template <bool VT>
+// Loads of cache cells, with the non-temporal hint (nt: the line is not kept
+// for reuse) when NT: in the verification-rows form each (page, KV head) is
+// read by one workgroup; the chunk form's pages are read by every query tile
+// and stay cacheable.
+template <bool NT, typename T>
+__device__ __forceinline__ T cell_load(const T* p) {
+  if constexpr (NT) {
+    if constexpr (sizeof(T) == 16) {
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+    } else {
+      return __builtin_nontemporal_load(p);
+    }
+  } else {
+    return *p;
+  }
+}
+
+template <bool VT, bool NT>
 __device__ __forceinline__ void load_k(const PrefillArgs& a, int64_t ph, int tid, KRaw& r) {
   const uint4* kt = reinterpret_cast<const uint4*>(a.k_nib + ph * (kPage * kHeadDim / 2));
   const uint16_t* ksc = a.k_scale + ph * (kPage * 8);
   const int w = tid >> 6, t = tid & 63;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) r.k[u] = kt[(2 * w + u) * 64 + t];
-  r.ks = *reinterpret_cast<const uint32_t*>(ksc + t * 8 + 2 * w);
+  for (int u = 0; u < 2; ++u) r.k[u] = cell_load<NT>(kt + (2 * w + u) * 64 + t);
+  r.ks = cell_load<NT>(reinterpret_cast<const uint32_t*>(ksc + t * 8 + 2 * w));
   if (VT)
-    r.vsd = *reinterpret_cast<const uint32_t*>(a.v_scale + ph * kPage + 2 * (tid & 31));
+    r.vsd = cell_load<NT>(reinterpret_cast<const uint32_t*>(a.v_scale + ph * kPage + 2 * (tid & 31)));
   else
-    r.vsd = *reinterpret_cast<const uint32_t*>(a.v_scale + ph * (kPage * 8) + (tid >> 2) * 8 + 2 * (tid & 3));
+    r.vsd = cell_load<NT>(
+        reinterpret_cast<const uint32_t*>(a.v_scale + ph * (kPage * 8) + (tid >> 2) * 8 + 2 * (tid & 3)));
 }
 
+template <bool NT>
 __device__ __forceinline__ void load_v(const PrefillArgs& a, int64_t ph, int tid, VRaw& r) {
   const uint4* vt = reinterpret_cast<const uint4*>(a.v_nib + ph * (kPage * kHeadDim / 2));
   const int w = tid >> 6, t = tid & 63;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) r.v[u] = vt[(2 * w + u) * 64 + t];
+  for (int u = 0; u < 2; ++u) r.v[u] = cell_load<NT>(vt + (2 * w + u) * 64 + t);
 }
 
 // This thread's dword of the page's V scale tile -> LDS [block][token] (VT:
@@ -354,11 +374,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   if (pbeg < pend) {
     KRaw k0;
     const int64_t ph0 = page_handle(pbeg, cur_valid);
-    load_k<VT>(a, ph0, tid, k0);
-    load_v(a, ph0, tid, vcur);
+    load_k<VT, ROWS>(a, ph0, tid, k0);
+    load_v<ROWS>(a, ph0, tid, vcur);
     if (pbeg + 1 < pend) {
       kraw_ph = page_handle(pbeg + 1, kraw_valid);
-      load_k<VT>(a, kraw_ph, tid, kraw);
+      load_k<VT, ROWS>(a, kraw_ph, tid, kraw);
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) unpack_k(sm, k0, tid, x >> 2, x & 3, nmagic);
@@ -532,9 +552,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     if (lp + 2 < pend) {
       kahead_valid = static_cast<uint32_t>(pid_next) < static_cast<uint32_t>(a.num_pages);
       kahead_ph = static_cast<int64_t>(kahead_valid ? pid_next : 0) * a.Hkv + g;
-      load_k<VT>(a, kahead_ph, tid, kahead);
+      load_k<VT, ROWS>(a, kahead_ph, tid, kahead);
     }
-    if (lp + 1 < pend) load_v(a, kraw_ph, tid, vnext);
+    if (lp + 1 < pend) load_v<ROWS>(a, kraw_ph, tid, vnext);
     pid_next = pid_after;
     __syncthreads();  // K of this page is in LDS; every wave is done with the previous V
     __builtin_amdgcn_sched_barrier(0);
