@@ -197,6 +197,9 @@ __device__ __forceinline__ void unpack_k(Fp8Smem& sm, const KRaw& r, int tid, fl
 // 8 tokens of the unit fall in one 32-token group g and one 8-token column a
 // of it; within a group the MFMA takes tokens 8 a + 4 h + i from lane half h,
 // byte 4 a + i, so each channel gets two 4-byte pieces (h = 0, 1).
+// byte b of w as a float (v_cvt_f32_ubyte<b>)
+__device__ __forceinline__ float byte_to_f32(uint32_t w, int b) { return static_cast<float>((w >> (8 * b)) & 0xFFu); }
+
 template <bool VT>
 __device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, int parity) {
   const int c8 = tid >> 6, j = tid & 63;
@@ -216,16 +219,18 @@ __device__ __forceinline__ void unpack_v(Fp8Smem& sm, const VRaw& r, int tid, in
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t w = word(r.v, k);
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // one nibble per byte, converted by byte (v_cvt_f32_ubyte0..3)
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimiser, which would otherwise extract each nibble by itself
+    asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int tk = 2 * k + rr;
       const float s = sv[tk], z = -8.0f * sv[tk];
-      const uint32_t l8 = lo >> (16 * rr), h8 = hi >> (16 * rr);
-      x[tk][0] = fmaf(static_cast<float>(l8 & 0xFF), s, z);
-      x[tk][1] = fmaf(static_cast<float>(h8 & 0xFF), s, z);
-      x[tk][2] = fmaf(static_cast<float>((l8 >> 8) & 0xFF), s, z);
-      x[tk][3] = fmaf(static_cast<float>((h8 >> 8) & 0xFF), s, z);
+      x[tk][0] = fmaf(byte_to_f32(lo, 2 * rr), s, z);
+      x[tk][1] = fmaf(byte_to_f32(hi, 2 * rr), s, z);
+      x[tk][2] = fmaf(byte_to_f32(lo, 2 * rr + 1), s, z);
+      x[tk][3] = fmaf(byte_to_f32(hi, 2 * rr + 1), s, z);
     }
   }
 #pragma unroll
@@ -384,27 +389,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fp8_kernel(Fp8Args a, con
     // (the mask only on pages that reach past the tile's first position: a
     // branch of its own, which keeps its compares off the other pages)
     const bool need_mask = !cur_valid || lp * kPage + 63 > qpos_first;
-    float gmax[2];
     if (need_mask) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float mx = -INFINITY;
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int tok = lp * kPage + 32 * tt + 8 * (e >> 2) + 4 * half + (e & 3);
+          // in place: the unmasked pages keep the scores where they are
+          asm volatile("" : "+v"(x[tt][e]));
           if (!(cur_valid && qvalid && tok <= qpos)) x[tt][e] = -INFINITY;
-          mx = fmaxf(mx, x[tt][e]);
+          asm volatile("" : "+v"(x[tt][e]));
         }
-        gmax[tt] = mx;
-      }
-    } else {
+    }
+    float gmax[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float mx = x[tt][0];
+    for (int tt = 0; tt < 2; ++tt) {
+      float mx = x[tt][0];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[tt][e]);
-        gmax[tt] = mx;
-      }
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[tt][e]);
+      gmax[tt] = mx;
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) gmax[tt] = fmaxf(gmax[tt], __shfl_xor(gmax[tt], 32, 64)) * row_scale;
