@@ -517,6 +517,52 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     }
   };
 
+  // The same first part cut into pieces for the matrix phases: part 0 masks
+  // the tile where needed and takes the maximum of its first 8 scores, part 1
+  // that of the other 8 and starts the exchange with the other half's row,
+  // max_finish settles the row maximum and the lazy raise.
+  auto max_part = [&](float16_t& st, int lp, int tt, int part, float& mx, float& other) {
+    if (part == 0) {
+      const bool need_mask = !cur_valid || lp * kPage + tt * 32 + 31 > qpos_first;
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+          const bool ok = cur_valid && qvalid[0] && tok <= qpos[0];
+          st[i] = ok ? st[i] : -INFINITY;
+        }
+      }
+      mx = st[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, st[i]);
+    } else {
+#pragma unroll
+      for (int i = 8; i < 16; ++i) mx = fmaxf(mx, st[i]);
+      other = __shfl_xor(mx, 32, 64);
+    }
+  };
+  auto max_finish = [&](float mx, float other, half8_t* pb_prev, half8_t* pl_prev) {
+    mx = fmaxf(mx, other) * qk;  // log2 units
+    s_max[0] = fmaxf(s_max[0], mx);
+    const bool raise = mx > m_run[0] + kSlack;
+    if (__ballot(raise)) {
+      const float mn = raise ? ceilf(mx) : m_run[0];
+      const float alpha = m_run[0] == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_run[0] - mn));
+      m_run[0] = mn;
+      l_lane[0] *= alpha;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) acc[0][d] *= alpha;
+      if (pb_prev) {
+        const _Float16 ah = static_cast<_Float16>(alpha);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          pb_prev[s2] *= ah;
+          pl_prev[s2] *= ah;
+        }
+      }
+    }
+  };
+
   // Softmax, second part, in half-pieces of one score pair (2j, 2j + 1): the
   // even half exponentiates, the odd half splits.  B operands per k-step: P *
   // 2^11 as hi and lo (rounded toward zero).  P stays below 2^kSlack, so P *
@@ -590,36 +636,48 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
     s_phase(0, st0, [&](int step) {
       if (step < 24) v_piece(sm, vcur, vs, tid, step >> 3, step & 7, hv, lv, nmagic);
     });
-    softmax_max(st0, lp, 0, nullptr, nullptr);
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- tile 1: S^T, the last V channel and tile 0's P meanwhile ----
+    // ---- tile 1: S^T; tile 0's maximum (in pieces), the last V channel and tile 0's P meanwhile ----
     half8_t pb0[2], pl0[2], pb1[2], pl1[2];
     float e[2], psum = 0.0f;
-    const float off0 = p_offset();
+    float off0 = 0.0f, mx0 = 0.0f, ot0 = 0.0f;
     float16_t st1{};
     s_phase(1, st1, [&](int step) {
-      if (step < 8)
-        v_piece(sm, vcur, vs, tid, 3, step, hv, lv, nmagic);
-      else if (step < 24)
-        p_half(st0, off0, step - 8, e, psum, pb0, pl0);
+      if (step == 1 || step == 2) {
+        max_part(st0, lp, 0, step - 1, mx0, ot0);
+      } else if (step == 5) {
+        max_finish(mx0, ot0, nullptr, nullptr);
+        off0 = p_offset();
+      } else if (step >= 6 && step < 30) {  // (steps 3 and 4: the exchange of the row maximum is in flight)
+        if (step < 14)
+          v_piece(sm, vcur, vs, tid, 3, step - 6, hv, lv, nmagic);
+        else
+          p_half(st0, off0, step - 14, e, psum, pb0, pl0);
+      }
     });
     l_lane[0] += psum * (1.0f / 2048.0f);
     // keeps tile 0's P inside that phase (it would otherwise sink to its first use)
     asm volatile("" ::"v"(pb0[0]), "v"(pb0[1]), "v"(pl0[0]), "v"(pl0[1]));
-    softmax_max(st1, lp, 1, pb0, pl0);
     __syncthreads();  // V of this page is in LDS; every wave is done with this K
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- PV of tile 0, tile 1's P and K channels of the next page meanwhile ----
-    const float off1 = p_offset();
+    // ---- PV of tile 0; tile 1's maximum (in pieces), its P and K channels of the next page meanwhile ----
+    // A raise of the maximum here rescales the accumulator (with the products
+    // of tile 0 already in it) and the P operands of tile 0 not yet
+    // multiplied, by the same power of two.
+    float off1 = 0.0f, mx1 = 0.0f, ot1 = 0.0f;
     psum = 0.0f;
     pv_phase(0, pb0, pl0, [&](int step) {
-      if (step < 8) {
-        p_half(st1, off1, 2 * step, e, psum, pb1, pl1);
-        p_half(st1, off1, 2 * step + 1, e, psum, pb1, pl1);
-      } else if (step < 13) {
-        unpack_k(sm, kraw, tid, (step - 8) >> 2, (step - 8) & 3, nmagic);
+      if (step == 0 || step == 1) {
+        max_part(st1, lp, 1, step, mx1, ot1);
+      } else if (step == 3) {
+        max_finish(mx1, ot1, pb0, pl0);
+        off1 = p_offset();
+      } else if (step >= 4 && step < 12) {
+        p_half(st1, off1, 2 * (step - 4), e, psum, pb1, pl1);
+        p_half(st1, off1, 2 * (step - 4) + 1, e, psum, pb1, pl1);
+      } else if (step >= 12) {
+        unpack_k(sm, kraw, tid, (step - 12) >> 2, (step - 12) & 3, nmagic);
       }
     });
     l_lane[0] += psum * (1.0f / 2048.0f);
@@ -627,9 +685,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
 
     // ---- PV of tile 1, the rest of the next page's K meanwhile ----
     pv_phase(1, pb1, pl1, [&](int step) {
-      if (step < 3)
-        unpack_k(sm, kraw, tid, (step + 5) >> 2, (step + 5) & 3, nmagic);
-      else if (step == 3)
+      if (step < 4)
+        unpack_k(sm, kraw, tid, (step + 4) >> 2, (step + 4) & 3, nmagic);
+      else if (step == 4)
         store_vscales<VT>(sm, kraw, tid, (lp + 1) & 1);
     });
     }
