@@ -479,48 +479,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
   // any P operands not yet multiplied are rescaled) only when a score exceeds it
   // by more than kSlack; the new max is rounded up to an integer, so the rescale
   // factor is an exact power of two.  The exact maximum is tracked and restored
-  // at the end.
-  auto softmax_max = [&](float16_t& st, int lp, int tt, half8_t* pb_prev, half8_t* pl_prev) {
-    float mx = -INFINITY;
-    const bool need_mask = !cur_valid || lp * kPage + tt * 32 + 31 > qpos_first;
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = lp * kPage + tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-        const bool ok = cur_valid && qvalid[0] && tok <= qpos[0];
-        st[i] = ok ? st[i] : -INFINITY;
-        mx = fmaxf(mx, st[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qk;  // log2 units
-    s_max[0] = fmaxf(s_max[0], mx);
-    const bool raise = mx > m_run[0] + kSlack;
-    if (__ballot(raise)) {
-      const float mn = raise ? ceilf(mx) : m_run[0];
-      // 2^(m_run - mn), exact; 0 while nothing has been accumulated
-      const float alpha = m_run[0] == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_run[0] - mn));
-      m_run[0] = mn;
-      l_lane[0] *= alpha;
-#pragma unroll
-      for (int d = 0; d < kD; ++d) acc[0][d] *= alpha;
-      if (pb_prev) {  // the other tile's P operands, computed with the old max
-        const _Float16 ah = static_cast<_Float16>(alpha);
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          pb_prev[s2] *= ah;
-          pl_prev[s2] *= ah;
-        }
-      }
-    }
-  };
-
-  // The same first part cut into pieces for the matrix phases: part 0 masks
-  // the tile where needed and takes the maximum of its first 8 scores, part 1
-  // that of the other 8 and starts the exchange with the other half's row,
-  // max_finish settles the row maximum and the lazy raise.
+  // at the end.  In pieces, for the matrix phases: part 0 masks the tile where
+  // needed and takes the maximum of its first 8 scores, part 1 that of the
+  // other 8 and starts the exchange with the other half's row, max_finish
+  // settles the row maximum and the lazy raise.
   auto max_part = [&](float16_t& st, int lp, int tt, int part, float& mx, float& other) {
     if (part == 0) {
       const bool need_mask = !cur_valid || lp * kPage + tt * 32 + 31 > qpos_first;
@@ -561,6 +523,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
         }
       }
     }
+  };
+
+  // The whole first part at once (the ROWS form).
+  auto softmax_max = [&](float16_t& st, int lp, int tt) {
+    float mx, other;
+    max_part(st, lp, tt, 0, mx, other);
+    max_part(st, lp, tt, 1, mx, other);
+    max_finish(mx, other, nullptr, nullptr);
   };
 
   // Softmax, second part, in half-pieces of one score pair (2j, 2j + 1): the
@@ -612,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a, con
       uint32_t hv[4], lv[4];
       float16_t st{};
       s_phase(tt_w, st, [&](int step) { v_piece(sm, vcur, vs, tid, step >> 3, step & 7, hv, lv, nmagic); });
-      softmax_max(st, lp, tt_w, nullptr, nullptr);
+      softmax_max(st, lp, tt_w);
       half8_t pb[2], pl[2];
       float e[2], psum = 0.0f;
       const float off = p_offset();
