@@ -438,9 +438,21 @@ def bench_gather(iters=10):
     # read: the cells; written: two bf16 rows of D values per token and head; plus the page table
     by = total * HKV * (BYTES_PER_TOKEN_HEAD + 2 * D * 2) + L.num_pages * 4
     del L, k, v
+    torch.cuda.empty_cache()
+    # the gather writes 3.5x what it reads: a write ceiling on the same box
+    # (torch's fill of 2 GiB, median of 5); main() adds the bound from it and
+    # the measured read ceiling
+    n = 2 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    fill_ms = float(np.median(timed(lambda: buf.zero_(), 5)))
+    del buf
+    torch.cuda.empty_cache()
+    gbs = by / (ms / 1e3) / 1e9
     return {"workload": "gather_kv_cache_f4, 3 x 262,144 tokens -> bf16 rows", "ms": ms,
-            "gbs": by / (ms / 1e3) / 1e9, "hbm_frac": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "bytes": by}
+            "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bytes": by,
+            "bytes_read": by - total * HKV * 2 * D * 2, "bytes_written": total * HKV * 2 * D * 2,
+            "write_ceiling_gbs": n / (fill_ms / 1e3) / 1e9,
+            "write_ceiling": "torch fill of 2 GiB on the same box, median of 5"}
 
 
 def bench_ragged(iters=20):
@@ -718,7 +730,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=458752)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="also run a plain device copy of BYTES bytes 3 times (calibrates HBM byte counters)")
-    ap.add_argument("--only", choices=["1m", "ragged", "prefill", "prefill_fp8", "rows8"], default=None,
+    ap.add_argument("--only", choices=["1m", "ragged", "prefill", "prefill_fp8", "rows8", "gather"], default=None,
                     help="run one workload alone (for profiling) and print its result; no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -732,7 +744,8 @@ def main():
         copy_probe(args.copy_probe)
     if args.only:
         run = {"1m": bench_1m, "ragged": bench_ragged, "prefill": bench_prefill,
-               "prefill_fp8": lambda: bench_prefill(fp8=True), "rows8": lambda: bench_rows(8)}[args.only]
+               "prefill_fp8": lambda: bench_prefill(fp8=True), "rows8": lambda: bench_rows(8),
+               "gather": bench_gather}[args.only]
         log(args.only, run())
         return
     r = bench_config1(args.steps, args.warmup)
@@ -800,6 +813,11 @@ def main():
         if "prefill_fp8" in extra:
             p = extra["prefill_fp8"]
             p["kernel_frac_of_measured_mfma"] = p["kernel_tflops"] / ceil["mfma_fp8_tflops"]
+        if "gather_bf16" in extra:
+            gth = extra["gather_bf16"]
+            # the time of its reads at the read ceiling plus its writes at the write ceiling
+            bound_ms = (gth["bytes_read"] / ceil["hbm_read_gbs"] + gth["bytes_written"] / gth["write_ceiling_gbs"]) / 1e6
+            gth["frac_of_read_write_ceilings"] = bound_ms / gth["ms"]
     line = {
         "metric": METRIC,
         "value": r["value"],
