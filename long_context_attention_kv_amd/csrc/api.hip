@@ -406,8 +406,9 @@ int gather_kv_cache_f4(const f4kv_cache* cache, const int32_t* page_table, const
   if (B == 0 || total_tokens == 0) return ok();
   if (max_pages <= 0 || max_pages > INT32_MAX / f4kv::kPage)
     return fail(F4KV_ERR_INVALID, "%s: max_pages out of range (%d)", fn, max_pages);
-  if (static_cast<int64_t>(max_pages) * cache->num_kv_heads > INT32_MAX)
-    return fail(F4KV_ERR_INVALID, "%s: max_pages * num_kv_heads must fit in int32", fn);
+  if ((static_cast<int64_t>(max_pages) + 7) / 8 * 8 * cache->num_kv_heads > INT32_MAX)
+    return fail(F4KV_ERR_INVALID, "%s: max_pages (rounded up to a multiple of 8) * num_kv_heads must fit in int32",
+                fn);
   if (cache->head_dim != f4kv::kHeadDim)
     return fail(F4KV_ERR_UNSUPPORTED, "%s: head_dim %d not implemented (256 is)", fn, cache->head_dim);
   if (!page_table || !cu_seq_lens || !k_out || !v_out) return fail(F4KV_ERR_INVALID, "%s: NULL array", fn);

@@ -7,7 +7,8 @@
 // in fp32; a bf16 output is that value rounded to nearest-even.
 //
 // A workgroup owns one page of one sequence and one KV head; its cells go
-// through LDS so that the loads and the stores are both contiguous.
+// through LDS so that the loads and the stores are both contiguous.  The grid
+// puts the heads of a page on one XCD (their output rows interleave).
 #include "f4kv_internal.h"
 
 namespace f4kv {
@@ -63,9 +64,12 @@ __device__ __forceinline__ uint4 nt_load(const uint4* p) {
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-  // The KV heads of one page are adjacent in dispatch order, so the
-  // workgroups in flight together fill whole output rows (H x D values).
-  const int lp = blockIdx.x / a.H, h = blockIdx.x - lp * a.H, b = blockIdx.y;
+  // blockIdx.x = (page / 8 * H + head) * 8 + page % 8: the workgroups are
+  // dealt to the XCDs in turn, so the H heads of a page (whose output rows
+  // interleave) run on one XCD, and consecutive pages on different ones.
+  const int x8 = blockIdx.x & 7, rest = static_cast<int>(blockIdx.x >> 3);
+  const int h = rest % a.H, lp = (rest / a.H) * 8 + x8, b = blockIdx.y;
+  if (lp >= a.max_pages) return;
   const int tid = threadIdx.x;
   const int32_t row0 = a.cu[b];
   const int32_t len = a.cu[b + 1] - row0;
@@ -144,7 +148,7 @@ hipError_t launch_gather(const f4kv_cache& c, const int32_t* pt, const int32_t* 
   a.total = total;
   a.bf16 = bf16;
   a.v_per_token = c.v_scale_per_token;
-  const dim3 grid(max_pages * c.num_kv_heads, B);  // both checked by the caller
+  const dim3 grid((max_pages + 7) / 8 * 8 * c.num_kv_heads, B);  // both checked by the caller
   if (bf16)
     hipLaunchKernelGGL(gather_kernel<true>, grid, dim3(256), 0, s, a);
   else
