@@ -797,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     const float tmask = (pvalid && tok >= t0 && tok < t1) ? 0.0f : -INFINITY;
 
     // keys: lane = token, on the matrix cores (mfma4): per block 8 products
-    // of 4 channels each, started from the block's "- 8" term; the block
+    // of 4 channels each on the centred operands (n - 8) 2^-24; the block
     // scale is applied once per block
     float logit[G];
 #pragma unroll
