@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x, grp = tid >> 6, t = tid & 63;
   __shared__ float s_red[kMergeThreads];
-  __shared__ float s_gm[kGroups], s_gl[kGroups];
+  __shared__ float s_gl[kGroups];
   __shared__ float4_t s_acc[kGroups][64];
 
   // global max over live states
