@@ -2,7 +2,6 @@
 the checks on, raises the flag of the bad value it was given (and still skips
 the value as without checks); good inputs raise nothing; with the checks off
 nothing is raised."""
-import numpy as np
 import pytest
 import torch
 
