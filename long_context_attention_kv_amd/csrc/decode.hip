@@ -20,14 +20,15 @@
 //    block-major K tile); the G logits are formed on the matrix cores with
 //    the 4 x 4 x 4 fp16 product in 16 blocks, whose lane layout is exactly
 //    lane = token (4 tokens per block, A = 4 query heads x 4 channels, read
-//    from LDS).  A nibble n becomes an exact fp16 operand with one AND and one
-//    packed fp16 add: 0x000F000F picks two nibbles into the mantissas of an
-//    fp16 pair, i.e. the subnormals n * 2^-24, and adding -8 * 2^-24 gives
-//    (n - 8) * 2^-24; 0x00F000F0 picks the next two as 16 n * 2^-24 (minus
-//    128 * 2^-24; the matching query pair is pre-divided by 16).  The block
-//    scale is applied once per block.  This takes the 512 dot products per
-//    page off the vector ALUs, which otherwise bound the kernel below the
-//    memory rate.
+//    from LDS).  A nibble n becomes an exact fp16 operand with one AND:
+//    0x000F000F picks two nibbles into the mantissas of an fp16 pair, i.e. the
+//    subnormals n * 2^-24; 0x00F000F0 picks the next two as 16 n * 2^-24 (the
+//    matching query pair is pre-divided by 16).  The "- 8" of every code is
+//    one term per (head, block), -8 2^-24 times the sum of the block's query
+//    operands, prepared with the query and used as the accumulator's start.
+//    The block scale is applied once per block.  This takes the 512 dot
+//    products per page off the vector ALUs, which otherwise bound the kernel
+//    below the memory rate.
 //  * values: lane = 4 consecutive channels, on the matrix cores as well.  The
 //    V tile stores 8 tokens x 4 channels per 16-byte unit, two tokens per
 //    dword, so the same masks and add yield fp16 pairs (n - 8) * 2^-24 (x16
@@ -39,10 +40,13 @@
 //    largest weight (about 21 bits each; a single fp16 weight, 11 bits, would
 //    leave ~2e-3 of the output RMS on channels whose values are many times
 //    the others').
-//    The operands are centred (n - 8, not n with the 8 taken off the sums
-//    afterwards) because the 4 x 4 x 4 product sums with a relative error of
-//    ~2^-19 (measured), which the cancellation of sum w n against 8 sum w
-//    would multiply on channels whose outputs are near zero.
+//    These operands are centred (n - 8, one packed fp16 add of -8 2^-24 per
+//    pair) because the 4 x 4 x 4 product sums with a relative error of ~2^-19
+//    (measured), which the cancellation of sum w n against 8 sum w would
+//    multiply on channels whose outputs are near zero (the weights w are all
+//    positive).  The keys need no such care: the query's signs already make
+//    sum q n and 8 sum q of the same order as their difference, and the
+//    measured errors equal those of centred keys.
 // The query is pre-scaled by a power of two per head so its fp16 copy keeps
 // full precision whatever its magnitude; fp32 accumulation throughout.
 #include <algorithm>
@@ -69,6 +73,7 @@ template <int G>
 struct __align__(64) QPrep {
   uint32_t pair[G][8][4][4];  // fp16 pairs [head][block][dword][pair], scaled by 2^e_h
   float kscale[G];            // 2^(24 - e_h) * sm_scale * log2(e)
+  float k8[8][G];             // per block and head: -8 2^-24 times the sum of the query operands
 };
 
 // The new token of each sequence for a decode step (paged_attn_decode_step_f4):
@@ -617,6 +622,19 @@ __global__ __launch_bounds__(kThreads) void decode_qprep_kernel(const uint16_t* 
     P.pair[h][c][k][p] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
   }
+  // the keys' "- 8": per (head, block) the sum of its 32 query operands as the
+  // products take them (the x16 slots carry q / 16 against 16 n), times -8 2^-24
+  for (int i = tid; i < G * 8; i += kThreads) {
+    const int h = i / 8, c = i % 8;
+    float sum = 0.0f;
+    for (int j = 0; j < kBlock; ++j) {
+      const int p = j & 3;
+      const int ex = qexp[h] - ((p & 1) ? 4 : 0);
+      const float a = static_cast<float>(static_cast<_Float16>(ldexpf(qf[h][32 * c + j], ex)));
+      sum += (p & 1) ? 16.0f * a : a;
+    }
+    P.k8[c][h] = sum * -0x1p-21f;
+  }
 }
 
 template <int G>
@@ -628,6 +646,7 @@ struct __align__(16) DecodeSmem {
   float fold_m[kWaves][G];
   float fold_l[kWaves][G];
   uint4 qa[G][8][4];  // the query pairs of QPrep, read as matrix-core operands
+  float k8[8][G];     // the keys' "- 8" terms of QPrep
 };
 
 // Combines the per-wave states in LDS (max in log2 units, sum, normalised
@@ -716,6 +735,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
     lim[h] = __builtin_amdgcn_readfirstlane(min(t1, ctx - (a.R - 1 - (a.r0 + h / a.Gq))));
 
   const QPrep<G>* QP = qprep + __builtin_amdgcn_readfirstlane(b * a.Hkv + g);
+  if (tid < 8 * G) (&sm.k8[0][0])[tid] = (&QP->k8[0][0])[tid];
   {
     const uint4* src = reinterpret_cast<const uint4*>(&QP->pair[0][0][0][0]);
     for (int i = tid; i < G * 32; i += kThreads) (&sm.qa[0][0][0])[i] = src[i];
@@ -815,16 +835,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a, const QP
         for (int k = 0; k < 4; ++k) qa[st][k] = sm.qa[4 * st + qh][c][k];
       float4_t acc[kSets];
 #pragma unroll
-      for (int st = 0; st < kSets; ++st) acc[st] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int st = 0; st < kSets; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[st][i] = 4 * st + i < G ? sm.k8[c][4 * st + i] : 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        // centred operands (n - 8) 2^-24 (x16 for p1, p3), as for the values
+        // operands n 2^-24 (x16 for p1, p3); the "- 8" started the accumulator
         const uint32_t wd = word(tl[c], k);
-        const uint32_t p0 = centre(wd & 0x000F000Fu, kM8);
-        const uint32_t p1 = centre(wd & 0x00F000F0u, kM128);
+        const uint32_t p0 = wd & 0x000F000Fu;
+        const uint32_t p1 = wd & 0x00F000F0u;
         const uint32_t w8 = wd >> 8;
-        const uint32_t p2 = centre(w8 & 0x000F000Fu, kM8);
-        const uint32_t p3 = centre(w8 & 0x00F000F0u, kM128);
+        const uint32_t p2 = w8 & 0x000F000Fu;
+        const uint32_t p3 = w8 & 0x00F000F0u;
         if (k == 3) {
           // the slot's next tile, V block c, requested once the K block is
           // unpacked (issued earlier, the load would need registers of its
